@@ -1,0 +1,200 @@
+/*
+ * dspark.h — C ABI of the DSpark draft-round hot path on MI355X (gfx950).
+ *
+ * Four operations, each the data-parallel core of one step of a DSpark draft
+ * round as the pages describe it:
+ *
+ *   dspark_block_attention  block-masked dual-source attention
+ *   dspark_markov_sample    Markov-head sequential gamma-step sampler
+ *   dspark_accept_rate      TV-distance accept rate (+ optional tau)
+ *   dspark_eval_mask        cumulative-product eval mask
+ *
+ * Sources (cited per entry point): page 1 = "03 · DSpark 建模：Markov 与
+ * Confidence" (devpress.csdn.net), page 2 = "从 DFlash 到 dLLM Self-Spec
+ * （三）" (r00kie-liu.github.io), page 4 = "DSpark 深度解读" (juejin.cn).
+ *
+ * Shape names follow page 1 §3.1: B batch, A anchors (blocks) per row,
+ * gamma block size, V vocabulary, Hq / Hkv query / key-value heads,
+ * D head dimension, r Markov rank, R Markov rows.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every tensor argument is a caller-owned DEVICE pointer to contiguous
+ *   row-major memory in the stated layout.  The library never allocates,
+ *   frees or keeps a pointer after the call returns.
+ * - Scratch memory is passed in as (ws, ws_bytes); size it with the matching
+ *   *_workspace_bytes() query (a pure host function of the shapes).  A
+ *   workspace may be reused by later calls on the same stream; two calls
+ *   that run concurrently must not share one.
+ * - `stream` is a hipStream_t (NULL = the default stream).  Calls only
+ *   enqueue work on it and never synchronise the host.
+ * - Arguments are validated on the host before any HIP call; an invalid
+ *   argument returns DSPARK_ERR_INVALID_ARG and enqueues nothing.
+ * - Data-dependent faults that only the device can see (an anchor outside
+ *   its context, a token outside [0, V), ...) set bits in the optional
+ *   device word *dev_status (atomic OR; pass NULL to ignore them).  Kernels
+ *   clamp such indices, so they never read or write out of bounds.
+ * - The human-readable reason of the last failing call on the calling host
+ *   thread is returned by dspark_last_error().
+ * - Outputs are bitwise deterministic for fixed inputs and launch shapes.
+ */
+#ifndef DSPARK_H
+#define DSPARK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define DSPARK_OK               0
+#define DSPARK_ERR_INVALID_ARG (-1)
+#define DSPARK_ERR_WORKSPACE   (-2)
+#define DSPARK_ERR_UNSUPPORTED (-3)
+#define DSPARK_ERR_HIP         (-4)
+
+/* element types */
+#define DSPARK_F32  0
+#define DSPARK_BF16 1
+
+/* bits OR-ed into *dev_status */
+#define DSPARK_STATUS_BAD_ANCHOR  1  /* kept block with anchor < 0 or > its context length */
+#define DSPARK_STATUS_BAD_TOKEN   2  /* previous token outside [0, V) */
+#define DSPARK_STATUS_BAD_OFFSETS 4  /* ctx_offsets not non-decreasing, or a context longer than max_ctx */
+#define DSPARK_STATUS_BAD_LABEL   8  /* label index beyond S_stride of the loss mask */
+
+/* Library version (major*10000 + minor*100 + patch). */
+int dspark_version(void);
+
+/* Reason of the last non-zero status returned on this host thread ("" if none). */
+const char* dspark_last_error(void);
+
+/* ------------------------------------------------------------------------
+ * Block-masked dual-source attention (page 1 §3.4 block attention mask and
+ * §3.5 custom attention; page 4 §3.2).  Queries come from the draft blocks
+ * only; keys/values are the context projections followed by the block's own
+ * projections.  For draft row (b, a, k) and query head h (key/value head
+ * kvh = h / (Hq / Hkv)):
+ *
+ *     out = sum_{j in vis} softmax_j(scale * <q, k_j>) * v_j
+ *     vis = context rows [0, anchor[b,a]) of request b
+ *           + the gamma own-block rows (b, a*gamma .. a*gamma+gamma-1)
+ *
+ * and a block with keep_mask[b,a] == 0 outputs zeros (lse = -inf).  Within a
+ * block every query sees all gamma own-block keys.
+ *
+ *   q            [B, A*gamma, Hq, D]    dtype
+ *   k_ctx, v_ctx [T, Hkv, D]            dtype, T = ctx_offsets[B]; request b
+ *                                        owns rows ctx_offsets[b] .. ctx_offsets[b+1]-1
+ *   ctx_offsets  [B+1] int32, non-decreasing, ctx_offsets[0] = 0
+ *   k_blk, v_blk [B, A*gamma, Hkv, D]   dtype
+ *   anchor_pos   [B, A] int32: 0 <= anchor <= context length of request b
+ *   keep_mask    [B, A] uint8 (0 = masked block; its anchor is ignored)
+ *   out          [B, A*gamma, Hq, D]    dtype (written for every row)
+ *   lse          [B, Hq, A*gamma] float32, natural-log log-sum-exp of the
+ *                scaled logits, -inf for masked rows (nullable)
+ *   max_ctx      host upper bound of every request's context length
+ *   total_ctx    rows allocated in k_ctx / v_ctx (T); every request's range
+ *                is clamped into [0, total_ctx) and a clamp is flagged
+ *                DSPARK_STATUS_BAD_OFFSETS, so bad offsets never read out of
+ *                bounds
+ *   scale        logit scale > 0 (1/sqrt(D) for Qwen3-style, 1.0 for Gemma4-style)
+ *   dtype        DSPARK_BF16 (fp32 accumulate, bf16 out) or DSPARK_F32
+ * Limits: D in {64, 128}; Hq % Hkv == 0; 1 <= gamma <= 64; A*gamma*Hq/Hkv
+ * rows per (b, kvh) below 2^31.  Out-of-range anchors are clamped into
+ * [0, context length] and flagged DSPARK_STATUS_BAD_ANCHOR.
+ * ---------------------------------------------------------------------- */
+size_t dspark_block_attention_workspace_bytes(int B, int A, int gamma, int Hq, int Hkv,
+                                              int D, int max_ctx);
+int dspark_block_attention(const void* q, const void* k_ctx, const void* v_ctx,
+                           const int32_t* ctx_offsets, const void* k_blk, const void* v_blk,
+                           const int32_t* anchor_pos, const uint8_t* keep_mask,
+                           void* out, float* lse,
+                           int B, int A, int gamma, int Hq, int Hkv, int D, int max_ctx,
+                           int total_ctx, float scale, int dtype,
+                           void* ws, size_t ws_bytes, int32_t* dev_status, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Markov-head sequential sampler (page 1 §3.7, the paper's Eq. 5; page 2
+ * §3.4 and §3.8.2 sample_block_tokens).  For every row, left to right over
+ * i = 0 .. gamma-1, with prev = first_prev[row] at i = 0:
+ *
+ *     l[v]  = base_logits[row, i, v] + sum_j W1[prev, j] * W2[j, v]
+ *     tok   = argmax_v l[v]                      (temperature == 0, greedy)
+ *           = argmax_v l[v] / T + G(seed,row,i,v) (temperature T > 0)
+ *     tokens[row, i] = tok;  prev = tok
+ *
+ * Ties go to the lowest index.  G is Gumbel(0,1) noise -ln(-ln u) with
+ * u = ((x >> 9) + 1/2) * 2^-23, x = word (v & 3) of Philox4x32-10 (Salmon
+ * et al., SC'11) at counter (v >> 2, i, row, 0) and key (seed mod 2^32,
+ * seed >> 32); `row` is the row's index in this call.
+ *
+ *   base_logits [R, gamma, V] float32
+ *   w1          [V, r]  wdtype (embedding table)
+ *   w2          [r, V]  wdtype (row j holds the rank-j output weights)
+ *   first_prev  [R] int32, in [0, V) (the anchor tokens)
+ *   tokens      [R, gamma] int32 (out)
+ *   step_logits [R, gamma, V] float32 (out, nullable): the l[v] above
+ *   wdtype      DSPARK_BF16 (MFMA path) or DSPARK_F32 (vector-ALU path)
+ * Limits: V >= 1, 1 <= r <= 1024 (bf16: r % 32 == 0), 1 <= gamma <= 1024,
+ * temperature >= 0 and finite.  Tokens outside [0, V) read as 0 and set
+ * DSPARK_STATUS_BAD_TOKEN.
+ * ---------------------------------------------------------------------- */
+size_t dspark_markov_sample_workspace_bytes(int R, int gamma, int V, int r, int wdtype);
+int dspark_markov_sample(const float* base_logits, const void* w1, const void* w2,
+                         const int32_t* first_prev, int32_t* tokens, float* step_logits,
+                         int R, int gamma, int V, int r, int wdtype,
+                         float temperature, uint64_t seed,
+                         void* ws, size_t ws_bytes, int32_t* dev_status, void* stream);
+
+/* ------------------------------------------------------------------------
+ * TV-distance accept rate (page 1 §3.9, the paper's Eq. 8; page 2 §3.5 and
+ * §3.8.3) and the tau statistic (page 1 §3.10).  Per row of V logits:
+ *
+ *     accept = clamp(1 - 1/2 * sum_v |softmax(draft)_v - softmax(target)_v|, 0, 1)
+ *
+ * softmaxes in float32 on the upcast stored values.  If tau != NULL:
+ *
+ *     tau[b, a] = 1 + sum_k prod_{i <= k} accept[b,a,i] * eval_mask[b,a,i]
+ *
+ * (eval_mask NULL = all ones).
+ *
+ *   draft_logits, target_logits [B, A, gamma, V] dtype
+ *   accept     [B, A, gamma] float32 (out)
+ *   eval_mask  [B, A, gamma] uint8 (nullable; only read for tau)
+ *   tau        [B, A] float32 (out, nullable)
+ * Limits: V >= 2, gamma <= 1024.  Launched cooperatively: the call fails
+ * with DSPARK_ERR_HIP if the device cannot host its persistent grid.
+ * ---------------------------------------------------------------------- */
+size_t dspark_accept_rate_workspace_bytes(int B, int A, int gamma, int V, int dtype);
+int dspark_accept_rate(const void* draft_logits, const void* target_logits, float* accept,
+                       const uint8_t* eval_mask, float* tau,
+                       int B, int A, int gamma, int V, int dtype,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Cumulative-product eval mask (page 1 §3.1 and §3.6).  For block (b, a)
+ * and block position k the label index is L = anchor + 1 + k, and
+ *
+ *     valid(k) = keep[b,a] != 0 && anchor >= 0 && L < seq_lens[b]
+ *                && (loss_mask == NULL || loss_mask[b, L] != 0)
+ *     eval_mask[b,a,k] = valid(0) && ... && valid(k)
+ *
+ *   anchor_pos [B, A] int32, keep_mask [B, A] uint8, seq_lens [B] int32
+ *   loss_mask  [B, S_stride] uint8 (nullable)
+ *   eval_mask  [B, A, gamma] uint8 (out, 0/1)
+ * A label index >= S_stride (possible only if seq_lens[b] > S_stride) is
+ * invalid and sets DSPARK_STATUS_BAD_LABEL.
+ * ---------------------------------------------------------------------- */
+int dspark_eval_mask(const int32_t* anchor_pos, const uint8_t* keep_mask,
+                     const int32_t* seq_lens, const uint8_t* loss_mask, uint8_t* eval_mask,
+                     int B, int A, int gamma, int S_stride,
+                     int32_t* dev_status, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSPARK_H */

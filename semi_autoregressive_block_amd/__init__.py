@@ -1,0 +1,241 @@
+"""DSpark draft-round hot path on MI355X: Python binding of libdspark.so.
+
+Each function marshals torch tensors (device memory, the current HIP stream)
+into one call of the C ABI declared in include/dspark.h and allocates the
+outputs and workspace it needs through torch's allocator.  All arithmetic
+runs in the library's HIP kernels; if the library is missing the import
+fails.
+
+Functions (same names and argument meaning as the C entry points):
+
+* ``block_attention``  — block-masked dual-source attention
+* ``markov_sample``    — Markov-head gamma-step sampler
+* ``accept_rate``      — TV accept rate (+ tau)
+* ``eval_mask``        — cumulative-product eval mask
+"""
+
+from __future__ import annotations
+
+import math
+
+import torch
+
+from . import _lib
+
+_LIB = _lib.load()
+
+__all__ = ["block_attention", "markov_sample", "accept_rate", "eval_mask",
+           "block_attention_workspace_bytes", "markov_sample_workspace_bytes",
+           "accept_rate_workspace_bytes", "last_error", "version", "DSparkError"]
+
+
+class DSparkError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        msg = _LIB.dspark_last_error().decode(errors="replace")
+        super().__init__(f"{where}: status {code}: {msg}")
+        self.code = code
+
+
+def last_error() -> str:
+    return _LIB.dspark_last_error().decode(errors="replace")
+
+
+def version() -> int:
+    return int(_LIB.dspark_version())
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _check(t, name, dtype=None, device=None, ndim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+
+
+def _dt(t):
+    if t.dtype == torch.bfloat16:
+        return _lib.BF16
+    if t.dtype == torch.float32:
+        return _lib.F32
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def _stream(device):
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _workspace(nbytes, device, workspace):
+    if nbytes == 0:
+        return None, 0
+    if workspace is not None:
+        if workspace.numel() * workspace.element_size() < nbytes:
+            raise ValueError(f"workspace too small: need {nbytes} bytes")
+        return workspace, workspace.numel() * workspace.element_size()
+    return torch.empty(nbytes, dtype=torch.uint8, device=device), nbytes
+
+
+def block_attention_workspace_bytes(B, A, gamma, Hq, Hkv, D, max_ctx) -> int:
+    return int(_LIB.dspark_block_attention_workspace_bytes(B, A, gamma, Hq, Hkv, D, max_ctx))
+
+
+def block_attention(q, k_ctx, v_ctx, ctx_offsets, k_blk, v_blk, anchor, keep, *, max_ctx,
+                    scale=None, out=None, lse=None, want_lse=False, status=None,
+                    workspace=None):
+    """q [B, A*gamma, Hq, D]; k_ctx/v_ctx [T, Hkv, D]; ctx_offsets [B+1] int32;
+    k_blk/v_blk [B, A*gamma, Hkv, D]; anchor [B, A] int32; keep [B, A] uint8.
+    Returns (out [B, A*gamma, Hq, D], lse [B, Hq, A*gamma] or None)."""
+    dev = q.device
+    _check(q, "q", (torch.bfloat16, torch.float32), ndim=4)
+    B, AG, Hq, D = q.shape
+    A = anchor.shape[1]
+    if A == 0 or AG % A:
+        raise ValueError("q rows must be A * gamma")
+    gamma = AG // A
+    for name, t in (("k_ctx", k_ctx), ("v_ctx", v_ctx)):
+        _check(t, name, q.dtype, dev, 3)
+    Hkv = k_ctx.shape[1]
+    for name, t in (("k_blk", k_blk), ("v_blk", v_blk)):
+        _check(t, name, q.dtype, dev, 4)
+        if tuple(t.shape) != (B, AG, Hkv, D):
+            raise ValueError(f"{name} shape {tuple(t.shape)} != {(B, AG, Hkv, D)}")
+    if tuple(k_ctx.shape[1:]) != (Hkv, D) or v_ctx.shape != k_ctx.shape:
+        raise ValueError("k_ctx / v_ctx must be [T, Hkv, D]")
+    _check(ctx_offsets, "ctx_offsets", torch.int32, dev, 1)
+    _check(anchor, "anchor", torch.int32, dev, 2)
+    _check(keep, "keep", torch.uint8, dev, 2)
+    if ctx_offsets.shape[0] != B + 1 or tuple(anchor.shape) != (B, A) or tuple(keep.shape) != (B, A):
+        raise ValueError("ctx_offsets / anchor / keep shapes do not match q")
+    if out is None:
+        out = torch.empty_like(q)
+    _check(out, "out", q.dtype, dev, 4)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq, AG), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _check(lse, "lse", torch.float32, dev, 3)
+    if status is not None:
+        _check(status, "status", torch.int32, dev)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    nbytes = block_attention_workspace_bytes(B, A, gamma, Hq, Hkv, D, max_ctx)
+    ws, wsb = _workspace(nbytes, dev, workspace)
+    rc = _LIB.dspark_block_attention(
+        _ptr(q), _ptr(k_ctx), _ptr(v_ctx), _ptr(ctx_offsets), _ptr(k_blk), _ptr(v_blk),
+        _ptr(anchor), _ptr(keep), _ptr(out), _ptr(lse), B, A, gamma, Hq, Hkv, D, int(max_ctx),
+        int(k_ctx.shape[0]), float(scale), _dt(q), _ptr(ws), wsb, _ptr(status), _stream(dev))
+    if rc != 0:
+        raise DSparkError(rc, "block_attention")
+    return out, lse
+
+
+def markov_sample_workspace_bytes(R, gamma, V, r, wdtype=_lib.BF16) -> int:
+    return int(_LIB.dspark_markov_sample_workspace_bytes(R, gamma, V, r, wdtype))
+
+
+def markov_sample(base, w1, w2, first_prev, *, temperature=0.0, seed=0, tokens=None,
+                  step_logits=None, want_step_logits=False, status=None, workspace=None):
+    """base [R, gamma, V] float32; w1 [V, r]; w2 [r, V] (same dtype, bf16 or
+    float32); first_prev [R] int32.  Returns (tokens [R, gamma] int32,
+    step_logits [R, gamma, V] float32 or None)."""
+    dev = base.device
+    _check(base, "base", torch.float32, ndim=3)
+    R, gamma, V = base.shape
+    _check(w1, "w1", (torch.bfloat16, torch.float32), dev, 2)
+    _check(w2, "w2", w1.dtype, dev, 2)
+    r = w1.shape[1]
+    if tuple(w1.shape) != (V, r) or tuple(w2.shape) != (r, V):
+        raise ValueError(f"w1 must be [V, r] and w2 [r, V]; got {tuple(w1.shape)}, {tuple(w2.shape)}")
+    _check(first_prev, "first_prev", torch.int32, dev, 1)
+    if first_prev.shape[0] != R:
+        raise ValueError("first_prev must have R entries")
+    if tokens is None:
+        tokens = torch.empty((R, gamma), dtype=torch.int32, device=dev)
+    _check(tokens, "tokens", torch.int32, dev, 2)
+    if step_logits is None and want_step_logits:
+        step_logits = torch.empty_like(base)
+    if step_logits is not None:
+        _check(step_logits, "step_logits", torch.float32, dev, 3)
+    if status is not None:
+        _check(status, "status", torch.int32, dev)
+    wdt = _dt(w1)
+    nbytes = markov_sample_workspace_bytes(R, gamma, V, r, wdt)
+    ws, wsb = _workspace(nbytes, dev, workspace)
+    rc = _LIB.dspark_markov_sample(
+        _ptr(base), _ptr(w1), _ptr(w2), _ptr(first_prev), _ptr(tokens), _ptr(step_logits),
+        R, gamma, V, r, wdt, float(temperature), int(seed) & (2**64 - 1), _ptr(ws), wsb,
+        _ptr(status), _stream(dev))
+    if rc != 0:
+        raise DSparkError(rc, "markov_sample")
+    return tokens, step_logits
+
+
+def accept_rate_workspace_bytes(B, A, gamma, V, dtype=_lib.BF16) -> int:
+    return int(_LIB.dspark_accept_rate_workspace_bytes(B, A, gamma, V, dtype))
+
+
+def accept_rate(draft, target, *, eval_mask=None, want_tau=False, accept=None, tau=None,
+                workspace=None):
+    """draft, target [B, A, gamma, V] (bf16 or float32); eval_mask [B, A, gamma]
+    uint8 (optional, used for tau).  Returns (accept [B, A, gamma] float32,
+    tau [B, A] float32 or None)."""
+    dev = draft.device
+    _check(draft, "draft", (torch.bfloat16, torch.float32), ndim=4)
+    _check(target, "target", draft.dtype, dev, 4)
+    if target.shape != draft.shape:
+        raise ValueError("draft and target shapes differ")
+    B, A, gamma, V = draft.shape
+    if accept is None:
+        accept = torch.empty((B, A, gamma), dtype=torch.float32, device=dev)
+    _check(accept, "accept", torch.float32, dev, 3)
+    if eval_mask is not None:
+        _check(eval_mask, "eval_mask", torch.uint8, dev, 3)
+    if tau is None and want_tau:
+        tau = torch.empty((B, A), dtype=torch.float32, device=dev)
+    if tau is not None:
+        _check(tau, "tau", torch.float32, dev, 2)
+    dt = _dt(draft)
+    nbytes = accept_rate_workspace_bytes(B, A, gamma, V, dt)
+    ws, wsb = _workspace(nbytes, dev, workspace)
+    rc = _LIB.dspark_accept_rate(_ptr(draft), _ptr(target), _ptr(accept), _ptr(eval_mask),
+                                 _ptr(tau), B, A, gamma, V, dt, _ptr(ws), wsb, _stream(dev))
+    if rc != 0:
+        raise DSparkError(rc, "accept_rate")
+    return accept, tau
+
+
+def eval_mask(anchor, keep, seq_lens, loss_mask=None, *, gamma, out=None, status=None):
+    """anchor [B, A] int32; keep [B, A] uint8; seq_lens [B] int32; loss_mask
+    [B, S_stride] uint8 or None.  Returns uint8 [B, A, gamma]."""
+    dev = anchor.device
+    _check(anchor, "anchor", torch.int32, ndim=2)
+    B, A = anchor.shape
+    _check(keep, "keep", torch.uint8, dev, 2)
+    _check(seq_lens, "seq_lens", torch.int32, dev, 1)
+    if tuple(keep.shape) != (B, A) or seq_lens.shape[0] != B:
+        raise ValueError("keep / seq_lens shapes do not match anchor")
+    S_stride = 0
+    if loss_mask is not None:
+        _check(loss_mask, "loss_mask", torch.uint8, dev, 2)
+        if loss_mask.shape[0] != B:
+            raise ValueError("loss_mask must have B rows")
+        S_stride = loss_mask.shape[1]
+    if out is None:
+        out = torch.empty((B, A, gamma), dtype=torch.uint8, device=dev)
+    _check(out, "out", torch.uint8, dev, 3)
+    if status is not None:
+        _check(status, "status", torch.int32, dev)
+    rc = _LIB.dspark_eval_mask(_ptr(anchor), _ptr(keep), _ptr(seq_lens), _ptr(loss_mask),
+                               _ptr(out), B, A, gamma, S_stride, _ptr(status), _stream(dev))
+    if rc != 0:
+        raise DSparkError(rc, "eval_mask")
+    return out

@@ -1,0 +1,405 @@
+// Markov-head sequential sampler (page 1, "03 · DSpark 建模", §3.7, the
+// paper's Eq. 5; page 2, "从 DFlash 到 dLLM Self-Spec（三）", §3.4 and
+// §3.8.2).
+//
+// For gamma steps, every row takes l = base[:, i, :] + W1[prev] @ W2 over the
+// whole vocabulary, picks argmax l (greedy) or argmax l/T + Gumbel, and feeds
+// the token forward.  Each step is one kernel launch:
+//
+// * The rank-r x V product is an MFMA contraction over the rank (bf16 in,
+//   fp32 accumulate, v_mfma_f32_16x16x32_bf16).  W2 is stored [r, V] with the
+//   vocabulary contiguous, so each lane loads an 8 (rank) x 4 (vocab) bf16
+//   block with 8-byte coalesced loads and transposes it in registers
+//   (v_perm); MFMA column slot n of product j then stands for vocabulary
+//   index tile + 4n + j.  E = W1[prev] (the A operand) is gathered once per
+//   step into LDS and shared by the workgroup's four waves.
+// * Every wave owns a balanced contiguous vocabulary range (the step streams
+//   W2 exactly once), all rows of its row group, and keeps a running
+//   (value, index) best per row in registers: the base add, the optional
+//   step-logit store, the Philox Gumbel perturbation and the argmax are fused
+//   into the epilogue of each 64-column sub-tile.
+// * Row maxima are folded with 64-bit keys (order-preserving float bits,
+//   then the inverted index so ties go to the lowest index): 16-lane
+//   shuffles, an LDS atomic max across the waves, then one global atomic max
+//   per row, skipped when the current global key is already larger.  The
+//   next step decodes prev from those keys on the device; there is no host
+//   round trip inside the gamma loop.
+#include "common.h"
+#include "philox.h"
+
+using namespace dspark;
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kSubTile = 64;  // vocabulary columns per wave sub-tile (16 lanes x 4)
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
+  const uint32_t lo = __shfl_xor((uint32_t)v, m, kWave);
+  const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), m, kWave);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ int decode_prev(const uint64_t* keys_prev, const int32_t* first_prev,
+                                           int row, int V, int32_t* status) {
+  int p;
+  if (keys_prev) {
+    p = (int)argmax_key_index(keys_prev[row]);
+  } else {
+    p = first_prev[row];
+  }
+  if (p < 0 || p >= V) {
+    status_or(status, DSPARK_STATUS_BAD_TOKEN);
+    p = 0;
+  }
+  return p;
+}
+
+__device__ __forceinline__ void fold_key_global(uint64_t* dst, uint64_t key) {
+  const uint64_t cur = __hip_atomic_load(dst, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (key > cur) atomicMax((unsigned long long*)dst, (unsigned long long)key);
+}
+
+// ----------------------------------------------------------------- MFMA path
+// NMB: 16-row m-blocks per workgroup (rows per row group = 16*NMB, shared by
+// all four waves).  KS: maximum number of 32-wide rank steps (r <= 32*KS).
+template <int NMB, int KS>
+__global__ __launch_bounds__(kThreads) void markov_step_mfma(
+    const float* __restrict__ base, const uint16_t* __restrict__ w1,
+    const uint16_t* __restrict__ w2, const int32_t* __restrict__ first_prev,
+    const uint64_t* __restrict__ keys_prev, uint64_t* __restrict__ keys_out,
+    float* __restrict__ step_logits, int R, int gamma, int V, int r, int step, float invT,
+    int greedy, uint32_t seed_lo, uint32_t seed_hi, int32_t* __restrict__ status) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  constexpr int RW = 16 * NMB;
+  const int rpad = ((r + 31) / 32) * 32;  // rank rounded up to a whole step
+  const int estride = rpad + 8;           // bf16 elements per LDS row (+16 B: fewer bank conflicts)
+  uint16_t* E = (uint16_t*)smem;
+  uint64_t* rowkey = (uint64_t*)(smem + (size_t)RW * estride * 2);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  const int row0 = blockIdx.y * RW;
+  const int ks = rpad / 32;
+
+  // ---- gather E = W1[prev] for this row group into LDS (zero-padded)
+  for (int c = threadIdx.x; c < RW * (estride / 8); c += kThreads) {
+    const int rr = c / (estride / 8), kc = (c % (estride / 8)) * 8;
+    const int row = row0 + rr;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (row < R && kc < r) {
+      const int p = decode_prev(keys_prev, first_prev, row, V, nullptr);
+      v = *(const u32x4*)(w1 + (int64_t)p * r + kc);
+    }
+    *(u32x4*)(E + rr * estride + kc) = v;
+  }
+  for (int i = threadIdx.x; i < RW; i += kThreads) rowkey[i] = 0ull;
+  if (threadIdx.x < RW && row0 + threadIdx.x < R && blockIdx.x == 0)
+    decode_prev(keys_prev, first_prev, row0 + threadIdx.x, V, status);  // flag bad tokens once
+  __syncthreads();
+
+  // ---- this wave's vocabulary range, in quads of 4 columns
+  const int64_t nq = V / 4;
+  const int64_t nw = (int64_t)gridDim.x * 4;
+  const int64_t gw = (int64_t)blockIdx.x * 4 + wave;
+  const int64_t q0 = gw * nq / nw, q1 = (gw + 1) * nq / nw;
+
+  float best_z[NMB][4];
+  uint32_t best_v[NMB][4];
+#pragma unroll
+  for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { best_z[mb][i] = -INFINITY; best_v[mb][i] = 0xffffffffu; }
+
+  for (int64_t qt = q0; qt < q1; qt += kSubTile / 4) {
+    const int64_t myq = qt + n;          // this lane's quad
+    const bool colok = myq < q1;
+    const int64_t v0 = myq * 4;          // first of this lane's 4 columns
+    f32x4 acc[NMB][4];
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[mb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    for (int kk = 0; kk < KS; ++kk) {
+      if (kk >= ks) break;
+      u32x2 raw[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int k = kk * 32 + g * 8 + i;
+        raw[i] = (colok && k < r) ? *(const u32x2*)(w2 + (int64_t)k * V + v0) : u32x2{0u, 0u};
+      }
+      u32x4 b[4];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        b[0][p] = pack_lo(raw[2 * p].x, raw[2 * p + 1].x);
+        b[1][p] = pack_hi(raw[2 * p].x, raw[2 * p + 1].x);
+        b[2][p] = pack_lo(raw[2 * p].y, raw[2 * p + 1].y);
+        b[3][p] = pack_hi(raw[2 * p].y, raw[2 * p + 1].y);
+      }
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb) {
+        const u32x4 a = *(const u32x4*)(E + (mb * 16 + n) * estride + kk * 32 + g * 8);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[mb][j] = mfma16x16x32(a, b[j], acc[mb][j]);
+      }
+    }
+
+    // ---- epilogue: base add, optional store, Gumbel, running argmax
+    if (colok) {
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = row0 + mb * 16 + g * 4 + i;
+          if (row < R) {
+            const int64_t off = ((int64_t)row * gamma + step) * V + v0;
+            const f32x4 bs = *(const f32x4*)(base + off);
+            f32x4 l;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) l[j] = acc[mb][j][i] + bs[j];
+            if (step_logits) *(f32x4*)(step_logits + off) = l;
+            f32x4 z = l;
+            if (!greedy) {
+              const u32x4 x = philox4x32_10(u32x4{(uint32_t)myq, (uint32_t)step, (uint32_t)row, 0u},
+                                            seed_lo, seed_hi);
+#pragma unroll
+              for (int j = 0; j < 4; ++j) z[j] = fmaf(l[j], invT, gumbel_from_bits(x[j]));
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              if (z[j] > best_z[mb][i]) { best_z[mb][i] = z[j]; best_v[mb][i] = (uint32_t)(v0 + j); }
+            }
+          }
+        }
+      }
+    }
+  }
+
+  // ---- fold: 16 lanes sharing a row, then the four waves, then the grid
+#pragma unroll
+  for (int mb = 0; mb < NMB; ++mb) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint64_t key = best_v[mb][i] == 0xffffffffu ? 0ull : argmax_key(best_z[mb][i], best_v[mb][i]);
+#pragma unroll
+      for (int m = 1; m < 16; m <<= 1) {
+        const uint64_t o = shfl_xor_u64(key, m);
+        key = o > key ? o : key;
+      }
+      if (n == 0 && key) atomicMax((unsigned long long*)&rowkey[mb * 16 + g * 4 + i], (unsigned long long)key);
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < RW) {
+    const int row = row0 + threadIdx.x;
+    const uint64_t key = rowkey[threadIdx.x];
+    if (row < R && key) fold_key_global(keys_out + row, key);
+  }
+}
+
+// ------------------------------------------------------------- vector path
+// float32 (or unaligned bf16) weights: one thread per quad of columns,
+// 16 rows per pass with E in LDS, fp32 FMAs.
+constexpr int kRowChunk = 16;
+
+template <bool kBf16W>
+__global__ __launch_bounds__(kThreads) void markov_step_valu(
+    const float* __restrict__ base, const void* __restrict__ w1v, const void* __restrict__ w2v,
+    const int32_t* __restrict__ first_prev, const uint64_t* __restrict__ keys_prev,
+    uint64_t* __restrict__ keys_out, float* __restrict__ step_logits, int R, int gamma, int V,
+    int r, int step, float invT, int greedy, uint32_t seed_lo, uint32_t seed_hi,
+    int32_t* __restrict__ status) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  float* E = (float*)smem;                                        // [kRowChunk][r]
+  uint64_t* rowkey = (uint64_t*)(smem + (size_t)kRowChunk * r * 4);  // [kRowChunk]
+  auto w1 = [&](int64_t i) -> float {
+    return kBf16W ? __uint_as_float((uint32_t)((const uint16_t*)w1v)[i] << 16) : ((const float*)w1v)[i];
+  };
+  auto w2 = [&](int64_t i) -> float {
+    return kBf16W ? __uint_as_float((uint32_t)((const uint16_t*)w2v)[i] << 16) : ((const float*)w2v)[i];
+  };
+  const int row0 = blockIdx.y * kRowChunk;
+  for (int c = threadIdx.x; c < kRowChunk * r; c += kThreads) {
+    const int rr = c / r, k = c % r, row = row0 + rr;
+    float v = 0.f;
+    if (row < R) v = w1((int64_t)decode_prev(keys_prev, first_prev, row, V, nullptr) * r + k);
+    E[c] = v;
+  }
+  if (threadIdx.x < kRowChunk) rowkey[threadIdx.x] = 0ull;
+  if (threadIdx.x < kRowChunk && row0 + threadIdx.x < R && blockIdx.x == 0)
+    decode_prev(keys_prev, first_prev, row0 + threadIdx.x, V, status);
+  __syncthreads();
+
+  const int64_t nq = (V + 3) / 4;
+  const int64_t q0 = (int64_t)blockIdx.x * nq / gridDim.x, q1 = (int64_t)(blockIdx.x + 1) * nq / gridDim.x;
+  float best_z[kRowChunk];
+  uint32_t best_v[kRowChunk];
+#pragma unroll
+  for (int i = 0; i < kRowChunk; ++i) { best_z[i] = -INFINITY; best_v[i] = 0xffffffffu; }
+  for (int64_t q = q0 + threadIdx.x; q < q1; q += kThreads) {
+    for (int j = 0; j < 4; ++j) {
+      const int64_t v = q * 4 + j;
+      if (v >= V) break;
+      float acc[kRowChunk];
+#pragma unroll
+      for (int i = 0; i < kRowChunk; ++i) acc[i] = 0.f;
+      for (int k = 0; k < r; ++k) {
+        const float w = w2((int64_t)k * V + v);
+#pragma unroll
+        for (int i = 0; i < kRowChunk; ++i) acc[i] = fmaf(E[i * r + k], w, acc[i]);
+      }
+      uint32_t x = 0;
+#pragma unroll
+      for (int i = 0; i < kRowChunk; ++i) {
+        const int row = row0 + i;
+        if (row >= R) break;
+        const int64_t off = ((int64_t)row * gamma + step) * V + v;
+        const float l = base[off] + acc[i];
+        if (step_logits) step_logits[off] = l;
+        float z = l;
+        if (!greedy) {
+          const u32x4 xs = philox4x32_10(u32x4{(uint32_t)q, (uint32_t)step, (uint32_t)row, 0u}, seed_lo, seed_hi);
+          x = xs[j];
+          z = fmaf(l, invT, gumbel_from_bits(x));
+        }
+        if (z > best_z[i]) { best_z[i] = z; best_v[i] = (uint32_t)v; }
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kRowChunk; ++i) {
+    uint64_t key = best_v[i] == 0xffffffffu ? 0ull : argmax_key(best_z[i], best_v[i]);
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+      const uint64_t o = shfl_xor_u64(key, m);
+      key = o > key ? o : key;
+    }
+    if ((threadIdx.x & 63) == 0 && key) atomicMax((unsigned long long*)&rowkey[i], (unsigned long long)key);
+  }
+  __syncthreads();
+  if (threadIdx.x < kRowChunk) {
+    const int row = row0 + threadIdx.x;
+    const uint64_t key = rowkey[threadIdx.x];
+    if (row < R && key) fold_key_global(keys_out + row, key);
+  }
+}
+
+__global__ void zero_u64_kernel(uint64_t* p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0ull;
+}
+
+__global__ void finalize_tokens_kernel(const uint64_t* __restrict__ keys, int32_t* __restrict__ tokens,
+                                       int R, int gamma, int V, int32_t* status) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // over [R, gamma]
+  if (i >= (int64_t)R * gamma) return;
+  const int row = (int)(i / gamma), step = (int)(i % gamma);
+  uint32_t t = argmax_key_index(keys[(int64_t)step * R + row]);
+  if (t >= (uint32_t)V) { status_or(status, DSPARK_STATUS_BAD_TOKEN); t = 0; }
+  tokens[i] = (int32_t)t;
+}
+
+int cu_count() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
+  return cus;
+}
+
+template <int NMB, int KS>
+hipError_t launch_mfma(int grid_x, int grid_y, hipStream_t s, const float* base, const uint16_t* w1,
+                       const uint16_t* w2, const int32_t* first_prev, const uint64_t* kp,
+                       uint64_t* ko, float* step_logits, int R, int gamma, int V, int r, int step,
+                       float invT, int greedy, uint32_t slo, uint32_t shi, int32_t* st) {
+  const int rpad = ((r + 31) / 32) * 32;
+  const size_t shm = (size_t)16 * NMB * (rpad + 8) * 2 + (size_t)16 * NMB * 8;
+  auto kern = markov_step_mfma<NMB, KS>;
+  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3(grid_x, grid_y), dim3(kThreads), shm, s, base, w1, w2, first_prev,
+                     kp, ko, step_logits, R, gamma, V, r, step, invT, greedy, slo, shi, st);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+extern "C" size_t dspark_markov_sample_workspace_bytes(int R, int gamma, int V, int r, int wdtype) {
+  (void)V; (void)r; (void)wdtype;
+  if (R <= 0 || gamma <= 0) return 0;
+  return (size_t)R * gamma * sizeof(uint64_t);
+}
+
+extern "C" int dspark_markov_sample(const float* base_logits, const void* w1, const void* w2,
+                                   const int32_t* first_prev, int32_t* tokens, float* step_logits,
+                                   int R, int gamma, int V, int r, int wdtype, float temperature,
+                                   uint64_t seed, void* ws, size_t ws_bytes, int32_t* dev_status,
+                                   void* stream) {
+  using namespace dspark_host;
+  if (R < 0 || gamma < 0) return fail(DSPARK_ERR_INVALID_ARG, "markov_sample: negative dimension");
+  if (V < 1 || r < 1 || r > 1024)
+    return fail(DSPARK_ERR_INVALID_ARG, "markov_sample: need V >= 1 and 1 <= r <= 1024 (V=%d r=%d)", V, r);
+  if (gamma > 1024) return fail(DSPARK_ERR_INVALID_ARG, "markov_sample: gamma > 1024");
+  if (wdtype != DSPARK_BF16 && wdtype != DSPARK_F32)
+    return fail(DSPARK_ERR_INVALID_ARG, "markov_sample: unknown wdtype %d", wdtype);
+  if (!(temperature >= 0.f) || temperature == INFINITY)
+    return fail(DSPARK_ERR_INVALID_ARG, "markov_sample: temperature must be finite and >= 0");
+  if ((int64_t)R * gamma == 0) return ok();
+  if (!base_logits || !w1 || !w2 || !first_prev || !tokens)
+    return fail(DSPARK_ERR_INVALID_ARG, "markov_sample: null required pointer");
+  const size_t need = dspark_markov_sample_workspace_bytes(R, gamma, V, r, wdtype);
+  if (ws_bytes < need || !ws)
+    return fail(DSPARK_ERR_WORKSPACE, "markov_sample: workspace %zu bytes < %zu", ws_bytes, need);
+  if ((uintptr_t)ws % 8) return fail(DSPARK_ERR_INVALID_ARG, "markov_sample: workspace not 8-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  uint64_t* keys = (uint64_t*)ws;  // [gamma][R]
+  const int64_t nk = (int64_t)R * gamma;
+  hipLaunchKernelGGL(zero_u64_kernel, dim3((unsigned)((nk + 255) / 256)), dim3(256), 0, s, keys, nk);
+  const int greedy = temperature == 0.f;
+  const float invT = greedy ? 1.f : 1.f / temperature;
+  const uint32_t slo = (uint32_t)seed, shi = (uint32_t)(seed >> 32);
+  const int cus = cu_count();
+  if (cus <= 0) return fail(DSPARK_ERR_HIP, "markov_sample: device query failed");
+
+  const bool bf = wdtype == DSPARK_BF16;
+  const bool mfma_ok = bf && V % 8 == 0 && r % 8 == 0 && r <= 512 && (uintptr_t)w1 % 16 == 0 &&
+                       (uintptr_t)w2 % 16 == 0 && (uintptr_t)base_logits % 16 == 0 &&
+                       (!step_logits || (uintptr_t)step_logits % 16 == 0);
+  for (int step = 0; step < gamma; ++step) {
+    const uint64_t* kp = step == 0 ? nullptr : keys + (int64_t)(step - 1) * R;
+    uint64_t* ko = keys + (int64_t)step * R;
+    hipError_t e = hipSuccess;
+    if (mfma_ok) {
+      // 64-row groups (grid.y); one workgroup per compute unit and two per
+      // unit when a single row group exists, each wave a balanced vocabulary
+      // range
+      const int gy = (R + 63) / 64;
+      int gx = gy == 1 ? 2 * cus : cus;
+      const int64_t quads = V / 4;
+      if ((int64_t)gx * 4 > quads) gx = (int)((quads + 3) / 4);
+      if (gx < 1) gx = 1;
+      if (r <= 256)
+        e = launch_mfma<4, 8>(gx, gy, s, base_logits, (const uint16_t*)w1, (const uint16_t*)w2, first_prev, kp, ko, step_logits, R, gamma, V, r, step, invT, greedy, slo, shi, dev_status);
+      else
+        e = launch_mfma<4, 16>(gx, gy, s, base_logits, (const uint16_t*)w1, (const uint16_t*)w2, first_prev, kp, ko, step_logits, R, gamma, V, r, step, invT, greedy, slo, shi, dev_status);
+    } else {
+      const int gy = (R + kRowChunk - 1) / kRowChunk;
+      int gx = 2 * cus;
+      const int64_t quads = (V + 3) / 4;
+      if ((int64_t)gx * kThreads > quads) gx = (int)((quads + kThreads - 1) / kThreads);
+      if (gx < 1) gx = 1;
+      const size_t shm = (size_t)kRowChunk * r * 4 + kRowChunk * 8;
+      if (bf) {
+        (void)hipFuncSetAttribute((const void*)markov_step_valu<true>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+        hipLaunchKernelGGL(markov_step_valu<true>, dim3(gx, gy), dim3(kThreads), shm, s, base_logits, w1, w2, first_prev, kp, ko, step_logits, R, gamma, V, r, step, invT, greedy, slo, shi, dev_status);
+      } else {
+        (void)hipFuncSetAttribute((const void*)markov_step_valu<false>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+        hipLaunchKernelGGL(markov_step_valu<false>, dim3(gx, gy), dim3(kThreads), shm, s, base_logits, w1, w2, first_prev, kp, ko, step_logits, R, gamma, V, r, step, invT, greedy, slo, shi, dev_status);
+      }
+      e = hipGetLastError();
+    }
+    if (e != hipSuccess) return fail(DSPARK_ERR_HIP, "markov_sample step %d: %s", step, hipGetErrorString(e));
+  }
+  hipLaunchKernelGGL(finalize_tokens_kernel, dim3((unsigned)((nk + 255) / 256)), dim3(256), 0, s, keys,
+                     tokens, R, gamma, V, dev_status);
+  return check_launch("markov_sample");
+}

@@ -1,0 +1,111 @@
+"""The C-ABI library: exports and host-side validation (CPU only, no compute
+calls reach the GPU: every case here is rejected before any HIP call)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dspark.h")
+LIB = os.path.join(ROOT, "semi_autoregressive_block_amd", "libdspark.so")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(dspark_\w+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libdspark.so is not built (run __graft_entry__.build())")
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(
+        "_dspark_lib", os.path.join(ROOT, "semi_autoregressive_block_amd", "_lib.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod, mod.load(LIB)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    mod, L = lib
+    names = _declared()
+    assert len(names) == 9, names
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(mod.SIGNATURES)
+
+
+def test_version_and_empty_error(lib):
+    _, L = lib
+    assert L.dspark_version() >= 100
+    assert isinstance(L.dspark_last_error(), bytes)
+
+
+def test_workspace_queries(lib):
+    _, L = lib
+    # multi-chunk attention needs partials; one chunk only needs counters
+    big = L.dspark_block_attention_workspace_bytes(128, 1, 16, 32, 8, 128, 8192)
+    small = L.dspark_block_attention_workspace_bytes(128, 1, 16, 32, 8, 128, 512)
+    assert big > small > 0
+    assert L.dspark_block_attention_workspace_bytes(1, 1, 1, 3, 2, 128, 10) == 0  # Hq % Hkv
+    assert L.dspark_markov_sample_workspace_bytes(64, 16, 151936, 256, 1) == 64 * 16 * 8
+    assert L.dspark_accept_rate_workspace_bytes(4, 512, 8, 151936, 1) > 0
+
+
+NULL = None
+
+
+def test_attention_rejects_bad_arguments_before_any_hip_call(lib):
+    mod, L = lib
+    p = ctypes.c_void_p(16)  # never dereferenced: validation fails first
+    def call(**kw):
+        a = dict(B=1, A=1, gamma=8, Hq=4, Hkv=2, D=128, max_ctx=16, total_ctx=16, scale=0.1, dtype=1)
+        a.update(kw)
+        return L.dspark_block_attention(p, p, p, p, p, p, p, p, p, NULL, a["B"], a["A"], a["gamma"],
+                                        a["Hq"], a["Hkv"], a["D"], a["max_ctx"], a["total_ctx"],
+                                        a["scale"], a["dtype"], NULL, 0, NULL, NULL)
+    assert call(D=96) == mod.ERR_INVALID_ARG and b"D must be" in L.dspark_last_error()
+    assert call(Hq=3) == mod.ERR_INVALID_ARG
+    assert call(gamma=65) == mod.ERR_INVALID_ARG
+    assert call(dtype=7) == mod.ERR_INVALID_ARG
+    assert call(scale=0.0) == mod.ERR_INVALID_ARG
+    assert call(scale=float("nan")) == mod.ERR_INVALID_ARG
+    assert call(B=-1) == mod.ERR_INVALID_ARG
+    assert call(B=0) == mod.OK  # empty: nothing to do, nothing enqueued
+    assert L.dspark_block_attention(NULL, p, p, p, p, p, p, p, p, NULL, 1, 1, 8, 4, 2, 128, 16, 16,
+                                    0.1, 1, NULL, 0, NULL, NULL) == mod.ERR_INVALID_ARG
+
+
+def test_markov_rejects_bad_arguments(lib):
+    mod, L = lib
+    p = ctypes.c_void_p(16)
+    def call(R=4, gamma=2, V=64, r=8, wdtype=1, T=0.0, ws=p, wsb=1 << 20):
+        return L.dspark_markov_sample(p, p, p, p, p, NULL, R, gamma, V, r, wdtype, T, 0, ws, wsb,
+                                      NULL, NULL)
+    assert call(r=0) == mod.ERR_INVALID_ARG
+    assert call(r=2048) == mod.ERR_INVALID_ARG
+    assert call(V=0) == mod.ERR_INVALID_ARG
+    assert call(T=-1.0) == mod.ERR_INVALID_ARG
+    assert call(T=float("inf")) == mod.ERR_INVALID_ARG
+    assert call(wdtype=5) == mod.ERR_INVALID_ARG
+    assert call(gamma=2000) == mod.ERR_INVALID_ARG
+    assert call(wsb=8) == mod.ERR_WORKSPACE
+    assert call(ws=NULL) == mod.ERR_WORKSPACE
+    assert call(R=0) == mod.OK
+
+
+def test_accept_rate_and_eval_mask_reject_bad_arguments(lib):
+    mod, L = lib
+    p = ctypes.c_void_p(16)
+    assert L.dspark_accept_rate(p, p, p, NULL, NULL, 1, 1, 1, 1, 1, p, 1 << 20, NULL) == mod.ERR_INVALID_ARG
+    assert L.dspark_accept_rate(p, p, p, NULL, NULL, 1, 1, 1, 64, 3, p, 1 << 20, NULL) == mod.ERR_INVALID_ARG
+    assert L.dspark_accept_rate(p, p, p, NULL, NULL, 1, 1, 1, 64, 1, p, 0, NULL) == mod.ERR_WORKSPACE
+    assert L.dspark_accept_rate(p, p, p, NULL, NULL, 0, 1, 1, 64, 1, NULL, 0, NULL) == mod.OK
+    assert L.dspark_eval_mask(p, p, p, NULL, p, -1, 1, 1, 0, NULL, NULL) == mod.ERR_INVALID_ARG
+    assert L.dspark_eval_mask(NULL, p, p, NULL, p, 1, 1, 1, 0, NULL, NULL) == mod.ERR_INVALID_ARG
+    assert L.dspark_eval_mask(p, p, p, p, p, 1, 1, 1, 0, NULL, NULL) == mod.ERR_INVALID_ARG  # S_stride
+    assert L.dspark_eval_mask(p, p, p, NULL, p, 0, 1, 1, 0, NULL, NULL) == mod.OK

@@ -1,0 +1,108 @@
+"""TV accept rate (+ tau) on the GPU vs the oracle.
+
+Tolerance: 2e-2 absolute for bf16 inputs and 1e-4 for float32 inputs; the
+kernel computes in float32 throughout, so both cases are in practice far
+tighter (asserted separately below where it matters)."""
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from gpu_util import as_dtype, dev, host_bits
+from oracle import accept_rate as OR
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": 2e-2, "f32": 1e-4}
+
+
+@pytest.fixture(scope="module")
+def dsp():
+    import semi_autoregressive_block_amd as m
+    return m
+
+
+def _pair(seed, shape, dtype, noise=1.0):
+    rng = np.random.default_rng(seed)
+    d = rng.standard_normal(shape, dtype=np.float32) * 3
+    t = d + rng.standard_normal(shape, dtype=np.float32) * np.float32(noise) * \
+        rng.uniform(0.1, 3, size=shape[:-1] + (1,)).astype(np.float32)
+    if dtype == "bf16":
+        d, t = W.to_bf16_bits(d), W.to_bf16_bits(t)
+    return d, t
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("V", [2, 7, 1000, 4096, 20000, 151936])
+def test_small_shapes(dsp, dtype, V):
+    shape = (2, 3, 4, V) if V < 100000 else (1, 2, 3, V)
+    d, t = _pair(V, shape, dtype)
+    acc, tau = dsp.accept_rate(as_dtype(d, dtype), as_dtype(t, dtype), want_tau=True)
+    dv, tv = W.values(d, dtype), W.values(t, dtype)
+    ref = OR.accept_rate(dv, tv)
+    err = np.abs(acc.cpu().numpy() - ref).max()
+    assert err < TOL[dtype], err
+    assert err < 2e-5  # float32 softmaxes: far inside the bar
+    np.testing.assert_allclose(tau.cpu().numpy(), OR.tau(ref, np.ones(ref.shape)), atol=1e-4)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_identical_and_symmetric(dsp, dtype):
+    d, t = _pair(3, (2, 2, 8, 151936 if dtype == "bf16" else 30000), dtype)
+    a1, _ = dsp.accept_rate(as_dtype(d, dtype), as_dtype(d, dtype))
+    assert np.abs(a1.cpu().numpy() - 1.0).max() < 2e-5
+    a2, _ = dsp.accept_rate(as_dtype(d, dtype), as_dtype(t, dtype))
+    a3, _ = dsp.accept_rate(as_dtype(t, dtype), as_dtype(d, dtype))
+    assert np.abs(a2.cpu().numpy() - a3.cpu().numpy()).max() < 2e-5
+
+
+def test_disjoint_spikes(dsp):
+    d = np.zeros((1, 1, 2, 64), np.float32)
+    t = np.zeros((1, 1, 2, 64), np.float32)
+    d[..., 3] = 50
+    t[..., 40] = 50
+    acc, _ = dsp.accept_rate(dev(d), dev(t))
+    assert acc.cpu().numpy().max() < 1e-6
+
+
+def test_tau_with_eval_mask(dsp):
+    d, t = _pair(11, (3, 5, 8, 2048), "bf16")
+    rng = np.random.default_rng(12)
+    m = (rng.random((3, 5, 8)) < 0.85).astype(np.uint8)
+    m = np.cumprod(m, axis=-1).astype(np.uint8)
+    acc, tau = dsp.accept_rate(as_dtype(d, "bf16"), as_dtype(t, "bf16"), eval_mask=dev(m),
+                               want_tau=True)
+    ref = OR.accept_rate(W.bf16_to_f32(d), W.bf16_to_f32(t))
+    np.testing.assert_allclose(tau.cpu().numpy(), OR.tau(ref, m), atol=1e-4)
+
+
+def test_deterministic(dsp):
+    d, t = _pair(13, (2, 4, 8, 151936), "bf16")
+    a, b = as_dtype(d, "bf16"), as_dtype(t, "bf16")
+    x1, _ = dsp.accept_rate(a, b)
+    x2, _ = dsp.accept_rate(a, b)
+    assert torch.equal(x1, x2)
+
+
+def test_config4_full_size_sampled(dsp):
+    """Full workload: 4 x 512 x 8 rows of V = 151936 bf16 (2 x 4.98 GB), the
+    launch the bench times; 40 sampled blocks checked against the oracle,
+    accept and tau; the rest checked for range."""
+    inp = W.config4_device(torch, torch.device("cuda:0"))
+    m = inp["mask"]
+    em = dsp.eval_mask(dev(m.anchor), dev(m.keep), dev(m.seq_lens), dev(m.loss_mask), gamma=8)
+    acc, tau = dsp.accept_rate(inp["draft"], inp["target"], eval_mask=em, want_tau=True)
+    acc_h, tau_h, em_h = acc.cpu().numpy(), tau.cpu().numpy(), em.cpu().numpy()
+    assert np.all((acc_h >= 0) & (acc_h <= 1))
+    rng = np.random.default_rng(44)
+    for _ in range(40):
+        b, a = int(rng.integers(0, 4)), int(rng.integers(0, 512))
+        dv = W.bf16_to_f32(host_bits(inp["draft"][b, a]))
+        tv = W.bf16_to_f32(host_bits(inp["target"][b, a]))
+        ref = OR.accept_rate(dv, tv)
+        assert np.abs(acc_h[b, a] - ref).max() < TOL["bf16"]
+        assert np.abs(acc_h[b, a] - ref).max() < 2e-5
+        assert abs(tau_h[b, a] - OR.tau(ref, em_h[b, a])) < 1e-4
+    del inp
+    torch.cuda.empty_cache()

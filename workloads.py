@@ -302,3 +302,95 @@ def device_normal(torch, gen, shape, std, dtype, device, chunk=1 << 27):
             x.mul_(std)
         flat[s:e].copy_(x)
     return out
+
+
+def _gen(torch, device, seed):
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return g
+
+
+def config2_device(torch, device):
+    """Training-style attention inputs at full size: Q [1, 4096, 32, 128],
+    K/V context [4096, 8, 128], K/V own blocks [1, 4096, 8, 128], all i.i.d.
+    N(0, 1) rounded to bf16, drawn on `device`; anchors from
+    config2_structure()."""
+    c = CONFIG2
+    anchor, keep = config2_structure()
+    g = _gen(torch, device, SEED_BASE + 2)
+    bf = torch.bfloat16
+    AG = c["A"] * c["gamma"]
+    out = dict(
+        q=device_normal(torch, g, (c["B"], AG, c["Hq"], c["D"]), 1.0, bf, device),
+        k_ctx=device_normal(torch, g, (c["S"], c["Hkv"], c["D"]), 1.0, bf, device),
+        v_ctx=device_normal(torch, g, (c["S"], c["Hkv"], c["D"]), 1.0, bf, device),
+        k_blk=device_normal(torch, g, (c["B"], AG, c["Hkv"], c["D"]), 1.0, bf, device),
+        v_blk=device_normal(torch, g, (c["B"], AG, c["Hkv"], c["D"]), 1.0, bf, device),
+        ctx_offsets=torch.tensor([0, c["S"]], dtype=torch.int32, device=device),
+        anchor=torch.from_numpy(anchor).to(device), keep=torch.from_numpy(keep).to(device),
+        anchor_host=anchor, keep_host=keep, max_ctx=c["S"])
+    return out
+
+
+def config3_device(torch, device):
+    """Markov sampling inputs at full size: base [64, 16, 151936] float32
+    N(0, 3^2); W1 [151936, 256] and W2 [256, 151936] bf16 N(0, 0.02^2);
+    first previous tokens uniform in [0, V); temperature 1, Philox seed 1003."""
+    c = CONFIG3
+    g = _gen(torch, device, SEED_BASE + 3)
+    return dict(
+        base=device_normal(torch, g, (c["R"], c["gamma"], c["V"]), 3.0, torch.float32, device),
+        w1=device_normal(torch, g, (c["V"], c["r"]), 0.02, torch.bfloat16, device),
+        w2=device_normal(torch, g, (c["r"], c["V"]), 0.02, torch.bfloat16, device),
+        first_prev=torch.from_numpy(config3_structure()).to(device),
+        temperature=c["temperature"], seed=SEED_BASE + 3)
+
+
+def config4_device(torch, device):
+    """Accept-rate inputs at full size: draft [4, 512, 8, 151936] bf16
+    N(0, 3^2); target = draft + N(0, sigma[b, a]^2) formed in float32 and
+    rounded to bf16, sigma from config4_structure(); eval-mask inputs as
+    there."""
+    c = CONFIG4
+    mask, sigma = config4_structure()
+    g = _gen(torch, device, SEED_BASE + 4)
+    shape = (c["B"], c["A"], c["gamma"], c["V"])
+    draft = device_normal(torch, g, shape, 3.0, torch.bfloat16, device)
+    target = torch.empty_like(draft)
+    sig = torch.from_numpy(sigma).to(device)
+    for b in range(c["B"]):
+        for a0 in range(0, c["A"], 64):
+            a1 = min(c["A"], a0 + 64)
+            x = draft[b, a0:a1].float()
+            x.add_(torch.randn(x.shape, generator=g, device=device, dtype=torch.float32)
+                   * sig[b, a0:a1, None, None])
+            target[b, a0:a1].copy_(x)
+    return dict(draft=draft, target=target, mask=mask, sigma=sigma)
+
+
+def config5_device(torch, device):
+    """Serving round inputs at full size (structure from config5_structure()):
+    Q [128, 16, 32, 128], K/V context [sum S_b, 8, 128] and own-block K/V
+    [128, 16, 8, 128], i.i.d. N(0, 1) bf16; Markov base [128, 16, 151936]
+    float32 N(0, 3^2), W1/W2 bf16 N(0, 0.02^2), greedy."""
+    c = CONFIG5
+    st = config5_structure()
+    g = _gen(torch, device, SEED_BASE + 5)
+    bf = torch.bfloat16
+    T = int(st["ctx_offsets"][-1])
+    B, G = c["B"], c["gamma"]
+    return dict(
+        q=device_normal(torch, g, (B, G, c["Hq"], c["D"]), 1.0, bf, device),
+        k_ctx=device_normal(torch, g, (T, c["Hkv"], c["D"]), 1.0, bf, device),
+        v_ctx=device_normal(torch, g, (T, c["Hkv"], c["D"]), 1.0, bf, device),
+        k_blk=device_normal(torch, g, (B, G, c["Hkv"], c["D"]), 1.0, bf, device),
+        v_blk=device_normal(torch, g, (B, G, c["Hkv"], c["D"]), 1.0, bf, device),
+        ctx_offsets=torch.from_numpy(st["ctx_offsets"]).to(device),
+        anchor=torch.from_numpy(st["anchor"]).to(device),
+        keep=torch.from_numpy(st["keep"]).to(device),
+        base=device_normal(torch, g, (B, G, c["V"]), 3.0, torch.float32, device),
+        w1=device_normal(torch, g, (c["V"], c["r"]), 0.02, bf, device),
+        w2=device_normal(torch, g, (c["r"], c["V"]), 0.02, bf, device),
+        first_prev=torch.from_numpy(st["first_prev"]).to(device),
+        seq_lens=torch.from_numpy(st["mask"].seq_lens).to(device),
+        structure=st, max_ctx=c["S_hi"])
