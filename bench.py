@@ -1,0 +1,262 @@
+"""Throughput of one DSpark draft round on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+A step is one serving-shaped draft round over one batch resident in HBM:
+eval mask, block-masked dual-source attention (one draft layer's attention
+core) and the gamma-step Markov sampler, all through the C ABI on one
+stream.  Workload: 128 requests with context lengths U{1024..8192}, one block
+per request anchored at the end of its context, gamma = 16, 32 query / 8 KV
+heads, head dim 128, V = 151936, Markov rank 256, greedy; bf16 inputs,
+float32 accumulation.  The TV accept rate (with tau), which needs target
+logits and so is not part of a serving round, is timed beside it on the
+4 x 512 x 8-row training-shaped workload and reported under "accept_rate".
+
+Prints ONE JSON line: metric, value (drafted tokens/s), ms_per_step, the
+per-operation breakdown, the roofline of the dominant kernel (achieved
+algorithmic GB/s from HIP events on the launch stream vs the 8 TB/s HBM
+peak) and the CPU oracle timed on a bounded sample of the same workload.
+
+--only {round,attention,markov,accept,copy} restricts the run to one part
+(for profiler runs); --no-cpu skips the CPU baseline.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--only", choices=["round", "attention", "markov", "accept", "copy"], default=None)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    return ap.parse_args()
+
+
+def timed(torch, fn, steps, warmup):
+    """Average ms of fn() over `steps` runs after `warmup`, bracketed by
+    device synchronisation; events recorded on the current stream (the
+    stream every library call is launched on)."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(steps):
+        fn()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / steps
+
+
+def round_inputs(torch, dsp, W, dev):
+    inp = W.config5_device(torch, dev)
+    st = inp["structure"]
+    c = W.CONFIG5
+    B, G, Hq, Hkv, D, V, r = c["B"], c["gamma"], c["Hq"], c["Hkv"], c["D"], c["V"], c["r"]
+    bufs = dict(
+        out=torch.empty_like(inp["q"]),
+        tokens=torch.empty((B, G), dtype=torch.int32, device=dev),
+        mask=torch.empty((B, 1, G), dtype=torch.uint8, device=dev),
+        ws_attn=torch.empty(max(1, dsp.block_attention_workspace_bytes(B, 1, G, Hq, Hkv, D, inp["max_ctx"])),
+                            dtype=torch.uint8, device=dev),
+        ws_mk=torch.empty(dsp.markov_sample_workspace_bytes(B, G, V, r), dtype=torch.uint8, device=dev),
+    )
+    ctx_total = int(st["ctx_offsets"][-1])
+    # algorithmic bytes: every input byte the definition reads once, every output written once
+    attn_bytes = (ctx_total * Hkv * D * 2 * 2          # context K and V
+                  + B * G * Hq * D * 2 * 2            # Q in, out
+                  + B * G * Hkv * D * 2 * 2           # own-block K and V
+                  + (B + 1) * 4 + B * 5)              # offsets, anchors, keep
+    attn_flops = 4.0 * D * G * Hq * float(sum(int(s) + G for s in st["ctx_lens"]))
+    step_bytes = r * V * 2 + B * V * 4 + B * r * 2 + B * 8  # W2, base slice, W1 rows, keys
+    return inp, bufs, dict(attn_bytes=attn_bytes, attn_flops=attn_flops,
+                           markov_step_bytes=step_bytes, markov_steps=G, tokens=B * G)
+
+
+def run_round(dsp, inp, bufs):
+    st = inp["structure"]
+    dsp.eval_mask(inp["anchor"], inp["keep"], inp["seq_lens"], gamma=16, out=bufs["mask"])
+    dsp.block_attention(inp["q"], inp["k_ctx"], inp["v_ctx"], inp["ctx_offsets"], inp["k_blk"],
+                        inp["v_blk"], inp["anchor"], inp["keep"], max_ctx=inp["max_ctx"],
+                        out=bufs["out"], workspace=bufs["ws_attn"])
+    dsp.markov_sample(inp["base"], inp["w1"], inp["w2"], inp["first_prev"], tokens=bufs["tokens"],
+                      workspace=bufs["ws_mk"])
+
+
+def cpu_baseline(W, inp, budget_s):
+    """The oracle, as it is, on the first requests of the same round until
+    about `budget_s` of CPU time has been spent (at least two requests)."""
+    import numpy as np
+    from oracle import attention as OA
+    from oracle import eval_mask as OE
+    from oracle import markov as OM
+
+    f = lambda t: W.bf16_to_f32(t.contiguous().view(__import__("torch").int16).cpu().numpy().view(np.uint16))
+    st = inp["structure"]
+    offs = st["ctx_offsets"]
+    w1 = f(inp["w1"]).astype(np.float64)
+    w2 = f(inp["w2"]).astype(np.float64)
+    t0 = time.perf_counter()
+    n = 0
+    while n < 2 or (time.perf_counter() - t0 < budget_s and n < 128):
+        b = n
+        c0, c1 = int(offs[b]), int(offs[b + 1])
+        q = f(inp["q"][b:b + 1])
+        kc, vc = f(inp["k_ctx"][c0:c1]), f(inp["v_ctx"][c0:c1])
+        kb, vb = f(inp["k_blk"][b:b + 1]), f(inp["v_blk"][b:b + 1])
+        OE.eval_mask(st["anchor"][b:b + 1], st["keep"][b:b + 1], st["mask"].seq_lens[b:b + 1], None, 16)
+        OA.block_attention(q, kc, vc, np.array([0, c1 - c0]), kb, vb, st["anchor"][b:b + 1],
+                           st["keep"][b:b + 1], 16, 1.0 / np.sqrt(128))
+        base = inp["base"][b:b + 1].cpu().numpy()
+        OM.sample_block_tokens(base, w1, w2, st["first_prev"][b:b + 1], 0.0, 0)
+        n += 1
+    el = time.perf_counter() - t0
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = 1
+    return dict(value=n * 16 / el, unit="drafted tokens/s", cores=int(cores), kind="oracle",
+                sample=f"first {n} of 128 requests of the same round (attention over their "
+                       f"contexts, 16 Markov steps over V=151936, eval mask); {el:.1f} s; "
+                       "float64 numpy, BLAS threads = cores")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+
+    import semi_autoregressive_block_amd as dsp
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    K, Wm = args.steps, args.warmup
+    result = {}
+
+    if args.only == "copy":
+        # plain copy of a known size: the scale factor for the HBM counters
+        n = 1 << 30
+        a = torch.empty(n, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        ms = timed(torch, lambda: b.copy_(a), K, Wm)
+        print(json.dumps({"copy_bytes": n, "ms": ms, "GBps": 2 * n / ms / 1e6}))
+        return
+
+    if args.only in (None, "round", "attention", "markov"):
+        inp, bufs, alg = round_inputs(torch, dsp, W, dev)
+        f_attn = lambda: dsp.block_attention(
+            inp["q"], inp["k_ctx"], inp["v_ctx"], inp["ctx_offsets"], inp["k_blk"], inp["v_blk"],
+            inp["anchor"], inp["keep"], max_ctx=inp["max_ctx"], out=bufs["out"],
+            workspace=bufs["ws_attn"])
+        f_mk = lambda: dsp.markov_sample(inp["base"], inp["w1"], inp["w2"], inp["first_prev"],
+                                         tokens=bufs["tokens"], workspace=bufs["ws_mk"])
+        f_mask = lambda: dsp.eval_mask(inp["anchor"], inp["keep"], inp["seq_lens"], gamma=16,
+                                       out=bufs["mask"])
+        if args.only == "attention":
+            ms = timed(torch, f_attn, K, Wm)
+            print(json.dumps({"attention_ms": ms, "GBps": alg["attn_bytes"] / ms / 1e6}))
+            return
+        if args.only == "markov":
+            ms = timed(torch, f_mk, K, Wm)
+            print(json.dumps({"markov_ms": ms,
+                              "GBps": alg["markov_step_bytes"] * 16 / ms / 1e6}))
+            return
+        round_ms = timed(torch, lambda: run_round(dsp, inp, bufs), K, Wm)
+        if args.only == "round":
+            print(json.dumps({"round_ms": round_ms}))
+            return
+        attn_ms = timed(torch, f_attn, K, Wm)
+        mk_ms = timed(torch, f_mk, K, Wm)
+        mask_ms = timed(torch, f_mask, K, Wm)
+        result["round"] = dict(ms=round_ms, attn_ms=attn_ms, markov_ms=mk_ms, mask_ms=mask_ms, **alg)
+        if not args.no_cpu:
+            result["cpu"] = cpu_baseline(W, inp, args.cpu_seconds)
+        del inp, bufs
+        torch.cuda.empty_cache()
+
+    if args.only in (None, "accept"):
+        a4 = W.config4_device(torch, dev)
+        m = a4["mask"]
+        em = dsp.eval_mask(torch.from_numpy(m.anchor).to(dev), torch.from_numpy(m.keep).to(dev),
+                           torch.from_numpy(m.seq_lens).to(dev), torch.from_numpy(m.loss_mask).to(dev),
+                           gamma=8)
+        acc = torch.empty((4, 512, 8), dtype=torch.float32, device=dev)
+        tau = torch.empty((4, 512), dtype=torch.float32, device=dev)
+        ws = torch.empty(dsp.accept_rate_workspace_bytes(4, 512, 8, 151936), dtype=torch.uint8, device=dev)
+        f_acc = lambda: dsp.accept_rate(a4["draft"], a4["target"], eval_mask=em, accept=acc, tau=tau,
+                                        workspace=ws)
+        acc_ms = timed(torch, f_acc, K, Wm)
+        acc_bytes = 2 * a4["draft"].numel() * 2 + 16384 * 4 + 16384 + 2048 * 4
+        if args.only == "accept":
+            print(json.dumps({"accept_ms": acc_ms, "GBps": acc_bytes / acc_ms / 1e6}))
+            return
+        result["accept"] = dict(ms=acc_ms, bytes=acc_bytes)
+        del a4
+        torch.cuda.empty_cache()
+
+    r = result["round"]
+    attn_gbs = r["attn_bytes"] / r["attn_ms"] / 1e6
+    mk_launch_ms = r["markov_ms"] / r["markov_steps"]
+    mk_gbs = r["markov_step_bytes"] / mk_launch_ms / 1e6
+    if r["attn_ms"] >= r["markov_ms"]:
+        roof = dict(kernel="block_attn_mfma<128>", bound="hbm", achieved=attn_gbs,
+                    peak=HBM_PEAK_GBS, unit="GB/s", frac=attn_gbs / HBM_PEAK_GBS, traffic=None,
+                    bytes_per_launch=r["attn_bytes"], launch_ms=r["attn_ms"])
+    else:
+        roof = dict(kernel="markov_step_mfma", bound="hbm", achieved=mk_gbs, peak=HBM_PEAK_GBS,
+                    unit="GB/s", frac=mk_gbs / HBM_PEAK_GBS, traffic=None,
+                    bytes_per_launch=r["markov_step_bytes"], launch_ms=mk_launch_ms)
+    line = {
+        "metric": "drafted tokens/s per draft round (attn+Markov)",
+        "value": r["tokens"] / (r["ms"] / 1e3),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": K, "warmup": Wm, "ms_per_step": r["ms"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "serving draft round: 128 requests, context U{1024..8192}, "
+                               "one block at the context end, gamma=16, Hq=32/Hkv=8, D=128, "
+                               "V=151936, Markov rank 256, greedy",
+                   "global_batch": 128, "seq_len": "1024-8192", "gamma": 16},
+        "breakdown_ms": {"eval_mask": r["mask_ms"], "block_attention": r["attn_ms"],
+                         "markov_sample": r["markov_ms"]},
+        "attention": {"GBps": attn_gbs, "hbm_frac": attn_gbs / HBM_PEAK_GBS,
+                      "TFLOPs": r["attn_flops"] / r["attn_ms"] / 1e9,
+                      "mfma_frac": r["attn_flops"] / r["attn_ms"] / 1e9 / MFMA_BF16_PEAK_TFLOPS},
+        "markov": {"GBps_per_launch": mk_gbs, "hbm_frac": mk_gbs / HBM_PEAK_GBS,
+                   "launch_ms": mk_launch_ms},
+        "roofline": roof,
+    }
+    if "accept" in result:
+        a = result["accept"]
+        gbs = a["bytes"] / a["ms"] / 1e6
+        line["accept_rate"] = {"workload": "4 x 512 x 8 rows, V=151936 bf16, with tau",
+                               "ms": a["ms"], "GBps": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
+                               "rows_per_s": 16384 / (a["ms"] / 1e3)}
+    if "cpu" in result:
+        line["cpu_baseline"] = result["cpu"]
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -19,6 +19,8 @@
 // cooperatively so every workgroup of a cluster is co-resident; every wait is
 // bounded.  The maximum of bf16 data is taken on the raw bits with packed
 // 16-bit integer max/min (two elements per instruction).
+#include <stdlib.h>
+
 #include "common.h"
 
 using namespace dspark;
@@ -26,7 +28,7 @@ using namespace dspark;
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kMaxVec = 10;          // 16-byte vectors per thread per tensor
+constexpr int kMaxVec = 5;  // 16-byte vectors per thread per tensor (152 VGPRs: 3 WGs per CU)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr unsigned kSpinLimit = 1u << 26;  // bounded wait (~seconds), then flag and go on
 
@@ -146,29 +148,36 @@ __device__ __forceinline__ float vec_summin(const u32x4* dv, const u32x4* tv, in
   return s0 + s1;
 }
 
-// Bounded wait for the cluster counter; false (and a flag) on time-out.
-__device__ __forceinline__ bool spin_until(unsigned* ctr, unsigned target, int32_t* err) {
+// ---- cluster exchange without fences.  Every published float travels with
+// its iteration number ("epoch") in one 64-bit word written and read with
+// relaxed agent-scope atomics (coherent across the XCDs' L2s), so a reader
+// that sees the right epoch also sees the value: no release/acquire cache
+// maintenance per poll.  Epochs start at 1; the slots are zeroed per launch.
+__device__ __forceinline__ void publish(uint64_t* slot, float v, uint32_t epoch) {
+  const uint64_t w = ((uint64_t)epoch << 32) | __float_as_uint(v);
+  __hip_atomic_store(slot, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Bounded wait for one slot; NaN (and a flag) on time-out.
+__device__ __forceinline__ float collect(uint64_t* slot, uint32_t epoch, int32_t* err, bool& ok) {
   unsigned n = 0;
-  while (__hip_atomic_load(ctr, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < target) {
-    __builtin_amdgcn_s_sleep(2);
-    if (++n > kSpinLimit) { atomicOr(err, 1); return false; }
+  for (;;) {
+    const uint64_t w = __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if ((uint32_t)(w >> 32) == epoch) return __uint_as_float((uint32_t)w);
+    if (!ok || ++n > kSpinLimit) {
+      if (ok) atomicOr(err, 1);
+      ok = false;
+      return NAN;
+    }
+    __builtin_amdgcn_s_sleep(1);
   }
-  return true;
 }
 
-__device__ __forceinline__ void st_relaxed(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float ld_relaxed(float* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Workspace per cluster: slots[2 phases][2 parities][G][4] floats + 2 counters.
+// Workspace per cluster: slots[2 phases][2 parities][G][4] 64-bit words.
 template <bool kBf16>
 __global__ __launch_bounds__(kThreads) void tv_cluster_kernel(
     const u32x4* __restrict__ d, const u32x4* __restrict__ t, float* __restrict__ accept,
     int64_t rows, int vec_per_row, int vec_per_wg, int G, int nclusters,
-    float* __restrict__ slots, unsigned* __restrict__ counters, int32_t* __restrict__ err) {
+    uint64_t* __restrict__ slots, int32_t* __restrict__ err) {
   __shared__ float red[8];
   __shared__ float bcast[4];
   const int cl = blockIdx.x / G, g = blockIdx.x % G;
@@ -176,11 +185,13 @@ __global__ __launch_bounds__(kThreads) void tv_cluster_kernel(
   const int v1 = min(v0 + vec_per_wg, vec_per_row);
   const int first = v0 + (int)threadIdx.x;
   const int nvalid = first < v1 ? min(kMaxVec, (v1 - first + kThreads - 1) / kThreads) : 0;
-  float* cslots = slots + (size_t)cl * 16 * G;
-  unsigned* cnt = counters + 2 * cl;
+  uint64_t* cslots = slots + (size_t)cl * 16 * G;
   int it = 0;
-  bool waits_ok = true;  // after one timed-out wait this workgroup stops waiting
+  bool ok = true;  // after one timed-out wait this workgroup stops waiting
   for (int64_t row = cl; row < rows; row += nclusters, ++it) {
+    const uint32_t epoch = (uint32_t)it + 1u;
+    uint64_t* slotA = cslots + (0 * 2 + (it & 1)) * G * 4;
+    uint64_t* slotB = cslots + (1 * 2 + (it & 1)) * G * 4;
     const u32x4* dr = d + row * vec_per_row;
     const u32x4* tr = t + row * vec_per_row;
     u32x4 dv[kMaxVec], tv[kMaxVec];
@@ -200,28 +211,39 @@ __global__ __launch_bounds__(kThreads) void tv_cluster_kernel(
     // ---- cluster exchange of (max, sum) for both tensors
     float Md = md, Sd = sd, Mt = mt, St = st;
     if (G > 1) {
-      if (threadIdx.x == 0) {
-        float* my = cslots + ((0 * 2 + (it & 1)) * G + g) * 4;
-        st_relaxed(my + 0, md); st_relaxed(my + 1, sd);
-        st_relaxed(my + 2, mt); st_relaxed(my + 3, st);
-        __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-        const bool arrived = waits_ok && spin_until(cnt, (unsigned)G * (unsigned)(it + 1), err);
-        waits_ok = arrived;
-        const float* all = cslots + (0 * 2 + (it & 1)) * G * 4;
-        float a = -INFINITY, b = -INFINITY;
-        for (int j = 0; j < G; ++j) {
-          a = fmaxf(a, ld_relaxed((float*)all + 4 * j + 0));
-          b = fmaxf(b, ld_relaxed((float*)all + 4 * j + 2));
+      if (threadIdx.x < 4) {
+        const float mine = threadIdx.x == 0 ? md : threadIdx.x == 1 ? sd : threadIdx.x == 2 ? mt : st;
+        publish(slotA + g * 4 + threadIdx.x, mine, epoch);
+      }
+      // lanes j < G of wave 0 collect workgroup j's statistics
+      if (threadIdx.x < 64) {
+        const int j = threadIdx.x;
+        float mj = -INFINITY, sj = 0.f, nj = -INFINITY, tj = 0.f;
+        if (j < G) {
+          mj = collect(slotA + j * 4 + 0, epoch, err, ok);
+          sj = collect(slotA + j * 4 + 1, epoch, err, ok);
+          nj = collect(slotA + j * 4 + 2, epoch, err, ok);
+          tj = collect(slotA + j * 4 + 3, epoch, err, ok);
         }
-        float sa = 0.f, sb = 0.f;
-        for (int j = 0; j < G; ++j) {
-          const float mj = ld_relaxed((float*)all + 4 * j + 0), sj = ld_relaxed((float*)all + 4 * j + 1);
-          const float nj = ld_relaxed((float*)all + 4 * j + 2), tj = ld_relaxed((float*)all + 4 * j + 3);
-          if (sj > 0.f) sa += sj * exp2_fast((mj - a) * kLog2e);
-          if (tj > 0.f) sb += tj * exp2_fast((nj - b) * kLog2e);
+        float a = mj, b = nj;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          a = fmaxf(a, __shfl_xor(a, o, kWave));
+          b = fmaxf(b, __shfl_xor(b, o, kWave));
         }
-        // a wait that timed out poisons the row instead of using stale statistics
-        bcast[0] = arrived ? a : NAN; bcast[1] = sa; bcast[2] = b; bcast[3] = sb;
+        float sa = sj > 0.f ? sj * exp2_fast((mj - a) * kLog2e) : 0.f;
+        float sb = tj > 0.f ? tj * exp2_fast((nj - b) * kLog2e) : 0.f;
+        // fixed-order sum over j (lanes) so every workgroup gets identical bits
+        float SA = 0.f, SB = 0.f;
+        for (int q = 0; q < G; ++q) {
+          SA += __shfl(sa, q, kWave);
+          SB += __shfl(sb, q, kWave);
+        }
+        const bool poisoned = __any(!ok);  // a timed-out wait poisons the row
+        if (j == 0) {
+          bcast[0] = poisoned ? NAN : a;
+          bcast[1] = SA; bcast[2] = b; bcast[3] = SB;
+        }
       }
       __syncthreads();
       Md = bcast[0]; Sd = bcast[1]; Mt = bcast[2]; St = bcast[3];
@@ -234,15 +256,15 @@ __global__ __launch_bounds__(kThreads) void tv_cluster_kernel(
     block_reduce2<false>(part, dummy, red);
     if (G == 1) {
       if (threadIdx.x == 0) accept[row] = fminf(fmaxf(part, 0.f), 1.f);
-    } else if (threadIdx.x == 0) {
-      float* my = cslots + ((1 * 2 + (it & 1)) * G + g) * 4;
-      st_relaxed(my, part);
-      const unsigned old = __hip_atomic_fetch_add(cnt + 1, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-      if (old == (unsigned)G * (unsigned)(it + 1) - 1u) {  // last of the cluster: fold and write
-        const float* all = cslots + (1 * 2 + (it & 1)) * G * 4;
+    } else {
+      if (threadIdx.x == 0) publish(slotB + g * 4, part, epoch);
+      // one workgroup per row (rotating) folds the partial sums in fixed order
+      if (g == it % G && threadIdx.x < 64) {
+        const int j = threadIdx.x;
+        const float pj = j < G ? collect(slotB + j * 4, epoch, err, ok) : 0.f;
         float s = 0.f;
-        for (int j = 0; j < G; ++j) s += ld_relaxed((float*)all + 4 * j);
-        accept[row] = fminf(fmaxf(s, 0.f), 1.f);
+        for (int q = 0; q < G; ++q) s += __shfl(pj, q, kWave);
+        if (j == 0) accept[row] = fminf(fmaxf(s, 0.f), 1.f);
       }
     }
   }
@@ -308,6 +330,13 @@ struct Plan {
   int vec_per_row, G, vec_per_wg, nclusters;
 };
 
+int device_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
+  return cus;
+}
+
 int device_wg_capacity(const void* kernel) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return -1;
@@ -337,7 +366,7 @@ Plan make_plan(int64_t rows, int V, int dtype, int capacity) {
 extern "C" size_t dspark_accept_rate_workspace_bytes(int B, int A, int gamma, int V, int dtype) {
   if (B < 0 || A < 0 || gamma < 0 || V < 0) return 0;
   // Upper bound independent of the device: one cluster per row at most and
-  // at most 8 workgroups per compute unit on 256 compute units.
+  // at most 16 workgroups per compute unit on 256 compute units.
   const int64_t rows = (int64_t)B * A * gamma;
   const int epv = dtype == DSPARK_BF16 ? 8 : 4;
   const int64_t vpr = V / epv > 0 ? V / epv : 1;
@@ -345,7 +374,7 @@ extern "C" size_t dspark_accept_rate_workspace_bytes(int B, int A, int gamma, in
   int64_t cl = (256 * 16) / (G > 0 ? G : 1);
   if (cl > rows) cl = rows;
   if (cl < 1) cl = 1;
-  return (size_t)(cl * 16 * G * sizeof(float) + cl * 2 * sizeof(unsigned) + 64);
+  return (size_t)(cl * 16 * G * sizeof(uint64_t) + 64);
 }
 
 extern "C" int dspark_accept_rate(const void* draft_logits, const void* target_logits,
@@ -377,21 +406,23 @@ extern "C" int dspark_accept_rate(const void* draft_logits, const void* target_l
     // the workspace bound assumes at most 16 workgroups per CU on 256 CUs
     const int64_t max_cl = (256 * 16) / p.G;
     if (p.nclusters > max_cl) p.nclusters = (int)max_cl;
-    float* slots = (float*)ws;
-    unsigned* counters = (unsigned*)((char*)ws + (size_t)p.nclusters * 16 * p.G * sizeof(float));
-    const int nc = 2 * p.nclusters;
-    int32_t* err = (int32_t*)(counters + nc);  // one spare word after the counters
-    // counters and the error word must start at zero (a fill kernel, not a
-    // memset node, so the sequence stays safe under graph capture)
-    hipLaunchKernelGGL(zero_u32_kernel, dim3((nc + 1 + 255) / 256), dim3(256), 0, s, counters,
-                       nc + 1);
+    uint64_t* slots = (uint64_t*)ws;
+    const int64_t nslot = (int64_t)p.nclusters * 16 * p.G;
+    int32_t* err = (int32_t*)(slots + nslot);  // one spare word after the slots
+    // slots (epoch 0 = empty) and the error word start at zero: a fill
+    // kernel, not a memset node, so the sequence stays safe under graph capture
+    const int64_t nwords = nslot * 2 + 1;
+    hipLaunchKernelGGL(zero_u32_kernel, dim3((unsigned)((nwords + 255) / 256)), dim3(256), 0, s,
+                       (unsigned*)ws, (int)nwords);
     const u32x4* dp = (const u32x4*)draft_logits;
     const u32x4* tp = (const u32x4*)target_logits;
     int64_t rows_arg = rows;
     int vpr = p.vec_per_row, vpw = p.vec_per_wg, G = p.G, ncl = p.nclusters;
     void* args[] = {(void*)&dp, (void*)&tp, (void*)&accept, (void*)&rows_arg, (void*)&vpr,
-                    (void*)&vpw, (void*)&G, (void*)&ncl, (void*)&slots, (void*)&counters,
-                    (void*)&err};
+                    (void*)&vpw, (void*)&G, (void*)&ncl, (void*)&slots, (void*)&err};
+    if (getenv("DSPARK_VERBOSE"))
+      fprintf(stderr, "[dspark] accept_rate: capacity %d WGs (%d CUs), G=%d, clusters=%d, vec/row=%d\n",
+              cap, device_cus(), p.G, p.nclusters, p.vec_per_row);
     hipError_t e = hipLaunchCooperativeKernel(kern, dim3((unsigned)(p.nclusters * p.G)),
                                               dim3(kThreads), args, 0, s);
     if (e != hipSuccess)

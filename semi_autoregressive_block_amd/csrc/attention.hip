@@ -14,11 +14,17 @@
 //   packs several heads (and, for short blocks, several consecutive blocks)
 //   against the same keys: the MFMA M/N extent is filled by GQA packing, not
 //   by padding gamma.
-// * Work item = (b, kvh, tile, context chunk of kChunk keys).  A tile's
-//   context length is the largest anchor of its kept blocks; chunks past it
-//   exit at once, so block-sparse work is skipped at chunk granularity and
-//   masked per score inside the last slab.  The own-block keys of the tile's
-//   blocks form extra 32-key slabs of chunk 0 with a block-diagonal mask.
+// * One workgroup owns one tile for its whole key range: no split across
+//   workgroups, so no partial results, counters or cache-maintenance fences.
+//   A tile's context length is the largest anchor of its kept blocks; the
+//   own-block keys of its blocks form extra 32-key slabs with a
+//   block-diagonal mask, and per-score masking handles each block's anchor.
+// * Load balance comes from the launch order: a one-workgroup planner sorts
+//   the (request, tile) pairs by work, longest first (counting sort), and
+//   the main grid walks that order, so the hardware's in-order dispatch is a
+//   longest-processing-time schedule.  Within one rank the KV heads are
+//   adjacent, so with 8 KV heads workgroup i runs on XCD i % 8 = kvh and
+//   each XCD keeps one head's context K/V in its L2.
 // * Four waves per workgroup: two 32-row groups x two key parities.  Per
 //   32-key slab a wave computes S^T = K Q^T (v_mfma_f32_32x32x16_bf16; K rows
 //   and Q rows are loaded as 16-byte row pieces), so each lane owns ONE query
@@ -27,10 +33,10 @@
 //   the S^T accumulator layout (no transpose of P); V's head dimension is
 //   permuted (slot m of product j is d = NJ*m + j) so every lane loads
 //   NJ*2-byte pieces of key rows and transposes them in registers.
-// * Parities merge through LDS; chunks of one tile merge through workspace
-//   partials folded by the last chunk to finish (fixed order: deterministic).
-// * Workgroup ids run kvh fastest, so with 8 KV heads the eight XCDs each
-//   serve one head and keep its context K/V in their own L2.
+// * The slab loop is software-pipelined: the wave's next slab is loaded
+//   (unconditionally, from clamped addresses, so the loads stay in flight
+//   across the MFMA work) while the current one is computed.  Parities merge
+//   through LDS at the end.
 #include "common.h"
 
 using namespace dspark;
@@ -39,7 +45,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kTileRows = 64;
-constexpr int kChunk = 1024;  // context keys per work item
+constexpr int kPlanBins = 4096;  // cost buckets of the planner's counting sort
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.69314718055994531f;
 
@@ -54,8 +60,7 @@ struct Params {
   const uint8_t* keep;
   uint16_t* out;
   float* lse;
-  float* partial;     // [items][kTileRows][D + 2]
-  unsigned* counter;  // [ntiles * B * Hkv]
+  const int32_t* order;  // launch order of tile ids (planner output)
   int32_t* status;
   int B, A, gamma, Hq, Hkv, group, ntiles, nrows;  // nrows = A * group * gamma
   int total_ctx, max_ctx;
@@ -82,59 +87,247 @@ __device__ __forceinline__ int visible_ctx(const Params& p, int b, int a, int S,
   return clampi(an, 0, S);
 }
 
+// One 32-key slab as this lane holds it: K as the A operand of S^T (key slot
+// r32, head dims 16*kk + 8h .. +7) and the V pieces of the 16 keys of its
+// half (key of (t, s8) = 8*(2t + s8/4) + 4h + s8%4, head dims NJ*r32 .. +NJ-1).
+template <int D>
+struct Slab {
+  u32x4 kf[D / 16];
+  uint32_t v[2][8][D / 64];
+};
+
+// Per-workgroup constants of a work item.
+struct Item {
+  int64_t c0;        // first context row of the request
+  int S;             // context length
+  int cbeg, cend;    // context keys of this chunk
+  int n_ctx_slabs;
+  int64_t own0;      // first own-block row (k_blk / v_blk) of the tile's blocks
+  int n_own;         // own-block keys of the tile
+  int kvh, h, r32;
+};
+
+template <int D>
+__device__ __forceinline__ void fetch_slab(const Params& p, const Item& it, int s, Slab<D>& sl) {
+  constexpr int KK = D / 16, NJ = D / 32;
+  const bool own = s >= it.n_ctx_slabs;
+  const uint16_t* kbase = own ? p.kb : p.kc;
+  const uint16_t* vbase = own ? p.vb : p.vc;
+  int64_t krow;
+  int j0 = 0, os = 0;
+  if (!own) {
+    j0 = it.cbeg + s * 32;
+    krow = it.c0 + min(j0 + it.r32, it.S - 1);
+  } else {
+    os = (s - it.n_ctx_slabs) * 32;
+    krow = it.own0 + min(os + it.r32, it.n_own - 1);
+  }
+  const uint16_t* kp = kbase + (krow * p.Hkv + it.kvh) * D + it.h * 8;
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) sl.kf[kk] = *(const u32x4*)(kp + kk * 16);
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int s8 = 0; s8 < 8; ++s8) {
+      const int ks = 8 * (2 * t + s8 / 4) + 4 * it.h + (s8 & 3);
+      const int64_t vrow = own ? it.own0 + min(os + ks, it.n_own - 1) : it.c0 + min(j0 + ks, it.S - 1);
+      const uint16_t* vp = vbase + (vrow * p.Hkv + it.kvh) * D + NJ * it.r32;
+      if constexpr (NJ == 4) {
+        const u32x2 w = *(const u32x2*)vp;
+        sl.v[t][s8][0] = w.x;
+        sl.v[t][s8][1] = w.y;
+      } else {
+        sl.v[t][s8][0] = *(const uint32_t*)vp;
+      }
+    }
+}
+
+// Online-softmax update of this lane's row with one slab.
+template <int D>
+__device__ __forceinline__ void compute_slab(const Params& p, const Item& it, int s, const Slab<D>& sl,
+                                             const u32x4* qf, bool kept, int lim, int ua, int a_lo,
+                                             float c, float& m, float& l, f32x16* o) {
+  constexpr int KK = D / 16, NJ = D / 32;
+  const bool own = s >= it.n_ctx_slabs;
+  const int j0 = own ? 0 : it.cbeg + s * 32;
+  const int os = own ? (s - it.n_ctx_slabs) * 32 : 0;
+  f32x16 sc;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) sc[i] = 0.f;
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) sc = mfma32x32x16(sl.kf[kk], qf[kk], sc);
+  float smax = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int ks = 8 * (i / 4) + 4 * it.h + (i & 3);
+    bool vis;
+    if (!own) {
+      const int j = j0 + ks;
+      vis = kept && j < it.cend && j < lim;
+    } else {
+      const int o_i = os + ks;
+      vis = kept && o_i < it.n_own && (a_lo + o_i / p.gamma) == ua;
+    }
+    sc[i] = vis ? sc[i] : -INFINITY;
+    smax = fmaxf(smax, sc[i]);
+  }
+  smax = fmaxf(smax, __shfl_xor(smax, 32, kWave));
+  const float mnew = fmaxf(m, smax);
+  const float muse = mnew == -INFINITY ? 0.f : mnew;
+  const float alpha = __builtin_amdgcn_exp2f((m - muse) * c);
+  float psum = 0.f;
+  u32x4 pb[2];
+#pragma unroll
+  for (int i = 0; i < 16; i += 2) {
+    const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[i], c, -muse * c));
+    const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[i + 1], c, -muse * c));
+    psum += p0 + p1;
+    pb[i / 8][(i % 8) / 2] = f32_to_bf16(p0) | (f32_to_bf16(p1) << 16);
+  }
+  psum += __shfl_xor(psum, 32, kWave);
+  l = l * alpha + psum;
+  m = mnew;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[j][r] *= alpha;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      u32x4 va;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t lo = sl.v[t][2 * w][j / 2], hi = sl.v[t][2 * w + 1][j / 2];
+        va[w] = (j & 1) ? pack_hi(lo, hi) : pack_lo(lo, hi);
+      }
+      o[j] = mfma32x32x16(va, pb[t], o[j]);
+    }
+  }
+}
+
+// Head dim of accumulator register r of product j for a lane in half h.
+template <int NJ>
+__device__ __forceinline__ int head_dim(int r, int j, int h) { return NJ * (8 * (r / 4) + 4 * h + (r & 3)) + j; }
+
+// Work of a (request, tile) pair in 32-key slabs (context + own keys); -1
+// when none of its blocks is kept.
+__device__ __forceinline__ int tile_cost(const Params& p, int b, int tile, int& L, int& a_lo, int& a_hi,
+                                         bool& any_kept) {
+  int c0, S;
+  ctx_range(p, b, c0, S, false);
+  const int rpb = p.group * p.gamma;
+  const int u0 = tile * kTileRows;
+  a_lo = u0 / rpb;
+  a_hi = min(p.A - 1, (u0 + kTileRows - 1) / rpb);
+  L = 0;
+  any_kept = false;
+  for (int a = a_lo; a <= a_hi; ++a) {
+    const int v = visible_ctx(p, b, a, S, false);
+    if (v >= 0) { any_kept = true; L = max(L, v); }
+  }
+  const int n_own = (a_hi - a_lo + 1) * p.gamma;
+  return any_kept ? (L + 31) / 32 + (n_own + 31) / 32 : 0;
+}
+
+// Longest-first launch order: counting sort of the B*ntiles (request, tile)
+// pairs by cost, descending; entry r*Hkv + kvh of `order` is the tile id
+// (pair * Hkv + kvh).  Ties are ordered arbitrarily (results do not depend
+// on the order, only the schedule does).
+__global__ __launch_bounds__(1024) void attn_plan_kernel(Params p, int32_t* __restrict__ order) {
+  __shared__ int hist[kPlanBins];
+  __shared__ int part[1024];
+  const int npairs = p.B * p.ntiles;
+  for (int i = threadIdx.x; i < kPlanBins; i += 1024) hist[i] = 0;
+  __syncthreads();
+  for (int q = threadIdx.x; q < npairs; q += 1024) {
+    int L, a_lo, a_hi;
+    bool any;
+    const int cost = tile_cost(p, q % p.B, q / p.B, L, a_lo, a_hi, any);
+    atomicAdd(&hist[min(cost, kPlanBins - 1)], 1);
+  }
+  __syncthreads();
+  // exclusive scan in descending bin order: thread t owns bins 4095-4t .. 4092-4t
+  int local = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) local += hist[kPlanBins - 1 - 4 * threadIdx.x - k];
+  part[threadIdx.x] = local;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int t = 0; t < 1024; ++t) { const int v = part[t]; part[t] = run; run += v; }
+  }
+  __syncthreads();
+  int run = part[threadIdx.x];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int bin = kPlanBins - 1 - 4 * threadIdx.x - k;
+    const int v = hist[bin];
+    hist[bin] = run;
+    run += v;
+  }
+  __syncthreads();
+  for (int q = threadIdx.x; q < npairs; q += 1024) {
+    int L, a_lo, a_hi;
+    bool any;
+    const int cost = tile_cost(p, q % p.B, q / p.B, L, a_lo, a_hi, any);
+    const int pos = atomicAdd(&hist[min(cost, kPlanBins - 1)], 1);
+    const int b = q % p.B, tile = q / p.B;
+    for (int kvh = 0; kvh < p.Hkv; ++kvh)
+      order[(int64_t)pos * p.Hkv + kvh] = ((tile * p.B) + b) * p.Hkv + kvh;
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(kThreads) void block_attn_mfma(Params p) {
   constexpr int NJ = D / 32;  // head-dim groups of the PV product
   constexpr int KK = D / 16;  // k-steps of the QK product
   __shared__ float mrg[2][D + 2][32];
-  __shared__ int s_last;
 
-  // ---- decode the work item (kvh fastest)
-  int wid = blockIdx.x;
+  // ---- decode the work item (tile id = (tile * B + b) * Hkv + kvh)
+  int wid = p.order ? p.order[blockIdx.x] : (int)blockIdx.x;
   const int kvh = wid % p.Hkv; wid /= p.Hkv;
-  const int b = wid % p.B; wid /= p.B;
-  const int tile = wid % p.ntiles;
-  const int chunk = wid / p.ntiles;
+  const int b = wid % p.B;
+  const int tile = wid / p.B;
   int c0, S;
-  ctx_range(p, b, c0, S, chunk == 0 && tile == 0 && kvh == 0 && threadIdx.x == 0);
-  const int rpb = p.group * p.gamma;  // rows per block
+  ctx_range(p, b, c0, S, tile == 0 && kvh == 0 && threadIdx.x == 0);
+  int L, a_lo, a_hi;
+  bool any_kept;
+  tile_cost(p, b, tile, L, a_lo, a_hi, any_kept);
+  const int rpb = p.group * p.gamma;
   const int u0 = tile * kTileRows;
-  const int a_lo = u0 / rpb;
-  const int a_hi = min(p.A - 1, (u0 + kTileRows - 1) / rpb);
-  int L = 0;
-  bool any_kept = false;
-  for (int a = a_lo; a <= a_hi; ++a) {
-    const int v = visible_ctx(p, b, a, S, false);
-    if (v >= 0) { any_kept = true; L = max(L, v); }
-  }
-  const int nch = L > 0 ? (L + kChunk - 1) / kChunk : 1;
-  if (chunk >= nch) return;
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int rg = wave & 1, par = wave >> 1;
   const int h = lane >> 5, r32 = lane & 31;
-  // this lane's query row
+  // this lane's query row (rows past the row space are computed on a clamped
+  // row and not stored)
   const int u = u0 + rg * 32 + r32;
   const bool row_ok = u < p.nrows;
-  const int ua = row_ok ? u / rpb : a_lo;
-  const int uhg = (u / p.gamma) % p.group, uk = u % p.gamma;
+  const int uc = min(u, p.nrows - 1);
+  const int ua = uc / rpb;
+  const int uhg = (uc / p.gamma) % p.group, uk = uc % p.gamma;
   const int qh = kvh * p.group + uhg;
-  int lim = row_ok ? visible_ctx(p, b, ua, S, chunk == 0 && par == 0 && h == 0) : -1;
-  const bool kept = lim >= 0;
+  int lim = visible_ctx(p, b, ua, S, par == 0 && h == 0 && row_ok);
+  const bool kept = row_ok && lim >= 0;
   if (!kept) lim = 0;
   const int64_t qrow = ((int64_t)b * p.A * p.gamma + (int64_t)ua * p.gamma + uk) * p.Hq + qh;
 
   // Q^T operand pieces: d = 16*kk + 8*h .. +7
   u32x4 qf[KK];
 #pragma unroll
-  for (int kk = 0; kk < KK; ++kk)
-    qf[kk] = row_ok ? *(const u32x4*)(p.q + qrow * D + kk * 16 + h * 8) : u32x4{0u, 0u, 0u, 0u};
+  for (int kk = 0; kk < KK; ++kk) qf[kk] = *(const u32x4*)(p.q + qrow * D + kk * 16 + h * 8);
 
-  const int cbeg = chunk * kChunk, cend = min(L, cbeg + kChunk);
-  const int n_ctx_slabs = (cend - cbeg + 31) / 32;
-  const int n_own = (a_hi - a_lo + 1) * p.gamma;
-  const int n_own_slabs = (chunk == 0 && any_kept) ? (n_own + 31) / 32 : 0;
-  const int nslab = n_ctx_slabs + n_own_slabs;
+  Item it;
+  it.c0 = c0; it.S = S;
+  it.cbeg = 0;
+  it.cend = L;
+  it.n_ctx_slabs = (L + 31) / 32;
+  it.own0 = (int64_t)b * p.A * p.gamma + (int64_t)a_lo * p.gamma;
+  it.n_own = (a_hi - a_lo + 1) * p.gamma;
+  it.kvh = kvh; it.h = h; it.r32 = r32;
+  const int nslab = any_kept ? it.n_ctx_slabs + (it.n_own + 31) / 32 : 0;
   const float c = p.scale * kLog2e;
 
   float m = -INFINITY, l = 0.f;
@@ -144,102 +337,18 @@ __global__ __launch_bounds__(kThreads) void block_attn_mfma(Params p) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[j][r] = 0.f;
 
-  const int64_t kv_stride = (int64_t)p.Hkv * D;  // elements between consecutive keys
-  for (int s = par; s < nslab; s += 2) {
-    const bool own = s >= n_ctx_slabs;
-    // -- key rows this lane loads: K as the A operand (key slot r32) and the
-    //    V pieces for the 16 keys of its half (slots 8q + 4h + i)
-    const uint16_t *kbase, *vbase;
-    int64_t krow;
-    int j0 = 0, os = 0;
-    if (!own) {
-      j0 = cbeg + s * 32;
-      krow = (int64_t)c0 + min(j0 + r32, S - 1);
-      kbase = p.kc; vbase = p.vc;
-    } else {
-      os = (s - n_ctx_slabs) * 32;
-      const int o_i = min(os + r32, n_own - 1);
-      krow = (int64_t)b * p.A * p.gamma + (int64_t)a_lo * p.gamma + o_i;
-      kbase = p.kb; vbase = p.vb;
-    }
-    u32x4 kf[KK];
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
-      kf[kk] = *(const u32x4*)(kbase + (krow * p.Hkv + kvh) * D + kk * 16 + h * 8);
-    // V pieces: key of (t, s8) is 8*(2t + s8/4) + 4h + s8%4, head dims NJ*r32 .. +NJ-1
-    uint32_t vraw[2][8][NJ / 2 > 0 ? NJ / 2 : 1];
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int s8 = 0; s8 < 8; ++s8) {
-        const int ks = 8 * (2 * t + s8 / 4) + 4 * h + (s8 & 3);
-        int64_t vrow;
-        if (!own) vrow = (int64_t)c0 + min(j0 + ks, S - 1);
-        else vrow = (int64_t)b * p.A * p.gamma + (int64_t)a_lo * p.gamma + min(os + ks, n_own - 1);
-        const uint16_t* vp = vbase + (vrow * p.Hkv + kvh) * D + NJ * r32;
-        if constexpr (NJ == 4) {
-          const u32x2 w = *(const u32x2*)vp;
-          vraw[t][s8][0] = w.x;
-          vraw[t][s8][1] = w.y;
-        } else {
-          vraw[t][s8][0] = *(const uint32_t*)vp;
-        }
-      }
-    // -- S^T = K Q^T: lane holds row r32, keys 8*(i/4) + 4h + i%4
-    f32x16 sc;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) sc[i] = 0.f;
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) sc = mfma32x32x16(kf[kk], qf[kk], sc);
-    // -- mask and online softmax (lane-local row)
-    float smax = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int ks = 8 * (i / 4) + 4 * h + (i & 3);
-      bool vis;
-      if (!own) {
-        const int j = j0 + ks;
-        vis = kept && j < cend && j < lim;
-      } else {
-        const int o_i = os + ks;
-        vis = kept && o_i < n_own && (a_lo + o_i / p.gamma) == ua;
-      }
-      sc[i] = vis ? sc[i] : -INFINITY;
-      smax = fmaxf(smax, sc[i]);
-    }
-    smax = fmaxf(smax, __shfl_xor(smax, 32, kWave));
-    const float mnew = fmaxf(m, smax);
-    const float muse = mnew == -INFINITY ? 0.f : mnew;
-    const float alpha = __builtin_amdgcn_exp2f((m - muse) * c);
-    float psum = 0.f;
-    u32x4 pb[2];
-#pragma unroll
-    for (int i = 0; i < 16; i += 2) {
-      const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[i], c, -muse * c));
-      const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[i + 1], c, -muse * c));
-      psum += p0 + p1;
-      pb[i / 8][(i % 8) / 2] = f32_to_bf16(p0) | (f32_to_bf16(p1) << 16);
-    }
-    psum += __shfl_xor(psum, 32, kWave);
-    l = l * alpha + psum;
-    m = mnew;
-#pragma unroll
-    for (int j = 0; j < NJ; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[j][r] *= alpha;
-    // -- O^T += V^T P^T, two 16-key halves
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        u32x4 va;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const uint32_t lo = vraw[t][2 * w][j / 2], hi = vraw[t][2 * w + 1][j / 2];
-          va[w] = (j & 1) ? pack_hi(lo, hi) : pack_lo(lo, hi);
-        }
-        o[j] = mfma32x32x16(va, pb[t], o[j]);
-      }
+  // ---- slab loop, software-pipelined: the wave's next slab is in flight
+  //      while the current one is computed (the prefetch index is clamped so
+  //      the loads are unconditional)
+  if (par < nslab) {
+    Slab<D> sa, sb;
+    fetch_slab<D>(p, it, par, sa);
+    for (int s = par; s < nslab; s += 4) {
+      fetch_slab<D>(p, it, min(s + 2, nslab - 1), sb);
+      compute_slab<D>(p, it, s, sa, qf, kept, lim, ua, a_lo, c, m, l, o);
+      if (s + 2 >= nslab) break;
+      fetch_slab<D>(p, it, min(s + 4, nslab - 1), sa);
+      compute_slab<D>(p, it, s + 2, sb, qf, kept, lim, ua, a_lo, c, m, l, o);
     }
   }
 
@@ -248,14 +357,12 @@ __global__ __launch_bounds__(kThreads) void block_attn_mfma(Params p) {
 #pragma unroll
     for (int j = 0; j < NJ; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int d = NJ * (8 * (r / 4) + 4 * h + (r & 3)) + j;
-        mrg[rg][d][r32] = o[j][r];
-      }
+      for (int r = 0; r < 16; ++r) mrg[rg][head_dim<NJ>(r, j, h)][r32] = o[j][r];
     if (h == 0) { mrg[rg][D][r32] = m; mrg[rg][D + 1][r32] = l; }
   }
   __syncthreads();
-  if (par == 0) {
+  if (par == 1 || !row_ok) return;
+  {
     const float m1 = mrg[rg][D][r32], l1 = mrg[rg][D + 1][r32];
     const float mn = fmaxf(m, m1);
     const float mu = mn == -INFINITY ? 0.f : mn;
@@ -265,84 +372,29 @@ __global__ __launch_bounds__(kThreads) void block_attn_mfma(Params p) {
 #pragma unroll
     for (int j = 0; j < NJ; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int d = NJ * (8 * (r / 4) + 4 * h + (r & 3)) + j;
-        o[j][r] = o[j][r] * a0 + mrg[rg][d][r32] * a1;
-      }
-  }
-
-  // ---- several chunks: publish the partial, the last chunk folds them all
-  const int tile_id = (tile * p.B + b) * p.Hkv + kvh;
-  if (nch > 1) {
-    const int64_t item = ((int64_t)chunk * p.ntiles * p.B + (int64_t)tile * p.B + b) * p.Hkv + kvh;
-    float* part = p.partial + item * kTileRows * (D + 2);
-    if (par == 0) {
-      float* pr = part + (rg * 32 + r32) * (D + 2);
-#pragma unroll
-      for (int j = 0; j < NJ; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) pr[NJ * (8 * (r / 4) + 4 * h + (r & 3)) + j] = o[j][r];
-      if (h == 0) { pr[D] = m; pr[D + 1] = l; }
-    }
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      const unsigned old = atomicAdd(p.counter + tile_id, 1u);
-      s_last = old == (unsigned)(nch - 1);
-    }
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-    if (par == 0) {
-      float M = -INFINITY;
-      for (int ch = 0; ch < nch; ++ch) {
-        const int64_t it = ((int64_t)ch * p.ntiles * p.B + (int64_t)tile * p.B + b) * p.Hkv + kvh;
-        M = fmaxf(M, p.partial[(it * kTileRows + rg * 32 + r32) * (D + 2) + D]);
-      }
-      const float Mu = M == -INFINITY ? 0.f : M;
-      float Lsum = 0.f;
-#pragma unroll
-      for (int j = 0; j < NJ; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[j][r] = 0.f;
-      for (int ch = 0; ch < nch; ++ch) {
-        const int64_t it = ((int64_t)ch * p.ntiles * p.B + (int64_t)tile * p.B + b) * p.Hkv + kvh;
-        const float* pr = p.partial + (it * kTileRows + rg * 32 + r32) * (D + 2);
-        const float w = __builtin_amdgcn_exp2f((pr[D] - Mu) * c);
-        Lsum += pr[D + 1] * w;
-#pragma unroll
-        for (int j = 0; j < NJ; ++j)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) o[j][r] += pr[NJ * (8 * (r / 4) + 4 * h + (r & 3)) + j] * w;
-      }
-      m = M;
-      l = Lsum;
-    }
-    if (threadIdx.x == 0) p.counter[tile_id] = 0u;  // leave the counter clean
+      for (int r = 0; r < 16; ++r) o[j][r] = o[j][r] * a0 + mrg[rg][head_dim<NJ>(r, j, h)][r32] * a1;
   }
 
   // ---- final normalisation and store
-  if (par == 0 && row_ok) {
-    const float inv = (kept && l > 0.f) ? 1.f / l : 0.f;
-    uint16_t* orow = p.out + qrow * D;
+  const float inv = (kept && l > 0.f) ? 1.f / l : 0.f;
+  uint16_t* orow = p.out + qrow * D;
 #pragma unroll
-    for (int qd = 0; qd < 4; ++qd) {
-      // 4*NJ consecutive head dims start at NJ*(8*qd + 4h)
-      uint32_t w[2 * NJ];
+  for (int qd = 0; qd < 4; ++qd) {
+    // 4*NJ consecutive head dims start at NJ*(8*qd + 4h)
+    uint32_t w[2 * NJ];
 #pragma unroll
-      for (int e = 0; e < 4 * NJ; e += 2) {
-        const int r0 = 4 * qd + e / NJ, j0 = e % NJ;
-        const int r1 = 4 * qd + (e + 1) / NJ, j1 = (e + 1) % NJ;
-        w[e / 2] = f32_to_bf16(o[j0][r0] * inv) | (f32_to_bf16(o[j1][r1] * inv) << 16);
-      }
-      uint16_t* dst = orow + NJ * (8 * qd + 4 * h);
-      *(u32x4*)dst = u32x4{w[0], w[1], w[2], w[3]};
-      if constexpr (NJ == 4) *(u32x4*)(dst + 8) = u32x4{w[4], w[5], w[6], w[7]};
+    for (int e = 0; e < 4 * NJ; e += 2) {
+      const int r0 = 4 * qd + e / NJ, j0 = e % NJ;
+      const int r1 = 4 * qd + (e + 1) / NJ, j1 = (e + 1) % NJ;
+      w[e / 2] = f32_to_bf16(o[j0][r0] * inv) | (f32_to_bf16(o[j1][r1] * inv) << 16);
     }
-    if (p.lse && h == 0) {
-      const int64_t li = ((int64_t)b * p.Hq + qh) * ((int64_t)p.A * p.gamma) + (int64_t)ua * p.gamma + uk;
-      p.lse[li] = (kept && l > 0.f) ? m * p.scale + kLn2 * __builtin_amdgcn_logf(l) : -INFINITY;
-    }
+    uint16_t* dst = orow + NJ * (8 * qd + 4 * h);
+    *(u32x4*)dst = u32x4{w[0], w[1], w[2], w[3]};
+    if constexpr (NJ == 4) *(u32x4*)(dst + 8) = u32x4{w[4], w[5], w[6], w[7]};
+  }
+  if (p.lse && h == 0) {
+    const int64_t li = ((int64_t)b * p.Hq + qh) * ((int64_t)p.A * p.gamma) + (int64_t)ua * p.gamma + uk;
+    p.lse[li] = (kept && l > 0.f) ? m * p.scale + kLn2 * __builtin_amdgcn_logf(l) : -INFINITY;
   }
 }
 
@@ -430,23 +482,17 @@ __global__ __launch_bounds__(64) void block_attn_valu(Params p, int D) {
   }
 }
 
-__global__ void zero_u32_kernel(unsigned* p, int64_t n) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = 0u;
-}
-
 struct Shape {
-  int group, ntiles, nrows, nch_max;
-  int64_t items;
+  int group, ntiles, nrows;
+  int64_t tiles;  // B * ntiles * Hkv
 };
 
-Shape make_shape(int B, int A, int gamma, int Hq, int Hkv, int max_ctx) {
+Shape make_shape(int B, int A, int gamma, int Hq, int Hkv) {
   Shape s{};
   s.group = Hq / Hkv;
   s.nrows = A * s.group * gamma;
   s.ntiles = (s.nrows + kTileRows - 1) / kTileRows;
-  s.nch_max = max_ctx > 0 ? (max_ctx + kChunk - 1) / kChunk : 1;
-  s.items = (int64_t)s.nch_max * s.ntiles * B * Hkv;
+  s.tiles = (int64_t)s.ntiles * B * Hkv;
   return s;
 }
 
@@ -454,12 +500,10 @@ Shape make_shape(int B, int A, int gamma, int Hq, int Hkv, int max_ctx) {
 
 extern "C" size_t dspark_block_attention_workspace_bytes(int B, int A, int gamma, int Hq, int Hkv,
                                                          int D, int max_ctx) {
-  if (B <= 0 || A <= 0 || gamma <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || D <= 0 || max_ctx < 0)
-    return 0;
-  const Shape s = make_shape(B, A, gamma, Hq, Hkv, max_ctx);
-  const size_t part = s.nch_max > 1 ? (size_t)s.items * kTileRows * (D + 2) * sizeof(float) : 0;
-  const size_t cnt = (size_t)s.ntiles * B * Hkv * sizeof(unsigned);
-  return dspark_host::align_up(part, 256) + dspark_host::align_up(cnt, 256);
+  (void)D; (void)max_ctx;
+  if (B <= 0 || A <= 0 || gamma <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || max_ctx < 0) return 0;
+  const Shape s = make_shape(B, A, gamma, Hq, Hkv);
+  return dspark_host::align_up((size_t)s.tiles * sizeof(int32_t), 256);
 }
 
 extern "C" int dspark_block_attention(const void* q, const void* k_ctx, const void* v_ctx,
@@ -487,7 +531,7 @@ extern "C" int dspark_block_attention(const void* q, const void* k_ctx, const vo
       (total_ctx > 0 && (!k_ctx || !v_ctx)))
     return fail(DSPARK_ERR_INVALID_ARG, "block_attention: null required pointer");
   hipStream_t s = (hipStream_t)stream;
-  const Shape sh = make_shape(B, A, gamma, Hq, Hkv, max_ctx);
+  const Shape sh = make_shape(B, A, gamma, Hq, Hkv);
   Params p{};
   p.q = (const uint16_t*)q; p.kc = (const uint16_t*)k_ctx; p.vc = (const uint16_t*)v_ctx;
   p.offs = ctx_offsets; p.kb = (const uint16_t*)k_blk; p.vb = (const uint16_t*)v_blk;
@@ -502,16 +546,14 @@ extern "C" int dspark_block_attention(const void* q, const void* k_ctx, const vo
     const size_t need = dspark_block_attention_workspace_bytes(B, A, gamma, Hq, Hkv, D, max_ctx);
     if (ws_bytes < need || (need && !ws))
       return fail(DSPARK_ERR_WORKSPACE, "block_attention: workspace %zu bytes < %zu", ws_bytes, need);
-    const size_t part = sh.nch_max > 1 ? (size_t)sh.items * kTileRows * (D + 2) * sizeof(float) : 0;
-    p.partial = (float*)ws;
-    p.counter = (unsigned*)((char*)ws + align_up(part, 256));
-    const int64_t ncnt = (int64_t)sh.ntiles * B * Hkv;
-    hipLaunchKernelGGL(zero_u32_kernel, dim3((unsigned)((ncnt + 255) / 256)), dim3(256), 0, s, p.counter, ncnt);
-    if (sh.items >= (1ll << 31)) return fail(DSPARK_ERR_INVALID_ARG, "block_attention: grid too large");
+    if (sh.tiles >= (1ll << 31)) return fail(DSPARK_ERR_INVALID_ARG, "block_attention: grid too large");
+    int32_t* order = (int32_t*)ws;
+    hipLaunchKernelGGL(attn_plan_kernel, dim3(1), dim3(1024), 0, s, p, order);
+    p.order = order;
     if (D == 128)
-      hipLaunchKernelGGL(block_attn_mfma<128>, dim3((unsigned)sh.items), dim3(kThreads), 0, s, p);
+      hipLaunchKernelGGL(block_attn_mfma<128>, dim3((unsigned)sh.tiles), dim3(kThreads), 0, s, p);
     else
-      hipLaunchKernelGGL(block_attn_mfma<64>, dim3((unsigned)sh.items), dim3(kThreads), 0, s, p);
+      hipLaunchKernelGGL(block_attn_mfma<64>, dim3((unsigned)sh.tiles), dim3(kThreads), 0, s, p);
   } else {
     const int64_t nb = (int64_t)B * A * Hq;
     if (nb >= (1ll << 31)) return fail(DSPARK_ERR_INVALID_ARG, "block_attention: grid too large");

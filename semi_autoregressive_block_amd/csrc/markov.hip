@@ -61,139 +61,175 @@ __device__ __forceinline__ void fold_key_global(uint64_t* dst, uint64_t key) {
 }
 
 // ----------------------------------------------------------------- MFMA path
-// NMB: 16-row m-blocks per workgroup (rows per row group = 16*NMB, shared by
-// all four waves).  KS: maximum number of 32-wide rank steps (r <= 32*KS).
-template <int NMB, int KS>
-__global__ __launch_bounds__(kThreads) void markov_step_mfma(
+// NW waves per workgroup, 16 rows per wave (row group = 16*NW rows), KS
+// maximum 32-wide rank steps.  The vocabulary is cut into 64-column tiles
+// handed out interleaved: at step t of its loop workgroup w owns tile
+// t*grid + w, so the workgroups running side by side read one contiguous
+// span of every W2 row and every base row.  W2[0:r, tile] is staged through
+// a double-buffered LDS tile while the next tile's W2 and base slices are in
+// flight (register staging).  Every global load is unconditional from a
+// clamped, always-valid address (invalid lanes are zeroed after the load),
+// so the loads stay in flight across the MFMA work instead of serialising
+// behind branches.
+constexpr int kTileCols = 64;
+constexpr int kLdsRow = kTileCols * 2 + 8;  // bytes per staged W2 row (+8: spreads banks)
+
+template <int NW, int KS>
+__global__ __launch_bounds__(64 * NW) void markov_step_mfma(
     const float* __restrict__ base, const uint16_t* __restrict__ w1,
     const uint16_t* __restrict__ w2, const int32_t* __restrict__ first_prev,
     const uint64_t* __restrict__ keys_prev, uint64_t* __restrict__ keys_out,
     float* __restrict__ step_logits, int R, int gamma, int V, int r, int step, float invT,
     int greedy, uint32_t seed_lo, uint32_t seed_hi, int32_t* __restrict__ status) {
   extern __shared__ __align__(16) unsigned char smem[];
-  constexpr int RW = 16 * NMB;
-  const int rpad = ((r + 31) / 32) * 32;  // rank rounded up to a whole step
-  const int estride = rpad + 8;           // bf16 elements per LDS row (+16 B: fewer bank conflicts)
-  uint16_t* E = (uint16_t*)smem;
-  uint64_t* rowkey = (uint64_t*)(smem + (size_t)RW * estride * 2);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int n = lane & 15, g = lane >> 4;
-  const int row0 = blockIdx.y * RW;
+  constexpr int NT = 64 * NW;                       // threads
+  constexpr int STG = (KS * 32 * 8 + NT - 1) / NT;  // 16-byte W2 pieces per thread per tile
+  const int rpad = ((r + 31) / 32) * 32;
   const int ks = rpad / 32;
+  unsigned char* buf0 = smem;
+  unsigned char* buf1 = smem + (size_t)rpad * kLdsRow;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 15, g = lane >> 4;
+  const int rowbase = blockIdx.y * 16 * NW + wave * 16;
 
-  // ---- gather E = W1[prev] for this row group into LDS (zero-padded)
-  for (int c = threadIdx.x; c < RW * (estride / 8); c += kThreads) {
-    const int rr = c / (estride / 8), kc = (c % (estride / 8)) * 8;
-    const int row = row0 + rr;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (row < R && kc < r) {
-      const int p = decode_prev(keys_prev, first_prev, row, V, nullptr);
-      v = *(const u32x4*)(w1 + (int64_t)p * r + kc);
-    }
-    *(u32x4*)(E + rr * estride + kc) = v;
-  }
-  for (int i = threadIdx.x; i < RW; i += kThreads) rowkey[i] = 0ull;
-  if (threadIdx.x < RW && row0 + threadIdx.x < R && blockIdx.x == 0)
-    decode_prev(keys_prev, first_prev, row0 + threadIdx.x, V, status);  // flag bad tokens once
-  __syncthreads();
+  const int ntiles_all = (V + kTileCols - 1) / kTileCols;
+  const int ntile = ntiles_all > (int)blockIdx.x ? (ntiles_all - 1 - (int)blockIdx.x) / (int)gridDim.x + 1 : 0;
+  auto tile_col = [&](int t) -> int64_t { return ((int64_t)t * gridDim.x + blockIdx.x) * kTileCols; };
 
-  // ---- this wave's vocabulary range, in quads of 4 columns
-  const int64_t nq = V / 4;
-  const int64_t nw = (int64_t)gridDim.x * 4;
-  const int64_t gw = (int64_t)blockIdx.x * 4 + wave;
-  const int64_t q0 = gw * nq / nw, q1 = (gw + 1) * nq / nw;
-
-  float best_z[NMB][4];
-  uint32_t best_v[NMB][4];
+  // ---- E = W1[prev] as MFMA A operands: row rowbase + n, rank 32kk + 8g .. +7
+  u32x4 ea[KS];
+  {
+    const int row = rowbase + n;
+    const int pv = decode_prev(keys_prev, first_prev, min(row, R - 1), V,
+                               blockIdx.x == 0 && g == 0 && row < R ? status : nullptr);
 #pragma unroll
-  for (int mb = 0; mb < NMB; ++mb)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) { best_z[mb][i] = -INFINITY; best_v[mb][i] = 0xffffffffu; }
-
-  for (int64_t qt = q0; qt < q1; qt += kSubTile / 4) {
-    const int64_t myq = qt + n;          // this lane's quad
-    const bool colok = myq < q1;
-    const int64_t v0 = myq * 4;          // first of this lane's 4 columns
-    f32x4 acc[NMB][4];
-#pragma unroll
-    for (int mb = 0; mb < NMB; ++mb)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[mb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
     for (int kk = 0; kk < KS; ++kk) {
-      if (kk >= ks) break;
-      u32x2 raw[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int k = kk * 32 + g * 8 + i;
-        raw[i] = (colok && k < r) ? *(const u32x2*)(w2 + (int64_t)k * V + v0) : u32x2{0u, 0u};
+      if (kk < ks) {
+        const int k = kk * 32 + g * 8;
+        const u32x4 v = *(const u32x4*)(w1 + (int64_t)pv * r + min(k, r - 8));
+        ea[kk] = (row < R && k < r) ? v : u32x4{0u, 0u, 0u, 0u};
+      } else {
+        ea[kk] = u32x4{0u, 0u, 0u, 0u};
       }
-      u32x4 b[4];
+    }
+  }
+
+  // staging of one tile's W2 rows: piece i of thread t is row (t + i*NT) / 8,
+  // octet (t + i*NT) % 8 of the tile
+  auto stage_load = [&](int t, u32x4* st) {
+    const int64_t tc = tile_col(t);
 #pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        b[0][p] = pack_lo(raw[2 * p].x, raw[2 * p + 1].x);
-        b[1][p] = pack_hi(raw[2 * p].x, raw[2 * p + 1].x);
-        b[2][p] = pack_lo(raw[2 * p].y, raw[2 * p + 1].y);
-        b[3][p] = pack_hi(raw[2 * p].y, raw[2 * p + 1].y);
-      }
+    for (int i = 0; i < STG; ++i) {
+      const int pc = threadIdx.x + i * NT;
+      const int k = pc >> 3, oc = pc & 7;
+      const int64_t col = tc + oc * 8;
+      const u32x4 v = *(const u32x4*)(w2 + (int64_t)min(k, r - 1) * V + min(col, (int64_t)V - 8));
+      st[i] = (k < r && col < V) ? v : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto stage_store = [&](unsigned char* bufp, const u32x4* st) {
 #pragma unroll
-      for (int mb = 0; mb < NMB; ++mb) {
-        const u32x4 a = *(const u32x4*)(E + (mb * 16 + n) * estride + kk * 32 + g * 8);
+    for (int i = 0; i < STG; ++i) {
+      const int pc = threadIdx.x + i * NT;
+      const int k = pc >> 3, oc = pc & 7;
+      if (KS * 32 == rpad || k < rpad) *(u32x4*)(bufp + k * kLdsRow + oc * 16) = st[i];
+    }
+  };
+  // base slices of the lane's four rows (4g + i) at columns tile + 4n .. +3
+  auto base_load = [&](int t, f32x4* bs) {
+    const int64_t col = min(tile_col(t) + 4 * n, (int64_t)V - 4);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[mb][j] = mfma16x16x32(a, b[j], acc[mb][j]);
+    for (int i = 0; i < 4; ++i) {
+      const int row = min(rowbase + 4 * g + i, R - 1);
+      bs[i] = *(const f32x4*)(base + ((int64_t)row * gamma + step) * V + col);
+    }
+  };
+
+  float best_z[4];
+  uint32_t best_v[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { best_z[i] = -INFINITY; best_v[i] = 0xffffffffu; }
+
+  u32x4 st[STG];
+  f32x4 bs[4], bsn[4];
+  if (ntile > 0) {
+    stage_load(0, st);
+    base_load(0, bs);
+    stage_store(buf0, st);
+  }
+  __syncthreads();
+  for (int t = 0; t < ntile; ++t) {
+    unsigned char* cur = (t & 1) ? buf1 : buf0;
+    unsigned char* nxt = (t & 1) ? buf0 : buf1;
+    const int tn = min(t + 1, ntile - 1);  // clamped: the prefetch is unconditional
+    stage_load(tn, st);
+    base_load(tn, bsn);
+
+    f32x4 acc[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      if (kk < ks) {
+        u32x2 raw[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) raw[i] = *(const u32x2*)(cur + (kk * 32 + g * 8 + i) * kLdsRow + n * 8);
+        u32x4 b[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          b[0][q] = pack_lo(raw[2 * q].x, raw[2 * q + 1].x);
+          b[1][q] = pack_hi(raw[2 * q].x, raw[2 * q + 1].x);
+          b[2][q] = pack_lo(raw[2 * q].y, raw[2 * q + 1].y);
+          b[3][q] = pack_hi(raw[2 * q].y, raw[2 * q + 1].y);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[j] = mfma16x16x32(ea[kk], b[j], acc[j]);
       }
     }
 
     // ---- epilogue: base add, optional store, Gumbel, running argmax
-    if (colok) {
-#pragma unroll
-      for (int mb = 0; mb < NMB; ++mb) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = row0 + mb * 16 + g * 4 + i;
-          if (row < R) {
-            const int64_t off = ((int64_t)row * gamma + step) * V + v0;
-            const f32x4 bs = *(const f32x4*)(base + off);
-            f32x4 l;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) l[j] = acc[mb][j][i] + bs[j];
-            if (step_logits) *(f32x4*)(step_logits + off) = l;
-            f32x4 z = l;
-            if (!greedy) {
-              const u32x4 x = philox4x32_10(u32x4{(uint32_t)myq, (uint32_t)step, (uint32_t)row, 0u},
-                                            seed_lo, seed_hi);
-#pragma unroll
-              for (int j = 0; j < 4; ++j) z[j] = fmaf(l[j], invT, gumbel_from_bits(x[j]));
-            }
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              if (z[j] > best_z[mb][i]) { best_z[mb][i] = z[j]; best_v[mb][i] = (uint32_t)(v0 + j); }
-            }
-          }
-        }
-      }
-    }
-  }
-
-  // ---- fold: 16 lanes sharing a row, then the four waves, then the grid
-#pragma unroll
-  for (int mb = 0; mb < NMB; ++mb) {
+    const int64_t v0 = tile_col(t) + 4 * n;
+    const bool colok = v0 < V;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      uint64_t key = best_v[mb][i] == 0xffffffffu ? 0ull : argmax_key(best_z[mb][i], best_v[mb][i]);
+      const int row = rowbase + 4 * g + i;
+      f32x4 l;
 #pragma unroll
-      for (int m = 1; m < 16; m <<= 1) {
-        const uint64_t o = shfl_xor_u64(key, m);
-        key = o > key ? o : key;
+      for (int j = 0; j < 4; ++j) l[j] = acc[j][i] + bs[i][j];
+      if (step_logits && colok && row < R)
+        *(f32x4*)(step_logits + ((int64_t)row * gamma + step) * V + v0) = l;
+      f32x4 z = l;
+      if (!greedy) {
+        const u32x4 x = philox4x32_10(u32x4{(uint32_t)(v0 >> 2), (uint32_t)step, (uint32_t)row, 0u},
+                                      seed_lo, seed_hi);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) z[j] = fmaf(l[j], invT, gumbel_from_bits(x[j]));
       }
-      if (n == 0 && key) atomicMax((unsigned long long*)&rowkey[mb * 16 + g * 4 + i], (unsigned long long)key);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bool better = colok && z[j] > best_z[i];
+        best_z[i] = better ? z[j] : best_z[i];
+        best_v[i] = better ? (uint32_t)(v0 + j) : best_v[i];
+      }
     }
+    stage_store(nxt, st);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) bs[i] = bsn[i];
+    __syncthreads();
   }
-  __syncthreads();
-  if (threadIdx.x < RW) {
-    const int row = row0 + threadIdx.x;
-    const uint64_t key = rowkey[threadIdx.x];
-    if (row < R && key) fold_key_global(keys_out + row, key);
+
+  // ---- fold: the 16 lanes sharing a row, then the grid
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint64_t key = best_v[i] == 0xffffffffu ? 0ull : argmax_key(best_z[i], best_v[i]);
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) {
+      const uint64_t o = shfl_xor_u64(key, m);
+      key = o > key ? o : key;
+    }
+    const int row = rowbase + 4 * g + i;
+    if (n == 0 && key && row < R) fold_key_global(keys_out + row, key);
   }
 }
 
@@ -306,17 +342,17 @@ int cu_count() {
   return cus;
 }
 
-template <int NMB, int KS>
+template <int NW, int KS>
 hipError_t launch_mfma(int grid_x, int grid_y, hipStream_t s, const float* base, const uint16_t* w1,
                        const uint16_t* w2, const int32_t* first_prev, const uint64_t* kp,
                        uint64_t* ko, float* step_logits, int R, int gamma, int V, int r, int step,
                        float invT, int greedy, uint32_t slo, uint32_t shi, int32_t* st) {
   const int rpad = ((r + 31) / 32) * 32;
-  const size_t shm = (size_t)16 * NMB * (rpad + 8) * 2 + (size_t)16 * NMB * 8;
-  auto kern = markov_step_mfma<NMB, KS>;
+  const size_t shm = (size_t)2 * rpad * kLdsRow;
+  auto kern = markov_step_mfma<NW, KS>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(grid_x, grid_y), dim3(kThreads), shm, s, base, w1, w2, first_prev,
+  hipLaunchKernelGGL(kern, dim3(grid_x, grid_y), dim3(64 * NW), shm, s, base, w1, w2, first_prev,
                      kp, ko, step_logits, R, gamma, V, r, step, invT, greedy, slo, shi, st);
   return hipGetLastError();
 }
@@ -369,18 +405,21 @@ extern "C" int dspark_markov_sample(const float* base_logits, const void* w1, co
     uint64_t* ko = keys + (int64_t)step * R;
     hipError_t e = hipSuccess;
     if (mfma_ok) {
-      // 64-row groups (grid.y); one workgroup per compute unit and two per
-      // unit when a single row group exists, each wave a balanced vocabulary
-      // range
-      const int gy = (R + 63) / 64;
-      int gx = gy == 1 ? 2 * cus : cus;
-      const int64_t quads = V / 4;
-      if ((int64_t)gx * 4 > quads) gx = (int)((quads + 3) / 4);
+      // up to 128 rows per workgroup (8 waves, one compute unit each); up to
+      // 64 rows use 4 waves and two workgroups per compute unit
+      const bool wide = R > 64;
+      const int rows_per = wide ? 128 : 64;
+      const int gy = (R + rows_per - 1) / rows_per;
+      int gx = wide ? cus : 2 * cus;
+      const int64_t tiles = (V + 63) / 64;
+      if (gx > tiles) gx = (int)tiles;
       if (gx < 1) gx = 1;
-      if (r <= 256)
-        e = launch_mfma<4, 8>(gx, gy, s, base_logits, (const uint16_t*)w1, (const uint16_t*)w2, first_prev, kp, ko, step_logits, R, gamma, V, r, step, invT, greedy, slo, shi, dev_status);
+      if (wide)
+        e = r <= 256 ? launch_mfma<8, 8>(gx, gy, s, base_logits, (const uint16_t*)w1, (const uint16_t*)w2, first_prev, kp, ko, step_logits, R, gamma, V, r, step, invT, greedy, slo, shi, dev_status)
+                     : launch_mfma<8, 16>(gx, gy, s, base_logits, (const uint16_t*)w1, (const uint16_t*)w2, first_prev, kp, ko, step_logits, R, gamma, V, r, step, invT, greedy, slo, shi, dev_status);
       else
-        e = launch_mfma<4, 16>(gx, gy, s, base_logits, (const uint16_t*)w1, (const uint16_t*)w2, first_prev, kp, ko, step_logits, R, gamma, V, r, step, invT, greedy, slo, shi, dev_status);
+        e = r <= 256 ? launch_mfma<4, 8>(gx, gy, s, base_logits, (const uint16_t*)w1, (const uint16_t*)w2, first_prev, kp, ko, step_logits, R, gamma, V, r, step, invT, greedy, slo, shi, dev_status)
+                     : launch_mfma<4, 16>(gx, gy, s, base_logits, (const uint16_t*)w1, (const uint16_t*)w2, first_prev, kp, ko, step_logits, R, gamma, V, r, step, invT, greedy, slo, shi, dev_status);
     } else {
       const int gy = (R + kRowChunk - 1) / kRowChunk;
       int gx = 2 * cus;

@@ -47,10 +47,9 @@ def test_version_and_empty_error(lib):
 
 def test_workspace_queries(lib):
     _, L = lib
-    # multi-chunk attention needs partials; one chunk only needs counters
-    big = L.dspark_block_attention_workspace_bytes(128, 1, 16, 32, 8, 128, 8192)
-    small = L.dspark_block_attention_workspace_bytes(128, 1, 16, 32, 8, 128, 512)
-    assert big > small > 0
+    # attention needs one int32 launch-order slot per (request, tile, KV head)
+    assert L.dspark_block_attention_workspace_bytes(128, 1, 16, 32, 8, 128, 8192) == 128 * 8 * 4
+    assert L.dspark_block_attention_workspace_bytes(1, 512, 8, 32, 8, 128, 4096) == 256 * 8 * 4
     assert L.dspark_block_attention_workspace_bytes(1, 1, 1, 3, 2, 128, 10) == 0  # Hq % Hkv
     assert L.dspark_markov_sample_workspace_bytes(64, 16, 151936, 256, 1) == 64 * 16 * 8
     assert L.dspark_accept_rate_workspace_bytes(4, 512, 8, 151936, 1) > 0
