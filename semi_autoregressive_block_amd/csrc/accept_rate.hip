@@ -21,6 +21,10 @@
 // 16-bit integer max/min (two elements per instruction).
 #include <stdlib.h>
 
+#include <map>
+#include <mutex>
+#include <utility>
+
 #include "common.h"
 
 using namespace dspark;
@@ -337,12 +341,20 @@ int device_cus() {
   return cus;
 }
 
+// Co-resident workgroups of `kernel` on the current device, cached per
+// (device, kernel): the occupancy query is far slower than a launch.
 int device_wg_capacity(const void* kernel) {
+  static std::mutex mu;
+  static std::map<std::pair<int, const void*>, int> cache;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return -1;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find({dev, kernel});
+  if (it != cache.end()) return it->second;
   int cus = 0, per = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, kThreads, 0) != hipSuccess) return -1;
+  cache[{dev, kernel}] = cus * per;
   return cus * per;
 }
 

@@ -20,10 +20,15 @@
 //   into the epilogue of each 64-column sub-tile.
 // * Row maxima are folded with 64-bit keys (order-preserving float bits,
 //   then the inverted index so ties go to the lowest index): 16-lane
-//   shuffles, an LDS atomic max across the waves, then one global atomic max
-//   per row, skipped when the current global key is already larger.  The
-//   next step decodes prev from those keys on the device; there is no host
-//   round trip inside the gamma loop.
+//   shuffles, then one device-scope atomic max per row and workgroup into
+//   one of 16 replica slots of the row (memory-side atomics on one address
+//   serialise; replicas spread them).  The next step decodes prev from the
+//   maximum over the replicas on the device; there is no host round trip
+//   inside the gamma loop.
+#include <atomic>
+#include <map>
+#include <mutex>
+
 #include "common.h"
 #include "philox.h"
 
@@ -32,7 +37,17 @@ using namespace dspark;
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kSubTile = 64;  // vocabulary columns per wave sub-tile (16 lanes x 4)
+
+// Per-row argmax keys are folded with device-scope atomics, which MI355X
+// executes at the memory side; thousands of them on the same few cache
+// lines serialise.  Each row therefore has kKeyReplicas slots, each replica
+// in its own 4 KB-aligned region: workgroup w folds into replica w % 16 and
+// readers take the maximum over the replicas.
+constexpr int kKeyReplicas = 16;
+__host__ __device__ __forceinline__ int64_t replica_stride(int R) {  // in 64-bit keys
+  return ((int64_t)R * 8 + 4095) / 4096 * 512;
+}
+__host__ __device__ __forceinline__ int64_t keys_per_step(int R) { return kKeyReplicas * replica_stride(R); }
 
 __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
   const uint32_t lo = __shfl_xor((uint32_t)v, m, kWave);
@@ -40,11 +55,21 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
   return ((uint64_t)hi << 32) | lo;
 }
 
+__device__ __forceinline__ uint64_t read_key(const uint64_t* keys, int row, int R) {
+  uint64_t k = 0;
+#pragma unroll
+  for (int q = 0; q < kKeyReplicas; ++q) {
+    const uint64_t x = keys[q * replica_stride(R) + row];
+    k = x > k ? x : k;
+  }
+  return k;
+}
+
 __device__ __forceinline__ int decode_prev(const uint64_t* keys_prev, const int32_t* first_prev,
-                                           int row, int V, int32_t* status) {
+                                           int row, int R, int V, int32_t* status) {
   int p;
   if (keys_prev) {
-    p = (int)argmax_key_index(keys_prev[row]);
+    p = (int)argmax_key_index(read_key(keys_prev, row, R));
   } else {
     p = first_prev[row];
   }
@@ -55,9 +80,9 @@ __device__ __forceinline__ int decode_prev(const uint64_t* keys_prev, const int3
   return p;
 }
 
-__device__ __forceinline__ void fold_key_global(uint64_t* dst, uint64_t key) {
-  const uint64_t cur = __hip_atomic_load(dst, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if (key > cur) atomicMax((unsigned long long*)dst, (unsigned long long)key);
+__device__ __forceinline__ void fold_key_global(uint64_t* keys, int row, int R, uint64_t key) {
+  uint64_t* dst = keys + (int64_t)(blockIdx.x % kKeyReplicas) * replica_stride(R) + row;
+  atomicMax((unsigned long long*)dst, (unsigned long long)key);
 }
 
 // ----------------------------------------------------------------- MFMA path
@@ -66,8 +91,8 @@ __device__ __forceinline__ void fold_key_global(uint64_t* dst, uint64_t key) {
 // handed out interleaved: at step t of its loop workgroup w owns tile
 // t*grid + w, so the workgroups running side by side read one contiguous
 // span of every W2 row and every base row.  W2[0:r, tile] is staged through
-// a double-buffered LDS tile while the next tile's W2 and base slices are in
-// flight (register staging).  Every global load is unconditional from a
+// a double-buffered LDS tile while the next TWO tiles' W2 and base slices are
+// in flight (two register staging sets).  Every global load is unconditional from a
 // clamped, always-valid address (invalid lanes are zeroed after the load),
 // so the loads stay in flight across the MFMA work instead of serialising
 // behind branches.
@@ -98,10 +123,11 @@ __global__ __launch_bounds__(64 * NW) void markov_step_mfma(
   auto tile_col = [&](int t) -> int64_t { return ((int64_t)t * gridDim.x + blockIdx.x) * kTileCols; };
 
   // ---- E = W1[prev] as MFMA A operands: row rowbase + n, rank 32kk + 8g .. +7
+  // (gathered after the first tiles' loads are in flight; see below)
   u32x4 ea[KS];
-  {
+  auto gather_e = [&]() {
     const int row = rowbase + n;
-    const int pv = decode_prev(keys_prev, first_prev, min(row, R - 1), V,
+    const int pv = decode_prev(keys_prev, first_prev, min(row, R - 1), R, V,
                                blockIdx.x == 0 && g == 0 && row < R ? status : nullptr);
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
@@ -113,7 +139,7 @@ __global__ __launch_bounds__(64 * NW) void markov_step_mfma(
         ea[kk] = u32x4{0u, 0u, 0u, 0u};
       }
     }
-  }
+  };
 
   // staging of one tile's W2 rows: piece i of thread t is row (t + i*NT) / 8,
   // octet (t + i*NT) % 8 of the tile
@@ -151,21 +177,8 @@ __global__ __launch_bounds__(64 * NW) void markov_step_mfma(
 #pragma unroll
   for (int i = 0; i < 4; ++i) { best_z[i] = -INFINITY; best_v[i] = 0xffffffffu; }
 
-  u32x4 st[STG];
-  f32x4 bs[4], bsn[4];
-  if (ntile > 0) {
-    stage_load(0, st);
-    base_load(0, bs);
-    stage_store(buf0, st);
-  }
-  __syncthreads();
-  for (int t = 0; t < ntile; ++t) {
-    unsigned char* cur = (t & 1) ? buf1 : buf0;
-    unsigned char* nxt = (t & 1) ? buf0 : buf1;
-    const int tn = min(t + 1, ntile - 1);  // clamped: the prefetch is unconditional
-    stage_load(tn, st);
-    base_load(tn, bsn);
-
+  // MFMA over one staged tile, then the fused epilogue
+  auto compute_tile = [&](int t, const unsigned char* cur, const f32x4* bs) {
     f32x4 acc[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -187,8 +200,6 @@ __global__ __launch_bounds__(64 * NW) void markov_step_mfma(
         for (int j = 0; j < 4; ++j) acc[j] = mfma16x16x32(ea[kk], b[j], acc[j]);
       }
     }
-
-    // ---- epilogue: base add, optional store, Gumbel, running argmax
     const int64_t v0 = tile_col(t) + 4 * n;
     const bool colok = v0 < V;
 #pragma unroll
@@ -213,9 +224,41 @@ __global__ __launch_bounds__(64 * NW) void markov_step_mfma(
         best_v[i] = better ? (uint32_t)(v0 + j) : best_v[i];
       }
     }
-    stage_store(nxt, st);
+  };
+
+  // Two tiles in flight: staging set A/B alternate, LDS buffers 0/1 alternate.
+  u32x4 stA[STG], stB[STG];
+  f32x4 bA[4], bB[4], bs[4];
+  // the first two tiles do not depend on the previous step's tokens: their
+  // loads go out before the dependent key -> W1 row gather
+  if (ntile > 0) {
+    stage_load(0, stA);
+    base_load(0, bA);
+    stage_load(min(1, ntile - 1), stB);
+    base_load(min(1, ntile - 1), bB);
+  }
+  gather_e();
+  if (ntile > 0) {
+    stage_store(buf0, stA);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) bs[i] = bsn[i];
+    for (int i = 0; i < 4; ++i) bs[i] = bA[i];
+  }
+  __syncthreads();
+  for (int t = 0; t < ntile; t += 2) {
+    stage_load(min(t + 2, ntile - 1), stA);
+    base_load(min(t + 2, ntile - 1), bA);
+    compute_tile(t, buf0, bs);
+    stage_store(buf1, stB);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) bs[i] = bB[i];
+    __syncthreads();
+    if (t + 1 >= ntile) break;
+    stage_load(min(t + 3, ntile - 1), stB);
+    base_load(min(t + 3, ntile - 1), bB);
+    compute_tile(t + 1, buf1, bs);
+    stage_store(buf0, stA);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) bs[i] = bA[i];
     __syncthreads();
   }
 
@@ -229,7 +272,7 @@ __global__ __launch_bounds__(64 * NW) void markov_step_mfma(
       key = o > key ? o : key;
     }
     const int row = rowbase + 4 * g + i;
-    if (n == 0 && key && row < R) fold_key_global(keys_out + row, key);
+    if (n == 0 && key && row < R) fold_key_global(keys_out, row, R, key);
   }
 }
 
@@ -258,12 +301,12 @@ __global__ __launch_bounds__(kThreads) void markov_step_valu(
   for (int c = threadIdx.x; c < kRowChunk * r; c += kThreads) {
     const int rr = c / r, k = c % r, row = row0 + rr;
     float v = 0.f;
-    if (row < R) v = w1((int64_t)decode_prev(keys_prev, first_prev, row, V, nullptr) * r + k);
+    if (row < R) v = w1((int64_t)decode_prev(keys_prev, first_prev, row, R, V, nullptr) * r + k);
     E[c] = v;
   }
   if (threadIdx.x < kRowChunk) rowkey[threadIdx.x] = 0ull;
   if (threadIdx.x < kRowChunk && row0 + threadIdx.x < R && blockIdx.x == 0)
-    decode_prev(keys_prev, first_prev, row0 + threadIdx.x, V, status);
+    decode_prev(keys_prev, first_prev, row0 + threadIdx.x, R, V, status);
   __syncthreads();
 
   const int64_t nq = (V + 3) / 4;
@@ -316,7 +359,7 @@ __global__ __launch_bounds__(kThreads) void markov_step_valu(
   if (threadIdx.x < kRowChunk) {
     const int row = row0 + threadIdx.x;
     const uint64_t key = rowkey[threadIdx.x];
-    if (row < R && key) fold_key_global(keys_out + row, key);
+    if (row < R && key) fold_key_global(keys_out, row, R, key);
   }
 }
 
@@ -330,16 +373,34 @@ __global__ void finalize_tokens_kernel(const uint64_t* __restrict__ keys, int32_
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // over [R, gamma]
   if (i >= (int64_t)R * gamma) return;
   const int row = (int)(i / gamma), step = (int)(i % gamma);
-  uint32_t t = argmax_key_index(keys[(int64_t)step * R + row]);
+  uint32_t t = argmax_key_index(read_key(keys + (int64_t)step * keys_per_step(R), row, R));
   if (t >= (uint32_t)V) { status_or(status, DSPARK_STATUS_BAD_TOKEN); t = 0; }
   tokens[i] = (int32_t)t;
 }
 
 int cu_count() {
+  static std::atomic<int> cache[64];  // per device, 0 = unknown
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess) return -1;
+  if (dev >= 0 && dev < 64 && (cus = cache[dev].load(std::memory_order_relaxed)) > 0) return cus;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
+  if (dev >= 0 && dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
   return cus;
+}
+
+// Raise a kernel's dynamic-LDS limit once per process (the call costs tens
+// of microseconds of host time, far more than a step's launch).
+template <typename K>
+hipError_t allow_lds_once(K kern, size_t bytes) {
+  static std::mutex mu;
+  static std::map<const void*, size_t> done;
+  std::lock_guard<std::mutex> lock(mu);
+  size_t& have = done[(const void*)kern];
+  if (have >= bytes) return hipSuccess;
+  const hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           (int)bytes);
+  if (e == hipSuccess) have = bytes;
+  return e;
 }
 
 template <int NW, int KS>
@@ -350,7 +411,7 @@ hipError_t launch_mfma(int grid_x, int grid_y, hipStream_t s, const float* base,
   const int rpad = ((r + 31) / 32) * 32;
   const size_t shm = (size_t)2 * rpad * kLdsRow;
   auto kern = markov_step_mfma<NW, KS>;
-  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+  hipError_t e = allow_lds_once(kern, shm);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(grid_x, grid_y), dim3(64 * NW), shm, s, base, w1, w2, first_prev,
                      kp, ko, step_logits, R, gamma, V, r, step, invT, greedy, slo, shi, st);
@@ -362,7 +423,7 @@ hipError_t launch_mfma(int grid_x, int grid_y, hipStream_t s, const float* base,
 extern "C" size_t dspark_markov_sample_workspace_bytes(int R, int gamma, int V, int r, int wdtype) {
   (void)V; (void)r; (void)wdtype;
   if (R <= 0 || gamma <= 0) return 0;
-  return (size_t)R * gamma * sizeof(uint64_t);
+  return (size_t)gamma * keys_per_step(R) * sizeof(uint64_t);
 }
 
 extern "C" int dspark_markov_sample(const float* base_logits, const void* w1, const void* w2,
@@ -387,8 +448,8 @@ extern "C" int dspark_markov_sample(const float* base_logits, const void* w1, co
     return fail(DSPARK_ERR_WORKSPACE, "markov_sample: workspace %zu bytes < %zu", ws_bytes, need);
   if ((uintptr_t)ws % 8) return fail(DSPARK_ERR_INVALID_ARG, "markov_sample: workspace not 8-byte aligned");
   hipStream_t s = (hipStream_t)stream;
-  uint64_t* keys = (uint64_t*)ws;  // [gamma][R]
-  const int64_t nk = (int64_t)R * gamma;
+  uint64_t* keys = (uint64_t*)ws;  // [gamma][kKeyReplicas][replica_stride(R)]
+  const int64_t nk = (int64_t)gamma * keys_per_step(R);
   hipLaunchKernelGGL(zero_u64_kernel, dim3((unsigned)((nk + 255) / 256)), dim3(256), 0, s, keys, nk);
   const int greedy = temperature == 0.f;
   const float invT = greedy ? 1.f : 1.f / temperature;
@@ -401,8 +462,8 @@ extern "C" int dspark_markov_sample(const float* base_logits, const void* w1, co
                        (uintptr_t)w2 % 16 == 0 && (uintptr_t)base_logits % 16 == 0 &&
                        (!step_logits || (uintptr_t)step_logits % 16 == 0);
   for (int step = 0; step < gamma; ++step) {
-    const uint64_t* kp = step == 0 ? nullptr : keys + (int64_t)(step - 1) * R;
-    uint64_t* ko = keys + (int64_t)step * R;
+    const uint64_t* kp = step == 0 ? nullptr : keys + (int64_t)(step - 1) * keys_per_step(R);
+    uint64_t* ko = keys + (int64_t)step * keys_per_step(R);
     hipError_t e = hipSuccess;
     if (mfma_ok) {
       // up to 128 rows per workgroup (8 waves, one compute unit each); up to
@@ -428,17 +489,18 @@ extern "C" int dspark_markov_sample(const float* base_logits, const void* w1, co
       if (gx < 1) gx = 1;
       const size_t shm = (size_t)kRowChunk * r * 4 + kRowChunk * 8;
       if (bf) {
-        (void)hipFuncSetAttribute((const void*)markov_step_valu<true>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+        (void)allow_lds_once(markov_step_valu<true>, shm);
         hipLaunchKernelGGL(markov_step_valu<true>, dim3(gx, gy), dim3(kThreads), shm, s, base_logits, w1, w2, first_prev, kp, ko, step_logits, R, gamma, V, r, step, invT, greedy, slo, shi, dev_status);
       } else {
-        (void)hipFuncSetAttribute((const void*)markov_step_valu<false>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+        (void)allow_lds_once(markov_step_valu<false>, shm);
         hipLaunchKernelGGL(markov_step_valu<false>, dim3(gx, gy), dim3(kThreads), shm, s, base_logits, w1, w2, first_prev, kp, ko, step_logits, R, gamma, V, r, step, invT, greedy, slo, shi, dev_status);
       }
       e = hipGetLastError();
     }
     if (e != hipSuccess) return fail(DSPARK_ERR_HIP, "markov_sample step %d: %s", step, hipGetErrorString(e));
   }
-  hipLaunchKernelGGL(finalize_tokens_kernel, dim3((unsigned)((nk + 255) / 256)), dim3(256), 0, s, keys,
+  const int64_t ntok = (int64_t)R * gamma;
+  hipLaunchKernelGGL(finalize_tokens_kernel, dim3((unsigned)((ntok + 255) / 256)), dim3(256), 0, s, keys,
                      tokens, R, gamma, V, dev_status);
   return check_launch("markov_sample");
 }

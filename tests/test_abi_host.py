@@ -51,7 +51,9 @@ def test_workspace_queries(lib):
     assert L.dspark_block_attention_workspace_bytes(128, 1, 16, 32, 8, 128, 8192) == 128 * 8 * 4
     assert L.dspark_block_attention_workspace_bytes(1, 512, 8, 32, 8, 128, 4096) == 256 * 8 * 4
     assert L.dspark_block_attention_workspace_bytes(1, 1, 1, 3, 2, 128, 10) == 0  # Hq % Hkv
-    assert L.dspark_markov_sample_workspace_bytes(64, 16, 151936, 256, 1) == 64 * 16 * 8
+    # gamma steps x 16 replica slots per row, each replica 4 KB-aligned
+    assert L.dspark_markov_sample_workspace_bytes(64, 16, 151936, 256, 1) == 16 * 16 * 4096
+    assert L.dspark_markov_sample_workspace_bytes(600, 2, 151936, 256, 1) == 2 * 16 * 8192
     assert L.dspark_accept_rate_workspace_bytes(4, 512, 8, 151936, 1) > 0
 
 
