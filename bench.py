@@ -48,6 +48,39 @@ def parse():
     return ap.parse_args()
 
 
+KERNEL_SOURCES = {
+    "block_attn_mfma<128>": "semi_autoregressive_block_amd/csrc/attention.hip",
+    "markov_step_mfma": "semi_autoregressive_block_amd/csrc/markov.hip",
+}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+
+
+def source_digest(kernel):
+    import hashlib
+    h = hashlib.sha256()
+    for rel in (KERNEL_SOURCES[kernel], "semi_autoregressive_block_amd/csrc/common.h"):
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary: FETCH_SIZE and WRITE_SIZE per dispatch, each scaled by what the
+    same counter reads for a copy of known size.  None when there is no
+    summary or the kernel's source changed since it was taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)[kernel]
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("source_sha256") != source_digest(kernel):
+        return None
+    fetch = rec["fetch_kib"] * rec["copy_bytes"] / rec["copy_fetch_kib"]
+    write = rec["write_kib"] * rec["copy_bytes"] / rec["copy_write_kib"]
+    return fetch + write
+
+
 def timed(torch, fn, steps, warmup):
     """Average ms of fn() over `steps` runs after `warmup`, bracketed by
     device synchronisation; events recorded on the current stream (the
@@ -220,12 +253,15 @@ def main():
     mk_launch_ms = r["markov_ms"] / r["markov_steps"]
     mk_gbs = r["markov_step_bytes"] / mk_launch_ms / 1e6
     if r["attn_ms"] >= r["markov_ms"]:
-        roof = dict(kernel="block_attn_mfma<128>", bound="hbm", achieved=attn_gbs,
-                    peak=HBM_PEAK_GBS, unit="GB/s", frac=attn_gbs / HBM_PEAK_GBS, traffic=None,
-                    bytes_per_launch=r["attn_bytes"], launch_ms=r["attn_ms"])
+        k = "block_attn_mfma<128>"
+        roof = dict(kernel=k, bound="hbm", achieved=attn_gbs,
+                    peak=HBM_PEAK_GBS, unit="GB/s", frac=attn_gbs / HBM_PEAK_GBS,
+                    traffic=measured_traffic(k), bytes_per_launch=r["attn_bytes"],
+                    launch_ms=r["attn_ms"])
     else:
-        roof = dict(kernel="markov_step_mfma", bound="hbm", achieved=mk_gbs, peak=HBM_PEAK_GBS,
-                    unit="GB/s", frac=mk_gbs / HBM_PEAK_GBS, traffic=None,
+        k = "markov_step_mfma"
+        roof = dict(kernel=k, bound="hbm", achieved=mk_gbs, peak=HBM_PEAK_GBS,
+                    unit="GB/s", frac=mk_gbs / HBM_PEAK_GBS, traffic=measured_traffic(k),
                     bytes_per_launch=r["markov_step_bytes"], launch_ms=mk_launch_ms)
     line = {
         "metric": "drafted tokens/s per draft round (attn+Markov)",
