@@ -4,23 +4,30 @@
 //   accept = clamp(1 - 1/2 sum_v |p_v - q_v|, 0, 1),  p = softmax(draft), q = softmax(target)
 //
 // computed through the equivalent form 1 - TV(p, q) = sum_v min(p_v, q_v)
-// (valid because both distributions sum to one): with
-// y_v = x_v * log2(e) - (M * log2(e) + log2 S), p_v = 2^{y_v}, and since 2^y
-// is monotonic, min(p_v, q_v) = 2^{min(yd_v, yt_v)} costs one exponential per
-// element pair instead of two.
+// (valid because both distributions sum to one), which needs no absolute
+// value and lets each workgroup fold its slice into one partial sum.
 //
 // HBM-bound design for gfx950: a row (2 x V logits) is split over a cluster of
-// G workgroups.  Each workgroup loads its slice of both tensors ONCE into
-// registers (16-byte coalesced loads), computes its local max and sum, and the
-// cluster exchanges (max, sum) through a few bytes of global memory; pass two
-// runs on the register-resident slice and the last workgroup of the cluster to
-// finish folds the partial sums (in fixed order, so results are deterministic)
-// and writes the accept rate.  The grid is persistent and launched
-// cooperatively so every workgroup of a cluster is co-resident; every wait is
-// bounded.  The maximum of bf16 data is taken on the raw bits with packed
-// 16-bit integer max/min (two elements per instruction).
+// G workgroups that stay resident for the whole launch (cooperative grid).
+// Each workgroup has three data waves and one exchange wave.  The data waves
+// turn their slice of both tensors into exponentials 2^{x log2e - a}
+// relative to the slice's own maximum a and sum them (pass one).  The row's
+// normaliser needs every slice's (max, sum), which the exchange wave trades
+// with the cluster through a few bytes of global memory; it issues no other
+// loads, so its polls never queue behind the data waves' streaming loads.
+// The exchange is pipelined: while it runs, the data waves park the row's
+// exponentials in LDS and go on with pass one of the next row; pass two of
+// a row (one multiply, one min and one add per element pair, no second
+// exponential) runs one iteration later.  Cluster members may therefore drift
+// apart by up to an iteration without stalling one another.  The next row's
+// slice streams in (16-byte buffer loads; a row past the end reads through an
+// empty buffer range, so the tail costs no traffic) while the current one is
+// reduced.  Each workgroup writes its slice's share of sum_v min(p_v, q_v) to
+// the workspace and a small kernel folds the G shares of a row in fixed
+// order (deterministic results) into the accept rate and tau.
 #include <stdlib.h>
 
+#include <algorithm>
 #include <map>
 #include <mutex>
 #include <utility>
@@ -31,247 +38,375 @@ using namespace dspark;
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kMaxVec = 5;  // 16-byte vectors per thread per tensor (152 VGPRs: 3 WGs per CU)
+constexpr int kDataWaves = 3;
+constexpr int kDataThreads = kDataWaves * kWave;  // threads that hold the row slice
+constexpr int kThreads = kDataThreads + kWave;    // plus the exchange wave
+constexpr int kVec = 3;                           // 16-byte vectors per data thread per tensor
+constexpr int kChunkVec = kDataThreads * kVec;    // vectors of one tensor per workgroup and row
+constexpr int kMaxG = 2 * kWave;                  // two cluster members per exchange lane
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr unsigned kSpinLimit = 1u << 26;  // bounded wait (~seconds), then flag and go on
-
-typedef short short2v __attribute__((ext_vector_type(2)));
+constexpr unsigned kSpinLimit = 1u << 20;  // bounded wait (well under a second), then flag and go on
+constexpr int kRsrcWord3 = 0x00020000;      // raw 32-bit buffer data format (gfx9 family)
+constexpr int kNonTemporal = 2;             // streaming loads
+constexpr int kLdsBytesPerCU = 160 * 1024;
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+// IEEE-754-2019 maximum / minimum (NaN-propagating): one v_maximum3 /
+// v_minimum3 each on gfx950, with no operand canonicalisation.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ __forceinline__ float vmin(float a, float b) { return __builtin_elementwise_minimum(a, b); }
 
+// ---- wave reductions: DPP inside each row of 16 lanes, then the four row
+// results through scalar registers.  Every lane returns the same value, and
+// the combination order is fixed, so equal inputs give equal bits anywhere.
+template <int kCtrl>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), kCtrl, 0xF, 0xF, false));
+}
+constexpr int kDppQuadSwap1 = 0xB1;   // quad_perm [1,0,3,2]
+constexpr int kDppQuadSwap2 = 0x4E;   // quad_perm [2,3,0,1]
+constexpr int kDppRowMirror = 0x140;
+constexpr int kDppHalfMirror = 0x141;
+
+__device__ __forceinline__ float lane_value(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+__device__ __forceinline__ float uniform(float v) {
+  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));
+}
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
+  v = vmax(v, dpp<kDppQuadSwap1>(v));
+  v = vmax(v, dpp<kDppQuadSwap2>(v));
+  v = vmax(v, dpp<kDppHalfMirror>(v));
+  v = vmax(v, dpp<kDppRowMirror>(v));
+  return vmax(vmax(lane_value(v, 0), lane_value(v, 16)), vmax(lane_value(v, 32), lane_value(v, 48)));
 }
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  v += dpp<kDppQuadSwap1>(v);
+  v += dpp<kDppQuadSwap2>(v);
+  v += dpp<kDppHalfMirror>(v);
+  v += dpp<kDppRowMirror>(v);
+  return (lane_value(v, 0) + lane_value(v, 16)) + (lane_value(v, 32) + lane_value(v, 48));
 }
 
-// Reduce two floats over the workgroup (max or sum); all threads get the result.
-template <bool kMax>
-__device__ __forceinline__ void block_reduce2(float& a, float& b, float* red) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  a = kMax ? wave_max(a) : wave_sum(a);
-  b = kMax ? wave_max(b) : wave_sum(b);
-  __syncthreads();  // red[] may still be read by the previous reduction
-  if (lane == 0) { red[w] = a; red[4 + w] = b; }
-  __syncthreads();
-  if (kMax) {
-    a = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    b = fmaxf(fmaxf(red[4], red[5]), fmaxf(red[6], red[7]));
-  } else {
-    a = (red[0] + red[1]) + (red[2] + red[3]);
-    b = (red[4] + red[5]) + (red[6] + red[7]);
+// ---- cluster exchange without fences.  A member publishes the four floats
+// of a row's slice statistics as one 16-byte word (two 64-bit relaxed
+// agent-scope atomic stores), and readers fetch it with two 64-bit relaxed
+// agent-scope atomic loads; these bypass the per-XCD, mutually incoherent
+// L2s and, unlike volatile accesses, make the wave wait for nothing until
+// the value is used.  Every 32-bit lane of the word is single-copy atomic
+// and carries a one-bit tag in its lowest mantissa bit, so a reader accepts
+// the word only when all four tags equal the tag of the epoch it waits for.
+// The slots alternate between two parities, so a slot awaited for epoch e
+// holds either epoch e, epoch e - 2 or (first use) the zeros of the launch;
+// the tag ((e + 1) >> 1) & 1 tells e from both, so no fence or per-poll
+// cache maintenance is needed.  Dropping one mantissa bit changes a value
+// by at most one unit in its last place.
+__device__ __forceinline__ uint32_t epoch_tag(uint32_t epoch) { return ((epoch + 1u) >> 1) & 1u; }
+__device__ __forceinline__ uint32_t tagged(float v, uint32_t tag) { return (__float_as_uint(v) & ~1u) | tag; }
+__device__ __forceinline__ void publish(u32x4* slot, float a0, float s0, float a1, float s1, uint32_t epoch) {
+  const uint32_t tg = epoch_tag(epoch);
+  uint64_t* q = (uint64_t*)slot;
+  __hip_atomic_store(q, ((uint64_t)tagged(s0, tg) << 32) | tagged(a0, tg), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(q + 1, ((uint64_t)tagged(s1, tg) << 32) | tagged(a1, tg), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ u32x4 peek(const u32x4* slot) {
+  uint64_t* q = (uint64_t*)slot;
+  const uint64_t lo = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint64_t hi = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return u32x4{(uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32)};
+}
+__device__ __forceinline__ bool fresh(const u32x4& w, uint32_t epoch) {
+  const uint32_t tg = epoch_tag(epoch);
+  return ((w[0] & 1u) == tg) & ((w[1] & 1u) == tg) & ((w[2] & 1u) == tg) & ((w[3] & 1u) == tg);
+}
+
+// Statistics of a workgroup's slice for one tensor, from the per-wave values
+// in LDS: a = max * log2(e) (0 when the slice holds only -inf), and the sum
+// of 2^{x log2e - a}.  Data wave 0 (which publishes them) and the exchange
+// wave (which uses them) run this same code, so both hold identical bits.
+struct SliceStats {
+  float a, s;
+};
+__device__ __forceinline__ SliceStats slice_stats(const float* wmax, const float* wsum) {
+  const float m = vmax(vmax(wmax[0], wmax[1]), wmax[2]);
+  return {m == -INFINITY ? 0.f : m * kLog2e, (wsum[0] + wsum[1]) + wsum[2]};
+}
+
+// bf16 (or float32) vector of the raw slice -> float32 values; lanes whose
+// vector lies past the row end hold zeros (empty buffer range) and are made
+// -inf, which drops them from the max and turns their exponentials into 0.
+template <bool kBf16>
+__device__ __forceinline__ void unpack(const u32x4& r, float* x, bool valid) {
+  const uint32_t pad = valid ? 0u : 0xff800000u;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    if (kBf16) {
+      x[2 * c] = __uint_as_float((r[c] << 16) | pad);
+      x[2 * c + 1] = __uint_as_float((r[c] & 0xffff0000u) | pad);
+    } else {
+      x[c] = __uint_as_float(r[c] | pad);
+    }
   }
 }
-
-// Largest value among the bf16 pairs reduced with packed int16 max/min.
-__device__ __forceinline__ float bf16_pair_max(short2v mx, short2v mn) {
-  const short hmax = mx.x > mx.y ? mx.x : mx.y;
-  if (hmax >= 0) return __uint_as_float((uint32_t)(uint16_t)hmax << 16);
-  // every element is negative: the largest is the one of smallest magnitude,
-  // whose sign-magnitude pattern is the smallest as int16
-  const short hmin = mn.x < mn.y ? mn.x : mn.y;
-  return __uint_as_float((uint32_t)(uint16_t)hmin << 16);
+template <bool kBf16>
+__device__ __forceinline__ void unpack_fast(const u32x4& r, float* x) {
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    if (kBf16) {
+      x[2 * c] = bf16lo(r[c]);
+      x[2 * c + 1] = bf16hi(r[c]);
+    } else {
+      x[c] = __uint_as_float(r[c]);
+    }
+  }
 }
 
 template <bool kBf16>
-__device__ __forceinline__ float vec_max(const u32x4* v, int nvalid) {
-  if (kBf16) {
-    short2v mx = {(short)-32768, (short)-32768}, mn = {(short)32767, (short)32767};
-#pragma unroll
-    for (int i = 0; i < kMaxVec; ++i) {
-      if (i < nvalid) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          short2v s = __builtin_bit_cast(short2v, v[i][c]);
-          mx = __builtin_elementwise_max(mx, s);
-          mn = __builtin_elementwise_min(mn, s);
-        }
-      }
-    }
-    return nvalid > 0 ? bf16_pair_max(mx, mn) : -INFINITY;
-  } else {
-    float m = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < kMaxVec; ++i)
-      if (i < nvalid)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) m = fmaxf(m, __uint_as_float(v[i][c]));
-    return m;
-  }
-}
+struct Shape {
+  static constexpr int kEl = kBf16 ? 8 : 4;  // elements per 16-byte vector
+  static constexpr int kN = kVec * kEl;      // floats per data thread per tensor
+  static constexpr int kPark = 2 * kN / 4;   // float4 slots per data thread (both tensors)
+};
 
-// sum of 2^{x*log2e - mL} over the thread's elements
-template <bool kBf16>
-__device__ __forceinline__ float vec_sumexp(const u32x4* v, int nvalid, float mL) {
-  float s0 = 0.f, s1 = 0.f;
-#pragma unroll
-  for (int i = 0; i < kMaxVec; ++i) {
-    if (i < nvalid) {
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const uint32_t w = v[i][c];
-        if (kBf16) {
-          s0 += exp2_fast(fmaf(bf16lo(w), kLog2e, -mL));
-          s1 += exp2_fast(fmaf(bf16hi(w), kLog2e, -mL));
-        } else {
-          s0 += exp2_fast(fmaf(__uint_as_float(w), kLog2e, -mL));
-        }
-      }
-    }
-  }
-  return s0 + s1;
-}
-
-// sum of 2^{min(yd, yt)}
-template <bool kBf16>
-__device__ __forceinline__ float vec_summin(const u32x4* dv, const u32x4* tv, int nvalid,
-                                            float offd, float offt) {
-  float s0 = 0.f, s1 = 0.f;
-#pragma unroll
-  for (int i = 0; i < kMaxVec; ++i) {
-    if (i < nvalid) {
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const uint32_t a = dv[i][c], b = tv[i][c];
-        if (kBf16) {
-          s0 += exp2_fast(fminf(fmaf(bf16lo(a), kLog2e, -offd), fmaf(bf16lo(b), kLog2e, -offt)));
-          s1 += exp2_fast(fminf(fmaf(bf16hi(a), kLog2e, -offd), fmaf(bf16hi(b), kLog2e, -offt)));
-        } else {
-          s0 += exp2_fast(fminf(fmaf(__uint_as_float(a), kLog2e, -offd),
-                                fmaf(__uint_as_float(b), kLog2e, -offt)));
-        }
-      }
-    }
-  }
-  return s0 + s1;
-}
-
-// ---- cluster exchange without fences.  Every published float travels with
-// its iteration number ("epoch") in one 64-bit word written and read with
-// relaxed agent-scope atomics (coherent across the XCDs' L2s), so a reader
-// that sees the right epoch also sees the value: no release/acquire cache
-// maintenance per poll.  Epochs start at 1; the slots are zeroed per launch.
-__device__ __forceinline__ void publish(uint64_t* slot, float v, uint32_t epoch) {
-  const uint64_t w = ((uint64_t)epoch << 32) | __float_as_uint(v);
-  __hip_atomic_store(slot, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-// Bounded wait for one slot; NaN (and a flag) on time-out.
-__device__ __forceinline__ float collect(uint64_t* slot, uint32_t epoch, int32_t* err, bool& ok) {
-  unsigned n = 0;
-  for (;;) {
-    const uint64_t w = __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if ((uint32_t)(w >> 32) == epoch) return __uint_as_float((uint32_t)w);
-    if (!ok || ++n > kSpinLimit) {
-      if (ok) atomicOr(err, 1);
-      ok = false;
-      return NAN;
-    }
-    __builtin_amdgcn_s_sleep(1);
-  }
-}
-
-// Workspace per cluster: slots[2 phases][2 parities][G][4] 64-bit words.
+// Workspace: shares [rows][G] float | slots [clusters][2 parities][G] 16-byte words | error word.
 template <bool kBf16>
 __global__ __launch_bounds__(kThreads) void tv_cluster_kernel(
-    const u32x4* __restrict__ d, const u32x4* __restrict__ t, float* __restrict__ accept,
-    int64_t rows, int vec_per_row, int vec_per_wg, int G, int nclusters,
-    uint64_t* __restrict__ slots, int32_t* __restrict__ err) {
-  __shared__ float red[8];
-  __shared__ float bcast[4];
+    const char* __restrict__ d, const char* __restrict__ t, float* __restrict__ share,
+    int64_t rows, int V, int vec_per_row, int G, int nclusters,
+    u32x4* __restrict__ slots, int32_t* __restrict__ err) {
+  constexpr int kEl = Shape<kBf16>::kEl, kN = Shape<kBf16>::kN, kPark = Shape<kBf16>::kPark;
+  __shared__ f32x4 park[kPark][kDataThreads];  // the previous row's exponentials
+  __shared__ float red_max[2][2][kDataWaves], red_sum[2][2][kDataWaves], red_part[kDataWaves];
+  __shared__ float glob[2][2];  // [parity of the row][draft, target]
   const int cl = blockIdx.x / G, g = blockIdx.x % G;
-  const int v0 = g * vec_per_wg;
-  const int v1 = min(v0 + vec_per_wg, vec_per_row);
-  const int first = v0 + (int)threadIdx.x;
-  const int nvalid = first < v1 ? min(kMaxVec, (v1 - first + kThreads - 1) / kThreads) : 0;
-  uint64_t* cslots = slots + (size_t)cl * 16 * G;
-  int it = 0;
-  bool ok = true;  // after one timed-out wait this workgroup stops waiting
-  for (int64_t row = cl; row < rows; row += nclusters, ++it) {
-    const uint32_t epoch = (uint32_t)it + 1u;
-    uint64_t* slotA = cslots + (0 * 2 + (it & 1)) * G * 4;
-    uint64_t* slotB = cslots + (1 * 2 + (it & 1)) * G * 4;
-    const u32x4* dr = d + row * vec_per_row;
-    const u32x4* tr = t + row * vec_per_row;
-    u32x4 dv[kMaxVec], tv[kMaxVec];
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform role
+  const uint32_t row_bytes = (uint32_t)V * (kBf16 ? 2u : 4u);
+  u32x4* cslots = slots + (size_t)cl * 2 * G;
+  const int64_t nk = (rows - cl + nclusters - 1) / nclusters;  // rows of this cluster (cl < rows)
+
+  if (w < kDataWaves) {
+    // ------------------------------------------------------------ data waves
+    const int tid = threadIdx.x;
+    const int vbase = g * kChunkVec;
+    // slot i of this thread is vector vbase + i * kDataThreads + tid of the
+    // row: one per-lane byte offset plus a per-slot scalar offset.  Vectors
+    // past the row end fall outside the buffer range and read as zeros.
+    const uint32_t voff = (uint32_t)(vbase + tid) * 16u;
+    bool full[kVec];
 #pragma unroll
-    for (int i = 0; i < kMaxVec; ++i) {
-      if (i < nvalid) {
-        dv[i] = __builtin_nontemporal_load(dr + first + i * kThreads);
-        tv[i] = __builtin_nontemporal_load(tr + first + i * kThreads);
-      }
-    }
-    // ---- local statistics (max, then sum relative to the workgroup max)
-    float md = vec_max<kBf16>(dv, nvalid), mt = vec_max<kBf16>(tv, nvalid);
-    block_reduce2<true>(md, mt, red);
-    float sd = vec_sumexp<kBf16>(dv, nvalid, md * kLog2e);
-    float st = vec_sumexp<kBf16>(tv, nvalid, mt * kLog2e);
-    block_reduce2<false>(sd, st, red);
-    // ---- cluster exchange of (max, sum) for both tensors
-    float Md = md, Sd = sd, Mt = mt, St = st;
-    if (G > 1) {
-      if (threadIdx.x < 4) {
-        const float mine = threadIdx.x == 0 ? md : threadIdx.x == 1 ? sd : threadIdx.x == 2 ? mt : st;
-        publish(slotA + g * 4 + threadIdx.x, mine, epoch);
-      }
-      // lanes j < G of wave 0 collect workgroup j's statistics
-      if (threadIdx.x < 64) {
-        const int j = threadIdx.x;
-        float mj = -INFINITY, sj = 0.f, nj = -INFINITY, tj = 0.f;
-        if (j < G) {
-          mj = collect(slotA + j * 4 + 0, epoch, err, ok);
-          sj = collect(slotA + j * 4 + 1, epoch, err, ok);
-          nj = collect(slotA + j * 4 + 2, epoch, err, ok);
-          tj = collect(slotA + j * 4 + 3, epoch, err, ok);
-        }
-        float a = mj, b = nj;
+    for (int i = 0; i < kVec; ++i) full[i] = vbase + (i + 1) * kDataThreads <= vec_per_row;  // uniform
+    u32x4 rd[kVec], rt[kVec];
+    auto issue = [&](int64_t row) {
+      const bool in = row < rows;
+      const int64_t off = (in ? row : 0) * (int64_t)row_bytes;
+      const int nrec = in ? (int)row_bytes : 0;
+      const __amdgpu_buffer_rsrc_t sd = __builtin_amdgcn_make_buffer_rsrc((void*)(d + off), 0, nrec, kRsrcWord3);
+      const __amdgpu_buffer_rsrc_t st = __builtin_amdgcn_make_buffer_rsrc((void*)(t + off), 0, nrec, kRsrcWord3);
 #pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          a = fmaxf(a, __shfl_xor(a, o, kWave));
-          b = fmaxf(b, __shfl_xor(b, o, kWave));
+      for (int i = 0; i < kVec; ++i) {
+        rd[i] = __builtin_amdgcn_raw_buffer_load_b128(sd, voff, i * kDataThreads * 16, kNonTemporal);
+        rt[i] = __builtin_amdgcn_raw_buffer_load_b128(st, voff, i * kDataThreads * 16, kNonTemporal);
+      }
+    };
+    issue(cl);
+    for (int64_t k = 0; k <= nk; ++k) {
+      const int64_t row = cl + k * nclusters;
+      const bool have = k < nk;  // iteration nk only finishes the last row
+      const int par = (int)(k & 1);
+      float xd[kN], xt[kN];
+      if (have) {
+#pragma unroll
+        for (int i = 0; i < kVec; ++i) {
+          if (full[i]) {
+            unpack_fast<kBf16>(rd[i], xd + i * kEl);
+            unpack_fast<kBf16>(rt[i], xt + i * kEl);
+          } else {
+            const bool valid = vbase + i * kDataThreads + tid < vec_per_row;
+            unpack<kBf16>(rd[i], xd + i * kEl, valid);
+            unpack<kBf16>(rt[i], xt + i * kEl, valid);
+          }
         }
-        float sa = sj > 0.f ? sj * exp2_fast((mj - a) * kLog2e) : 0.f;
-        float sb = tj > 0.f ? tj * exp2_fast((nj - b) * kLog2e) : 0.f;
-        // fixed-order sum over j (lanes) so every workgroup gets identical bits
-        float SA = 0.f, SB = 0.f;
-        for (int q = 0; q < G; ++q) {
-          SA += __shfl(sa, q, kWave);
-          SB += __shfl(sb, q, kWave);
+        issue(row + nclusters);  // the next row streams in while this one is reduced
+        float md = xd[0], mt = xt[0];
+#pragma unroll
+        for (int i = 1; i < kN; ++i) {
+          md = vmax(md, xd[i]);
+          mt = vmax(mt, xt[i]);
         }
-        const bool poisoned = __any(!ok);  // a timed-out wait poisons the row
-        if (j == 0) {
-          bcast[0] = poisoned ? NAN : a;
-          bcast[1] = SA; bcast[2] = b; bcast[3] = SB;
+        md = wave_max(md);
+        mt = wave_max(mt);
+        if (lane == 0) { red_max[par][0][w] = md; red_max[par][1][w] = mt; }
+      }
+      __syncthreads();  // A: slice maxima of row k; the partial sums of row k-2 are complete
+      if (have) {
+        const float mD = vmax(vmax(red_max[par][0][0], red_max[par][0][1]), red_max[par][0][2]);
+        const float mT = vmax(vmax(red_max[par][1][0], red_max[par][1][1]), red_max[par][1][2]);
+        const float aD = mD == -INFINITY ? 0.f : mD * kLog2e;
+        const float aT = mT == -INFINITY ? 0.f : mT * kLog2e;
+        float sd0 = 0.f, sd1 = 0.f, st0 = 0.f, st1 = 0.f;
+#pragma unroll
+        for (int i = 0; i < kN; i += 2) {
+          xd[i] = exp2_fast(fmaf(xd[i], kLog2e, -aD));
+          xd[i + 1] = exp2_fast(fmaf(xd[i + 1], kLog2e, -aD));
+          xt[i] = exp2_fast(fmaf(xt[i], kLog2e, -aT));
+          xt[i + 1] = exp2_fast(fmaf(xt[i + 1], kLog2e, -aT));
+          sd0 += xd[i]; sd1 += xd[i + 1];
+          st0 += xt[i]; st1 += xt[i + 1];
+        }
+        const float wsd = wave_sum(sd0 + sd1), wst = wave_sum(st0 + st1);
+        if (lane == 0) { red_sum[par][0][w] = wsd; red_sum[par][1][w] = wst; }
+      }
+      __syncthreads();  // B: sums of row k; the exchange wave has the offsets of row k-1
+      if (k >= 1) {
+        // pass two of row k-1 on its parked exponentials:
+        // p_v = ed_v * 2^{eD}, q_v = et_v * 2^{eT}; the side with the smaller
+        // exponent is scaled down (never up: no overflow, and 0 * c stays 0)
+        const float eD = uniform(glob[(k - 1) & 1][0]), eT = uniform(glob[(k - 1) & 1][1]);
+        float p0 = 0.f, p1 = 0.f;
+        if (eD >= eT) {
+          const float c = exp2_fast(eT - eD);
+#pragma unroll
+          for (int j = 0; j < kN / 4; ++j) {
+            const f32x4 a = park[j][tid], b = park[kN / 4 + j][tid];
+            p0 += vmin(a[0], b[0] * c); p1 += vmin(a[1], b[1] * c);
+            p0 += vmin(a[2], b[2] * c); p1 += vmin(a[3], b[3] * c);
+          }
+        } else {
+          const float c = exp2_fast(eD - eT);
+#pragma unroll
+          for (int j = 0; j < kN / 4; ++j) {
+            const f32x4 a = park[j][tid], b = park[kN / 4 + j][tid];
+            p0 += vmin(a[0] * c, b[0]); p1 += vmin(a[1] * c, b[1]);
+            p0 += vmin(a[2] * c, b[2]); p1 += vmin(a[3] * c, b[3]);
+          }
+        }
+        const float wp = wave_sum(p0 + p1);
+        if (lane == 0) red_part[w] = wp;  // times 2^{max(eD, eT)}: applied by the exchange wave
+      }
+      if (have) {
+#pragma unroll
+        for (int j = 0; j < kN / 4; ++j) {
+          park[j][tid] = f32x4{xd[4 * j], xd[4 * j + 1], xd[4 * j + 2], xd[4 * j + 3]};
+          park[kN / 4 + j][tid] = f32x4{xt[4 * j], xt[4 * j + 1], xt[4 * j + 2], xt[4 * j + 3]};
         }
       }
-      __syncthreads();
-      Md = bcast[0]; Sd = bcast[1]; Mt = bcast[2]; St = bcast[3];
     }
-    const float offd = Md * kLog2e + __builtin_amdgcn_logf(Sd);
-    const float offt = Mt * kLog2e + __builtin_amdgcn_logf(St);
-    // ---- pass two on the register-resident slice
-    float part = vec_summin<kBf16>(dv, tv, nvalid, offd, offt);
-    float dummy = 0.f;
-    block_reduce2<false>(part, dummy, red);
-    if (G == 1) {
-      if (threadIdx.x == 0) accept[row] = fminf(fmaxf(part, 0.f), 1.f);
-    } else {
-      if (threadIdx.x == 0) publish(slotB + g * 4, part, epoch);
-      // one workgroup per row (rotating) folds the partial sums in fixed order
-      if (g == it % G && threadIdx.x < 64) {
-        const int j = threadIdx.x;
-        const float pj = j < G ? collect(slotB + j * 4, epoch, err, ok) : 0.f;
-        float s = 0.f;
-        for (int q = 0; q < G; ++q) s += __shfl(pj, q, kWave);
-        if (j == 0) accept[row] = fminf(fmaxf(s, 0.f), 1.f);
+    __syncthreads();  // the last row's partial sums are complete
+  } else {
+    // --------------------------------------------------------- exchange wave
+    // It also does every global store of the workgroup (published statistics
+    // and shares), so that the data waves' waits on their streaming loads
+    // never include a store acknowledgement.  Its short, latency-bound
+    // sequence decides when the data waves may pass barrier B, so it issues
+    // ahead of them on its SIMD.
+    auto store_share = [&](int64_t kk) {  // share of the cluster's row kk, from red_part
+      if (lane == 0) {
+        const int pp = (int)(kk & 1);
+        const float scale = exp2_fast(vmax(glob[pp][0], glob[pp][1]));  // NaN stays NaN
+        share[(cl + kk * nclusters) * G + g] = ((red_part[0] + red_part[1]) + red_part[2]) * scale;
+      }
+    };
+    __builtin_amdgcn_s_setprio(3);
+    bool ok = true;  // after one timed-out wait this lane stops waiting
+    for (int64_t k = 0; k <= nk; ++k) {
+      unsigned n = 0;  // polls of this lane for this row, for the bound
+      // offsets of row k-1: the cluster publishes its slice statistics after
+      // its barrier B; lane l gathers members l and l + 64 (after barrier A)
+      const int par = (int)((k - 1) & 1);
+      const uint32_t epoch = (uint32_t)k;
+      float ad[2] = {-INFINITY, -INFINITY}, sd[2] = {0.f, 0.f};
+      float at[2] = {-INFINITY, -INFINITY}, st[2] = {0.f, 0.f};
+      bool got[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int j = lane + h * kWave;
+        got[h] = k == 0 || j >= G || j == g;  // nothing to fetch
+      }
+      auto poll = [&]() {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          if (!got[h]) {
+            const u32x4 v = peek(cslots + (size_t)par * G + lane + h * kWave);
+            if (fresh(v, epoch)) {
+              ad[h] = __uint_as_float(v[0]); sd[h] = __uint_as_float(v[1]);
+              at[h] = __uint_as_float(v[2]); st[h] = __uint_as_float(v[3]);
+              got[h] = true;
+            } else if (!ok || ++n > kSpinLimit) {
+              if (ok) atomicOr(err, 1);
+              ok = false;
+              got[h] = true;  // give up on this member: the row is poisoned below
+            }
+          }
+        }
+      };
+      __syncthreads();  // A
+      if (k >= 2) store_share(k - 2);
+      while (!__all(got[0] && got[1])) {
+        poll();
+        if (!__all(got[0] && got[1])) __builtin_amdgcn_s_sleep(1);
+      }
+      if (k >= 1) {
+        const SliceStats sD = slice_stats(red_max[par][0], red_sum[par][0]);
+        const SliceStats sT = slice_stats(red_max[par][1], red_sum[par][1]);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          if (lane + h * kWave == g) {  // this workgroup's own word, as the others read it
+            const uint32_t tg = epoch_tag(epoch);
+            ad[h] = __uint_as_float(tagged(sD.a, tg)); sd[h] = __uint_as_float(tagged(sD.s, tg));
+            at[h] = __uint_as_float(tagged(sT.a, tg)); st[h] = __uint_as_float(tagged(sT.s, tg));
+          }
+        }
+        // row normaliser in log2 units: off = M + log2(sum_j s_j 2^{a_j - M})
+        const float MD = wave_max(vmax(sd[0] > 0.f ? ad[0] : -INFINITY, sd[1] > 0.f ? ad[1] : -INFINITY));
+        const float MT = wave_max(vmax(st[0] > 0.f ? at[0] : -INFINITY, st[1] > 0.f ? at[1] : -INFINITY));
+        float xD = 0.f, xT = 0.f;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          xD += sd[h] > 0.f ? sd[h] * exp2_fast(ad[h] - MD) : 0.f;
+          xT += st[h] > 0.f ? st[h] * exp2_fast(at[h] - MT) : 0.f;
+        }
+        const float SD = wave_sum(xD), ST = wave_sum(xT);
+        const bool poisoned = __any(!ok);
+        if (lane == 0) {
+          glob[par][0] = poisoned ? NAN : sD.a - (MD + __builtin_amdgcn_logf(SD));
+          glob[par][1] = poisoned ? NAN : sT.a - (MT + __builtin_amdgcn_logf(ST));
+        }
+      }
+      __syncthreads();  // B
+      if (k < nk && lane == 0) {
+        const int pk = (int)(k & 1);
+        const SliceStats sD = slice_stats(red_max[pk][0], red_sum[pk][0]);
+        const SliceStats sT = slice_stats(red_max[pk][1], red_sum[pk][1]);
+        publish(cslots + (size_t)pk * G + g, sD.a, sD.s, sT.a, sT.s, (uint32_t)k + 1u);
       }
     }
+    __syncthreads();
+    if (nk >= 1) store_share(nk - 1);
   }
+}
+
+// accept[row] = clamp(sum_g share[row][g], 0, 1) in fixed order, and tau per
+// block of gamma rows (page 1 §3.10); one thread per block.
+__global__ void tv_finalize_kernel(const float* __restrict__ share, int G,
+                                   float* __restrict__ accept, const uint8_t* __restrict__ m,
+                                   float* __restrict__ tau, int64_t nblocks, int gamma) {
+  const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= nblocks) return;
+  float run = 1.f, s = 0.f;
+  for (int k = 0; k < gamma; ++k) {
+    const int64_t row = b * gamma + k;
+    float a = 0.f;
+    for (int j = 0; j < G; ++j) a += share[row * G + j];
+    a = fminf(fmaxf(a, 0.f), 1.f);
+    accept[row] = a;
+    run *= a * (m ? (float)(m[row] != 0) : 1.f);
+    s += run;
+  }
+  if (tau) tau[b] = 1.f + s;
 }
 
 __global__ void zero_u32_kernel(unsigned* p, int n) {
@@ -280,14 +415,27 @@ __global__ void zero_u32_kernel(unsigned* p, int n) {
 }
 
 // Fallback for rows that are not 16-byte aligned (V not a multiple of the
-// vector width): one workgroup per row, three streaming passes over global
-// memory.  Correctness path only.
+// vector width) or too long for one cluster: one workgroup per row, three
+// streaming passes over global memory.  Correctness path only.
+constexpr int kRowThreads = 256;
+
+template <bool kMax>
+__device__ __forceinline__ float block_reduce(float v, float* red) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  v = kMax ? wave_max(v) : wave_sum(v);
+  __syncthreads();  // red[] may still be read by the previous reduction
+  if (lane == 0) red[w] = v;
+  __syncthreads();
+  return kMax ? vmax(vmax(red[0], red[1]), vmax(red[2], red[3]))
+              : (red[0] + red[1]) + (red[2] + red[3]);
+}
+
 template <bool kBf16>
-__global__ __launch_bounds__(kThreads) void tv_rowwise_kernel(const void* __restrict__ d,
-                                                              const void* __restrict__ t,
-                                                              float* __restrict__ accept,
-                                                              int64_t rows, int V) {
-  __shared__ float red[8];
+__global__ __launch_bounds__(kRowThreads) void tv_rowwise_kernel(const void* __restrict__ d,
+                                                                 const void* __restrict__ t,
+                                                                 float* __restrict__ accept,
+                                                                 int64_t rows, int V) {
+  __shared__ float red[4];
   for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
     auto ld = [&](const void* p, int v) -> float {
       if (kBf16) {
@@ -297,20 +445,25 @@ __global__ __launch_bounds__(kThreads) void tv_rowwise_kernel(const void* __rest
       return ((const float*)p)[row * V + v];
     };
     float md = -INFINITY, mt = -INFINITY;
-    for (int v = threadIdx.x; v < V; v += kThreads) { md = fmaxf(md, ld(d, v)); mt = fmaxf(mt, ld(t, v)); }
-    block_reduce2<true>(md, mt, red);
+    for (int v = threadIdx.x; v < V; v += kRowThreads) {
+      md = fmaxf(md, ld(d, v));
+      mt = fmaxf(mt, ld(t, v));
+    }
+    md = block_reduce<true>(md, red);
+    mt = block_reduce<true>(mt, red);
     float sd = 0.f, st = 0.f;
-    for (int v = threadIdx.x; v < V; v += kThreads) {
+    for (int v = threadIdx.x; v < V; v += kRowThreads) {
       sd += exp2_fast((ld(d, v) - md) * kLog2e);
       st += exp2_fast((ld(t, v) - mt) * kLog2e);
     }
-    block_reduce2<false>(sd, st, red);
+    sd = block_reduce<false>(sd, red);
+    st = block_reduce<false>(st, red);
     const float offd = md * kLog2e + __builtin_amdgcn_logf(sd);
     const float offt = mt * kLog2e + __builtin_amdgcn_logf(st);
-    float s = 0.f, dummy = 0.f;
-    for (int v = threadIdx.x; v < V; v += kThreads)
+    float s = 0.f;
+    for (int v = threadIdx.x; v < V; v += kRowThreads)
       s += exp2_fast(fminf(fmaf(ld(d, v), kLog2e, -offd), fmaf(ld(t, v), kLog2e, -offt)));
-    block_reduce2<false>(s, dummy, red);
+    s = block_reduce<false>(s, red);
     if (threadIdx.x == 0) accept[row] = fminf(fmaxf(s, 0.f), 1.f);
   }
 }
@@ -329,11 +482,6 @@ __global__ void tau_kernel(const float* __restrict__ accept, const uint8_t* __re
   tau[i] = 1.f + s;
 }
 
-struct Plan {
-  bool vec;
-  int vec_per_row, G, vec_per_wg, nclusters;
-};
-
 int device_cus() {
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess) return -1;
@@ -342,7 +490,11 @@ int device_cus() {
 }
 
 // Co-resident workgroups of `kernel` on the current device, cached per
-// (device, kernel): the occupancy query is far slower than a launch.
+// (device, kernel): the occupancy query is far slower than a launch.  The
+// runtime's figure is capped by what the kernel's registers and LDS allow
+// (each workgroup of four waves puts one wave on each of the four SIMDs;
+// 512 VGPRs per SIMD lane, allocated in blocks of 8), so a cluster never
+// waits on a member that the hardware could not place.
 int device_wg_capacity(const void* kernel) {
   static std::mutex mu;
   static std::map<std::pair<int, const void*>, int> cache;
@@ -354,39 +506,50 @@ int device_wg_capacity(const void* kernel) {
   int cus = 0, per = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, kThreads, 0) != hipSuccess) return -1;
+  hipFuncAttributes attr{};
+  if (hipFuncGetAttributes(&attr, kernel) != hipSuccess) return -1;
+  static_assert(kThreads == 4 * kWave, "one wave per SIMD per workgroup");
+  const int vgprs = ((attr.numRegs > 0 ? attr.numRegs : 1) + 7) / 8 * 8;
+  const int by_regs = std::min(8, 512 / vgprs);
+  const int by_lds = attr.sharedSizeBytes > 0 ? kLdsBytesPerCU / (int)attr.sharedSizeBytes : 8;
+  per = std::min(per, std::min(by_regs, by_lds));
+  if (getenv("DSPARK_VERBOSE"))
+    fprintf(stderr, "[dspark] accept_rate: %d VGPRs, %zu B LDS -> %d workgroups per CU\n",
+            attr.numRegs, (size_t)attr.sharedSizeBytes, per);
   cache[{dev, kernel}] = cus * per;
   return cus * per;
 }
 
-Plan make_plan(int64_t rows, int V, int dtype, int capacity) {
-  Plan p{};
+// Cluster geometry: G workgroups per row, each holding kChunkVec vectors of
+// each tensor (the last one fewer).  Zero G means the row-wise fallback.
+struct Geometry {
+  int vec_per_row, G;
+};
+Geometry geometry(int V, int dtype) {
   const int epv = dtype == DSPARK_BF16 ? 8 : 4;
-  p.vec = (V % epv) == 0;
-  if (!p.vec) return p;
-  p.vec_per_row = V / epv;
-  p.G = (p.vec_per_row + kThreads * kMaxVec - 1) / (kThreads * kMaxVec);
-  p.vec_per_wg = (p.vec_per_row + p.G - 1) / p.G;
-  int64_t cl = capacity > 0 ? capacity / p.G : 1;
-  if (cl > rows) cl = rows;
-  if (cl < 1) cl = 1;
-  p.nclusters = (int)cl;
-  return p;
+  if (V % epv != 0) return {0, 0};
+  const int vpr = V / epv;
+  const int G = (vpr + kChunkVec - 1) / kChunkVec;
+  return {vpr, G <= kMaxG ? G : 0};
+}
+// Device-independent bound on resident clusters, for the workspace size:
+// at most 16 workgroups per compute unit on 256 compute units.
+int64_t max_clusters(int64_t rows, int G) {
+  int64_t cl = (256 * 16) / G;
+  return cl < rows ? cl : rows;
 }
 
 }  // namespace
 
 extern "C" size_t dspark_accept_rate_workspace_bytes(int B, int A, int gamma, int V, int dtype) {
+  using dspark_host::align_up;
   if (B < 0 || A < 0 || gamma < 0 || V < 0) return 0;
-  // Upper bound independent of the device: one cluster per row at most and
-  // at most 16 workgroups per compute unit on 256 compute units.
   const int64_t rows = (int64_t)B * A * gamma;
-  const int epv = dtype == DSPARK_BF16 ? 8 : 4;
-  const int64_t vpr = V / epv > 0 ? V / epv : 1;
-  const int64_t G = (vpr + kThreads * kMaxVec - 1) / (kThreads * kMaxVec);
-  int64_t cl = (256 * 16) / (G > 0 ? G : 1);
-  if (cl > rows) cl = rows;
-  if (cl < 1) cl = 1;
-  return (size_t)(cl * 16 * G * sizeof(uint64_t) + 64);
+  const Geometry geo = geometry(V, dtype);
+  if (geo.G == 0 || rows == 0) return 0;
+  const size_t shares = align_up((size_t)rows * geo.G * sizeof(float), 256);
+  const size_t slots = (size_t)max_clusters(rows, geo.G) * 2 * geo.G * sizeof(u32x4);
+  return shares + slots + 64;
 }
 
 extern "C" int dspark_accept_rate(const void* draft_logits, const void* target_logits,
@@ -410,48 +573,53 @@ extern "C" int dspark_accept_rate(const void* draft_logits, const void* target_l
   hipStream_t s = (hipStream_t)stream;
   const bool bf = dtype == DSPARK_BF16;
   const bool aligned = ((uintptr_t)draft_logits % 16 == 0) && ((uintptr_t)target_logits % 16 == 0);
+  const Geometry geo = geometry(V, dtype);
   const void* kern = bf ? (const void*)tv_cluster_kernel<true> : (const void*)tv_cluster_kernel<false>;
-  const int cap = device_wg_capacity(kern);
-  if (cap <= 0) return fail(DSPARK_ERR_HIP, "accept_rate: occupancy query failed");
-  Plan p = make_plan(rows, V, dtype, cap);
-  if (p.vec && aligned) {
-    // the workspace bound assumes at most 16 workgroups per CU on 256 CUs
-    const int64_t max_cl = (256 * 16) / p.G;
-    if (p.nclusters > max_cl) p.nclusters = (int)max_cl;
-    uint64_t* slots = (uint64_t*)ws;
-    const int64_t nslot = (int64_t)p.nclusters * 16 * p.G;
+  int64_t ncl = 0;
+  if (geo.G > 0 && aligned) {
+    const int cap = device_wg_capacity(kern);
+    if (cap <= 0) return fail(DSPARK_ERR_HIP, "accept_rate: occupancy query failed");
+    ncl = cap / geo.G;
+    const int64_t bound = max_clusters(rows, geo.G);
+    if (ncl > bound) ncl = bound;
+  }
+  const int64_t nb = (int64_t)B * A;
+  if (ncl >= 1) {
+    float* share = (float*)ws;
+    u32x4* slots = (u32x4*)((char*)ws + align_up((size_t)rows * geo.G * sizeof(float), 256));
+    const int64_t nslot = ncl * 2 * geo.G;
     int32_t* err = (int32_t*)(slots + nslot);  // one spare word after the slots
     // slots (epoch 0 = empty) and the error word start at zero: a fill
     // kernel, not a memset node, so the sequence stays safe under graph capture
-    const int64_t nwords = nslot * 2 + 1;
+    const int64_t nwords = nslot * 4 + 1;
     hipLaunchKernelGGL(zero_u32_kernel, dim3((unsigned)((nwords + 255) / 256)), dim3(256), 0, s,
-                       (unsigned*)ws, (int)nwords);
-    const u32x4* dp = (const u32x4*)draft_logits;
-    const u32x4* tp = (const u32x4*)target_logits;
+                       (unsigned*)slots, (int)nwords);
+    const char* dp = (const char*)draft_logits;
+    const char* tp = (const char*)target_logits;
     int64_t rows_arg = rows;
-    int vpr = p.vec_per_row, vpw = p.vec_per_wg, G = p.G, ncl = p.nclusters;
-    void* args[] = {(void*)&dp, (void*)&tp, (void*)&accept, (void*)&rows_arg, (void*)&vpr,
-                    (void*)&vpw, (void*)&G, (void*)&ncl, (void*)&slots, (void*)&err};
+    int Varg = V, vpr = geo.vec_per_row, G = geo.G, ncl_arg = (int)ncl;
+    void* args[] = {(void*)&dp, (void*)&tp, (void*)&share, (void*)&rows_arg, (void*)&Varg,
+                    (void*)&vpr, (void*)&G, (void*)&ncl_arg, (void*)&slots, (void*)&err};
     if (getenv("DSPARK_VERBOSE"))
-      fprintf(stderr, "[dspark] accept_rate: capacity %d WGs (%d CUs), G=%d, clusters=%d, vec/row=%d\n",
-              cap, device_cus(), p.G, p.nclusters, p.vec_per_row);
-    hipError_t e = hipLaunchCooperativeKernel(kern, dim3((unsigned)(p.nclusters * p.G)),
-                                              dim3(kThreads), args, 0, s);
+      fprintf(stderr, "[dspark] accept_rate: %d CUs, G=%d, clusters=%lld, vec/row=%d\n",
+              device_cus(), G, (long long)ncl, vpr);
+    hipError_t e = hipLaunchCooperativeKernel(kern, dim3((unsigned)(ncl * G)), dim3(kThreads),
+                                              args, 0, s);
     if (e != hipSuccess)
       return fail(DSPARK_ERR_HIP, "accept_rate: cooperative launch: %s", hipGetErrorString(e));
+    hipLaunchKernelGGL(tv_finalize_kernel, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, s,
+                       (const float*)share, G, accept, eval_mask, tau, nb, gamma);
   } else {
     int64_t grid = rows < 65536 ? rows : 65536;
     if (bf)
-      hipLaunchKernelGGL(tv_rowwise_kernel<true>, dim3((unsigned)grid), dim3(kThreads), 0, s,
+      hipLaunchKernelGGL(tv_rowwise_kernel<true>, dim3((unsigned)grid), dim3(kRowThreads), 0, s,
                          draft_logits, target_logits, accept, rows, V);
     else
-      hipLaunchKernelGGL(tv_rowwise_kernel<false>, dim3((unsigned)grid), dim3(kThreads), 0, s,
+      hipLaunchKernelGGL(tv_rowwise_kernel<false>, dim3((unsigned)grid), dim3(kRowThreads), 0, s,
                          draft_logits, target_logits, accept, rows, V);
-  }
-  if (tau) {
-    const int64_t nb = (int64_t)B * A;
-    hipLaunchKernelGGL(tau_kernel, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, s, accept,
-                       eval_mask, tau, nb, gamma);
+    if (tau)
+      hipLaunchKernelGGL(tau_kernel, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, s, accept,
+                         eval_mask, tau, nb, gamma);
   }
   return check_launch("accept_rate");
 }

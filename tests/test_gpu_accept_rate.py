@@ -106,3 +106,24 @@ def test_config4_full_size_sampled(dsp):
         assert abs(tau_h[b, a] - OR.tau(ref, em_h[b, a])) < 1e-4
     del inp
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_masked_vocabulary(dsp, dtype):
+    """-inf logits (a padded or masked vocabulary): random 10% of entries, and
+    in some rows a whole leading stretch of 8192 entries, so that a
+    workgroup's slice holds nothing but -inf; the oracle's softmax gives those
+    entries probability 0."""
+    V = 151936 if dtype == "bf16" else 40000
+    d, t = _pair(17, (2, 2, 4, V), dtype)
+    rng = np.random.default_rng(18)
+    ninf = W.to_bf16_bits(np.array([-np.inf], np.float32))[0] if dtype == "bf16" else np.float32(-np.inf)
+    for x in (d, t):
+        x[rng.random(x.shape) < 0.1] = ninf
+    d[0, 0, :, :8192] = ninf
+    t[1, 1, 1:3, :8192] = ninf
+    acc, _ = dsp.accept_rate(as_dtype(d, dtype), as_dtype(t, dtype))
+    ref = OR.accept_rate(W.values(d, dtype), W.values(t, dtype))
+    assert np.isfinite(ref).all()
+    err = np.abs(acc.cpu().numpy() - ref).max()
+    assert err < 2e-5, err
