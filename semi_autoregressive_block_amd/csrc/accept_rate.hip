@@ -344,7 +344,6 @@ __global__ __launch_bounds__(kThreads) void tv_cluster_kernel(
         }
       };
       __syncthreads();  // A
-      if (k >= 2) store_share(k - 2);
       while (!__all(got[0] && got[1])) {
         poll();
         if (!__all(got[0] && got[1])) __builtin_amdgcn_s_sleep(1);
@@ -376,6 +375,8 @@ __global__ __launch_bounds__(kThreads) void tv_cluster_kernel(
           glob[par][1] = poisoned ? NAN : sT.a - (MT + __builtin_amdgcn_logf(ST));
         }
       }
+      // after the polls, so that their wait never includes this store
+      if (k >= 2) store_share(k - 2);
       __syncthreads();  // B
       if (k < nk && lane == 0) {
         const int pk = (int)(k & 1);

@@ -9,7 +9,7 @@ import pytest
 import torch
 
 import workloads as W
-from gpu_util import as_dtype, dev, host_bits
+from gpu_util import DEV, as_dtype, dev, host_bits
 from oracle import accept_rate as OR
 
 pytestmark = pytest.mark.gpu
@@ -127,3 +127,25 @@ def test_masked_vocabulary(dsp, dtype):
     assert np.isfinite(ref).all()
     err = np.abs(acc.cpu().numpy() - ref).max()
     assert err < 2e-5, err
+
+
+def test_long_clusters_bf16(dsp):
+    """4096 rows of V = 151936: every cluster of workgroups walks through
+    more than a hundred rows, long enough for its members to drift apart by
+    the full depth of the exchange pipeline; sampled rows against the oracle
+    and every row finite and in range."""
+    R, V = 4096, 151936
+    g = W._gen(torch, DEV, 20)
+    db = W.device_normal(torch, g, (R, V), 3.0, torch.bfloat16, DEV)
+    sigma = torch.rand((R, 1), generator=g, device=DEV) * 2.9 + 0.1
+    noise = W.device_normal(torch, g, (R, V), 1.0, torch.float32, DEV)
+    tb = (db.float() + noise * sigma).to(torch.bfloat16)
+    del noise
+    acc, _ = dsp.accept_rate(db.view(1, R // 8, 8, V), tb.view(1, R // 8, 8, V))
+    acc_h = acc.cpu().numpy().reshape(R)
+    assert np.all(np.isfinite(acc_h)) and np.all((acc_h >= 0) & (acc_h <= 1))
+    rng = np.random.default_rng(19)
+    for r in list(rng.choice(R, size=24, replace=False)) + [0, R - 1]:
+        dv = W.bf16_to_f32(host_bits(db[r]))
+        tv = W.bf16_to_f32(host_bits(tb[r]))
+        assert abs(acc_h[r] - OR.accept_rate(dv, tv)) < 2e-5, r
