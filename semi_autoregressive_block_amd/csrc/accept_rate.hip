@@ -59,15 +59,6 @@ __device__ __forceinline__ float vmin(float a, float b) { return __builtin_eleme
 // ---- wave reductions: DPP inside each row of 16 lanes, then the four row
 // results through scalar registers.  Every lane returns the same value, and
 // the combination order is fixed, so equal inputs give equal bits anywhere.
-template <int kCtrl>
-__device__ __forceinline__ float dpp(float v) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), kCtrl, 0xF, 0xF, false));
-}
-constexpr int kDppQuadSwap1 = 0xB1;   // quad_perm [1,0,3,2]
-constexpr int kDppQuadSwap2 = 0x4E;   // quad_perm [2,3,0,1]
-constexpr int kDppRowMirror = 0x140;
-constexpr int kDppHalfMirror = 0x141;
-
 __device__ __forceinline__ float lane_value(float v, int l) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
 }
@@ -75,17 +66,17 @@ __device__ __forceinline__ float uniform(float v) {
   return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));
 }
 __device__ __forceinline__ float wave_max(float v) {
-  v = vmax(v, dpp<kDppQuadSwap1>(v));
-  v = vmax(v, dpp<kDppQuadSwap2>(v));
-  v = vmax(v, dpp<kDppHalfMirror>(v));
-  v = vmax(v, dpp<kDppRowMirror>(v));
+  v = vmax(v, dpp_f32<kDppQuadSwap1>(v));
+  v = vmax(v, dpp_f32<kDppQuadSwap2>(v));
+  v = vmax(v, dpp_f32<kDppHalfMirror>(v));
+  v = vmax(v, dpp_f32<kDppRowMirror>(v));
   return vmax(vmax(lane_value(v, 0), lane_value(v, 16)), vmax(lane_value(v, 32), lane_value(v, 48)));
 }
 __device__ __forceinline__ float wave_sum(float v) {
-  v += dpp<kDppQuadSwap1>(v);
-  v += dpp<kDppQuadSwap2>(v);
-  v += dpp<kDppHalfMirror>(v);
-  v += dpp<kDppRowMirror>(v);
+  v += dpp_f32<kDppQuadSwap1>(v);
+  v += dpp_f32<kDppQuadSwap2>(v);
+  v += dpp_f32<kDppHalfMirror>(v);
+  v += dpp_f32<kDppRowMirror>(v);
   return (lane_value(v, 0) + lane_value(v, 16)) + (lane_value(v, 32) + lane_value(v, 48));
 }
 

@@ -67,6 +67,16 @@ __device__ __forceinline__ uint32_t argmax_key_index(uint64_t k) {
   return 0xffffffffu - (uint32_t)(k & 0xffffffffu);
 }
 
+// DPP lane moves inside rows of 16 lanes (gfx9 encodings).
+constexpr int kDppQuadSwap1 = 0xB1;   // quad_perm [1,0,3,2]: lane ^ 1
+constexpr int kDppQuadSwap2 = 0x4E;   // quad_perm [2,3,0,1]: lane ^ 2
+constexpr int kDppRowMirror = 0x140;  // lane 15 - l inside each row
+constexpr int kDppHalfMirror = 0x141; // lane 7 - l inside each half row
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), kCtrl, 0xF, 0xF, false));
+}
+
 __device__ __forceinline__ void status_or(int32_t* st, int32_t bits) {
   if (st) atomicOr(st, bits);
 }
