@@ -10,14 +10,17 @@ per request anchored at the end of its context, gamma = 16, 32 query / 8 KV
 heads, head dim 128, V = 151936, Markov rank 256, greedy; bf16 inputs,
 float32 accumulation.  The TV accept rate (with tau), which needs target
 logits and so is not part of a serving round, is timed beside it on the
-4 x 512 x 8-row training-shaped workload and reported under "accept_rate".
+4 x 512 x 8-row training-shaped workload and reported under "accept_rate";
+the training-shaped all-anchor attention (1 x 4096 context, 512 anchors,
+gamma = 8; MFMA-bound) is timed too and reported under "attention_training"
+against the bf16 matrix-core peak.
 
 Prints ONE JSON line: metric, value (drafted tokens/s), ms_per_step, the
 per-operation breakdown, the roofline of the dominant kernel (achieved
 algorithmic GB/s from HIP events on the launch stream vs the 8 TB/s HBM
 peak) and the CPU oracle timed on a bounded sample of the same workload.
 
---only {round,attention,markov,accept,copy} restricts the run to one part
+--only {round,attention,markov,accept,train_attention,copy} restricts the run to one part
 (for profiler runs); --no-cpu skips the CPU baseline.
 """
 
@@ -42,7 +45,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", choices=["round", "attention", "markov", "accept", "copy"], default=None)
+    ap.add_argument("--only", choices=["round", "attention", "markov", "accept", "train_attention", "copy"],
+                    default=None)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     return ap.parse_args()
@@ -228,6 +232,29 @@ def main():
         del inp, bufs
         torch.cuda.empty_cache()
 
+    if args.only in (None, "train_attention"):
+        # training-shaped all-anchor attention: 472 kept blocks of 8 rows
+        # over one 4096-token context, 32 query / 8 KV heads, D = 128
+        t2 = W.config2_device(torch, dev)
+        c2 = W.CONFIG2
+        out2 = torch.empty_like(t2["q"])
+        ws2 = torch.empty(max(1, dsp.block_attention_workspace_bytes(1, c2["A"], c2["gamma"], c2["Hq"], c2["Hkv"],
+                                                                     c2["D"], c2["S"])),
+                          dtype=torch.uint8, device=dev)
+        f_t2 = lambda: dsp.block_attention(t2["q"], t2["k_ctx"], t2["v_ctx"], t2["ctx_offsets"], t2["k_blk"],
+                                           t2["v_blk"], t2["anchor"], t2["keep"], max_ctx=t2["max_ctx"],
+                                           out=out2, workspace=ws2)
+        t2_ms = timed(torch, f_t2, K, Wm)
+        a2, k2 = t2["anchor_host"], t2["keep_host"]
+        # QK^T and PV over the visible pairs only
+        t2_flops = 4.0 * c2["gamma"] * c2["D"] * c2["Hq"] * float(((a2 + c2["gamma"]) * (k2 != 0)).sum())
+        if args.only == "train_attention":
+            print(json.dumps({"train_attention_ms": t2_ms, "TFLOPs": t2_flops / t2_ms / 1e9}))
+            return
+        result["train_attention"] = dict(ms=t2_ms, flops=t2_flops)
+        del t2, out2, ws2
+        torch.cuda.empty_cache()
+
     if args.only in (None, "accept"):
         a4 = W.config4_device(torch, dev)
         m = a4["mask"]
@@ -289,6 +316,13 @@ def main():
         line["accept_rate"] = {"workload": "4 x 512 x 8 rows, V=151936 bf16, with tau",
                                "ms": a["ms"], "GBps": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
                                "rows_per_s": 16384 / (a["ms"] / 1e3)}
+    if "train_attention" in result:
+        a = result["train_attention"]
+        tf = a["flops"] / a["ms"] / 1e9
+        line["attention_training"] = {"workload": "1 x 4096 context, 512 anchors (472 kept), gamma=8, "
+                                                  "Hq=32/Hkv=8, D=128, bf16",
+                                      "ms": a["ms"], "TFLOPs": tf, "mfma_frac": tf / MFMA_BF16_PEAK_TFLOPS,
+                                      "algorithmic_flops": a["flops"]}
     if "cpu" in result:
         line["cpu_baseline"] = result["cpu"]
     print(json.dumps(line))

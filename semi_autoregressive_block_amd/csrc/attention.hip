@@ -142,6 +142,12 @@ __device__ __forceinline__ void fetch_slab(const Params& p, const Item& it, int 
     }
 }
 
+// The running maximum of a row is only moved when a slab's maximum exceeds
+// it by more than this many powers of two: the exponentials then stay below
+// 2^kLazyMax (exact in float32, and in bf16 as precise as any probability),
+// and most slabs skip the rescale of the accumulators entirely.
+constexpr float kLazyMax = 8.f;
+
 // Online-softmax update of this lane's row with one slab.
 template <int D>
 __device__ __forceinline__ void compute_slab(const Params& p, const Item& it, int s, const Slab<D>& sl,
@@ -156,41 +162,52 @@ __device__ __forceinline__ void compute_slab(const Params& p, const Item& it, in
   for (int i = 0; i < 16; ++i) sc[i] = 0.f;
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk) sc = mfma32x32x16(sl.kf[kk], qf[kk], sc);
-  float smax = -INFINITY;
+  // context slabs that every row of the wave sees whole need no masking
+  const bool whole = !own && kept && j0 + 32 <= min(it.cend, lim);
+  if (!__all(whole)) {
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int ks = 8 * (i / 4) + 4 * it.h + (i & 3);
-    bool vis;
-    if (!own) {
-      const int j = j0 + ks;
-      vis = kept && j < it.cend && j < lim;
-    } else {
-      const int o_i = os + ks;
-      vis = kept && o_i < it.n_own && (a_lo + o_i / p.gamma) == ua;
+    for (int i = 0; i < 16; ++i) {
+      const int ks = 8 * (i / 4) + 4 * it.h + (i & 3);
+      bool vis;
+      if (!own) {
+        const int j = j0 + ks;
+        vis = kept && j < it.cend && j < lim;
+      } else {
+        const int o_i = os + ks;
+        vis = kept && o_i < it.n_own && (a_lo + o_i / p.gamma) == ua;
+      }
+      sc[i] = vis ? sc[i] : -INFINITY;
     }
-    sc[i] = vis ? sc[i] : -INFINITY;
-    smax = fmaxf(smax, sc[i]);
   }
+  float smax = sc[0];
+#pragma unroll
+  for (int i = 1; i < 16; ++i) smax = fmaxf(smax, sc[i]);
   smax = fmaxf(smax, __shfl_xor(smax, 32, kWave));
-  const float mnew = fmaxf(m, smax);
-  const float muse = mnew == -INFINITY ? 0.f : mnew;
-  const float alpha = __builtin_amdgcn_exp2f((m - muse) * c);
+  // lazy maximum: move it (and rescale) only when this slab would push the
+  // exponentials past 2^kLazyMax
+  const bool grow = smax > m && (m == -INFINITY || (smax - m) * c > kLazyMax);
+  if (__any(grow)) {
+    const float mnew = grow ? smax : m;
+    const float alpha = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m - mnew) * c);
+    l *= alpha;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[j][r] *= alpha;
+    m = mnew;
+  }
+  const float mc = m == -INFINITY ? 0.f : m * c;
   float psum = 0.f;
   u32x4 pb[2];
 #pragma unroll
   for (int i = 0; i < 16; i += 2) {
-    const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[i], c, -muse * c));
-    const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[i + 1], c, -muse * c));
+    const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[i], c, -mc));
+    const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[i + 1], c, -mc));
     psum += p0 + p1;
-    pb[i / 8][(i % 8) / 2] = f32_to_bf16(p0) | (f32_to_bf16(p1) << 16);
+    pb[i / 8][(i % 8) / 2] = pack_bf16x2(p0, p1);
   }
   psum += __shfl_xor(psum, 32, kWave);
-  l = l * alpha + psum;
-  m = mnew;
-#pragma unroll
-  for (int j = 0; j < NJ; ++j)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) o[j][r] *= alpha;
+  l += psum;
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
 #pragma unroll
@@ -386,7 +403,7 @@ __global__ __launch_bounds__(kThreads) void block_attn_mfma(Params p) {
     for (int e = 0; e < 4 * NJ; e += 2) {
       const int r0 = 4 * qd + e / NJ, j0 = e % NJ;
       const int r1 = 4 * qd + (e + 1) / NJ, j1 = (e + 1) % NJ;
-      w[e / 2] = f32_to_bf16(o[j0][r0] * inv) | (f32_to_bf16(o[j1][r1] * inv) << 16);
+      w[e / 2] = pack_bf16x2(o[j0][r0] * inv, o[j1][r1] * inv);
     }
     uint16_t* dst = orow + NJ * (8 * qd + 4 * h);
     *(u32x4*)dst = u32x4{w[0], w[1], w[2], w[3]};
