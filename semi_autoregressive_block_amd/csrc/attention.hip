@@ -94,6 +94,8 @@ template <int D>
 struct Slab {
   u32x4 kf[D / 16];
   uint32_t v[2][8][D / 64];
+  __device__ u32x4 k(int kk) const { return kf[kk]; }
+  __device__ uint32_t vp(int t, int s8, int j2) const { return v[t][s8][j2]; }
 };
 
 // Per-workgroup constants of a work item.
@@ -107,41 +109,6 @@ struct Item {
   int kvh, h, r32;
 };
 
-template <int D>
-__device__ __forceinline__ void fetch_slab(const Params& p, const Item& it, int s, Slab<D>& sl) {
-  constexpr int KK = D / 16, NJ = D / 32;
-  const bool own = s >= it.n_ctx_slabs;
-  const uint16_t* kbase = own ? p.kb : p.kc;
-  const uint16_t* vbase = own ? p.vb : p.vc;
-  int64_t krow;
-  int j0 = 0, os = 0;
-  if (!own) {
-    j0 = it.cbeg + s * 32;
-    krow = it.c0 + min(j0 + it.r32, it.S - 1);
-  } else {
-    os = (s - it.n_ctx_slabs) * 32;
-    krow = it.own0 + min(os + it.r32, it.n_own - 1);
-  }
-  const uint16_t* kp = kbase + (krow * p.Hkv + it.kvh) * D + it.h * 8;
-#pragma unroll
-  for (int kk = 0; kk < KK; ++kk) sl.kf[kk] = *(const u32x4*)(kp + kk * 16);
-#pragma unroll
-  for (int t = 0; t < 2; ++t)
-#pragma unroll
-    for (int s8 = 0; s8 < 8; ++s8) {
-      const int ks = 8 * (2 * t + s8 / 4) + 4 * it.h + (s8 & 3);
-      const int64_t vrow = own ? it.own0 + min(os + ks, it.n_own - 1) : it.c0 + min(j0 + ks, it.S - 1);
-      const uint16_t* vp = vbase + (vrow * p.Hkv + it.kvh) * D + NJ * it.r32;
-      if constexpr (NJ == 4) {
-        const u32x2 w = *(const u32x2*)vp;
-        sl.v[t][s8][0] = w.x;
-        sl.v[t][s8][1] = w.y;
-      } else {
-        sl.v[t][s8][0] = *(const uint32_t*)vp;
-      }
-    }
-}
-
 // The running maximum of a row is only moved when a slab's maximum exceeds
 // it by more than this many powers of two: the exponentials then stay below
 // 2^kLazyMax (exact in float32, and in bf16 as precise as any probability),
@@ -149,8 +116,8 @@ __device__ __forceinline__ void fetch_slab(const Params& p, const Item& it, int 
 constexpr float kLazyMax = 8.f;
 
 // Online-softmax update of this lane's row with one slab.
-template <int D>
-__device__ __forceinline__ void compute_slab(const Params& p, const Item& it, int s, const Slab<D>& sl,
+template <int D, class Src>
+__device__ __forceinline__ void compute_slab(const Params& p, const Item& it, int s, const Src& sl,
                                              const u32x4* qf, bool kept, int lim, int ua, int a_lo,
                                              float c, float& m, float& l, f32x16* o) {
   constexpr int KK = D / 16, NJ = D / 32;
@@ -161,22 +128,23 @@ __device__ __forceinline__ void compute_slab(const Params& p, const Item& it, in
 #pragma unroll
   for (int i = 0; i < 16; ++i) sc[i] = 0.f;
 #pragma unroll
-  for (int kk = 0; kk < KK; ++kk) sc = mfma32x32x16(sl.kf[kk], qf[kk], sc);
-  // context slabs that every row of the wave sees whole need no masking
-  const bool whole = !own && kept && j0 + 32 <= min(it.cend, lim);
-  if (!__all(whole)) {
+  for (int kk = 0; kk < KK; ++kk) sc = mfma32x32x16(sl.k(kk), qf[kk], sc);
+  // visible keys of this lane's row in this slab: context keys below
+  // min(chunk end, anchor), own keys of its block only (one gamma range)
+  int vlo, vhi;
+  if (!own) {
+    vlo = -1 - j0;
+    vhi = kept ? min(it.cend, lim) - j0 : 0;
+  } else {
+    vlo = (ua - a_lo) * p.gamma - os;
+    vhi = kept ? vlo + p.gamma : vlo;
+  }
+  // slabs that every row of the wave sees whole need no masking
+  if (!__all(vlo <= 0 && vhi >= 32)) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int ks = 8 * (i / 4) + 4 * it.h + (i & 3);
-      bool vis;
-      if (!own) {
-        const int j = j0 + ks;
-        vis = kept && j < it.cend && j < lim;
-      } else {
-        const int o_i = os + ks;
-        vis = kept && o_i < it.n_own && (a_lo + o_i / p.gamma) == ua;
-      }
-      sc[i] = vis ? sc[i] : -INFINITY;
+      sc[i] = (ks >= vlo && ks < vhi) ? sc[i] : -INFINITY;
     }
   }
   float smax = sc[0];
@@ -215,7 +183,7 @@ __device__ __forceinline__ void compute_slab(const Params& p, const Item& it, in
       u32x4 va;
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        const uint32_t lo = sl.v[t][2 * w][j / 2], hi = sl.v[t][2 * w + 1][j / 2];
+        const uint32_t lo = sl.vp(t, 2 * w, j / 2), hi = sl.vp(t, 2 * w + 1, j / 2);
         va[w] = (j & 1) ? pack_hi(lo, hi) : pack_lo(lo, hi);
       }
       o[j] = mfma32x32x16(va, pb[t], o[j]);
@@ -295,31 +263,148 @@ __global__ __launch_bounds__(1024) void attn_plan_kernel(Params p, int32_t* __re
   }
 }
 
+// ------------------------------------------------------------ MFMA kernel
+// K and V reach the waves through LDS: the workgroup's four waves load each
+// pair of 32-key slabs (one per key parity) together, as 16-byte pieces,
+// into a two-slot ring, so a slab is fetched once per workgroup and read by
+// both row groups.  Loads in flight live in 32-register sets, which keeps a
+// wave within 256 registers: two workgroups share a compute unit and each
+// SIMD interleaves two waves' matrix-core and softmax work.  K rows are
+// stored with their 16-byte pieces XOR-swizzled by the key index, so the
+// MFMA-operand reads (one piece of 32 different keys) hit distinct LDS
+// banks; V rows are stored plainly (its reads are 32 consecutive pieces of
+// one key row).
 template <int D>
-__global__ __launch_bounds__(kThreads) void block_attn_mfma(Params p) {
-  constexpr int NJ = D / 32;  // head-dim groups of the PV product
-  constexpr int KK = D / 16;  // k-steps of the QK product
-  __shared__ float mrg[2][D + 2][32];
+struct Ring {
+  static constexpr int kPieces = D * 2 / 16;             // 16-byte pieces per key row
+  static constexpr int kTensorBytes = 32 * D * 2;        // one tensor of one slab
+  static constexpr int kSlabBytes = 2 * kTensorBytes;    // K then V
+  static constexpr int kPairBytes = 2 * kSlabBytes;      // parity-0 slab then parity-1 slab
+  static constexpr int kBytes = 2 * kPairBytes;          // two slots
+  static constexpr int kChunksPerThread = kPairBytes / 16 / kThreads;  // 16-byte pieces a thread moves per pair
+};
 
-  // ---- decode the work item (tile id = (tile * B + b) * Hkv + kvh)
-  int wid = p.order ? p.order[blockIdx.x] : (int)blockIdx.x;
+// Moves pairs of slabs from HBM/L2 through registers into the LDS ring.
+// Piece c = threadIdx.x + kThreads*j of a pair is 16 bytes of tensor
+// T = c / (32P) (slab T/2, K for even T, V for odd) of key (c mod 32P) / P,
+// head dims 8*(c mod P) .. +7 (P pieces per key row).  Since kThreads is a
+// multiple of P, a thread keeps one piece index and one key offset for all
+// j and the rest is a compile-time constant per j: LDS stores take
+// immediate offsets and a load is a wave-uniform slab base plus one 32-bit
+// lane offset.  Keys past a source's last row are read from that last row
+// (they are masked in the scores).
+template <int D>
+struct Stager {
+  using Rg = Ring<D>;
+  static constexpr int P = Rg::kPieces;
+  static constexpr int N = Rg::kChunksPerThread;
+  static_assert(kThreads % P == 0 && ((kThreads / P) % P == 0 || kThreads / P >= 32), "piece layout");
+  // per-thread constants
+  int key_t;           // key of piece j = 0
+  uint32_t piece_b;    // byte offset of the piece inside a key row
+  uint32_t lds_k, lds_v;  // LDS byte offset of piece j = 0 in a K / V tensor
+  // wave-uniform
+  const unsigned char *kc, *vc, *kb, *vb;
+  int64_t ctx_row0, own_row0;  // first row of the context chunk / of the tile's own keys
+  int ctx_keys, own_keys, n_ctx_slabs, nslab;
+  uint32_t row_b;              // bytes between consecutive rows (all heads)
+  uint32_t head_b;             // byte offset of this KV head inside a row
+
+  static constexpr int tensor_of(int j) { return (kThreads * j) / (32 * P); }
+  static constexpr int keyoff_of(int j) { return ((kThreads * j) % (32 * P)) / P; }
+
+  __device__ void load(int pair, u32x4 (&R)[N]) const {
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      const int T = tensor_of(j);
+      // an odd last pair repeats a slab (not computed)
+      const int s = min(2 * pair + T / 2, nslab - 1);
+      const bool own = s >= n_ctx_slabs;
+      const int k0 = own ? (s - n_ctx_slabs) * 32 : s * 32;
+      const int nvalid = (own ? own_keys : ctx_keys) - k0;
+      const unsigned char* src = (T & 1) ? (own ? vb : vc) : (own ? kb : kc);
+      src += ((own ? own_row0 : ctx_row0) + k0) * (int64_t)row_b + head_b;
+      const uint32_t off = (uint32_t)min(key_t + keyoff_of(j), nvalid - 1) * row_b + piece_b;
+      R[j] = *(const u32x4*)(src + off);
+    }
+  }
+
+  __device__ void store(unsigned char* slot, const u32x4 (&R)[N]) const {
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      const int T = tensor_of(j);
+      const uint32_t off = T * Rg::kTensorBytes + keyoff_of(j) * P * 16;
+      *(u32x4*)(slot + ((T & 1) ? lds_v : lds_k) + off) = R[j];
+    }
+  }
+};
+
+// This lane's operand pieces of one staged slab, all read from LDS into
+// registers before the products start.  K piece kk (key r32, head dims
+// 16*kk + 8h .. +7) sits at chunk r32*P + ((2kk + h) ^ (r32 mod P)) =
+// r32*P + (2kk ^ y) with y = h ^ (r32 mod P); V word (key ks, head dims
+// NJ*r32 + 2*j2 .. +1) at a lane constant plus an immediate.
+template <int D>
+struct SlabView {
+  static constexpr int P = Ring<D>::kPieces;
+  const unsigned char* sp;  // slab start in the ring
+  uint32_t kbase, kx, vbase;
+  __device__ SlabView(const unsigned char* slab, int h, int r32)
+      : sp(slab), kbase(r32 * P * 16), kx((h ^ (r32 % P)) * 16), vbase(4 * h * D * 2 + (D / 32) * 2 * r32) {}
+  __device__ u32x4 k(int kk) const { return *(const u32x4*)(sp + kbase + ((32 * kk) ^ kx)); }
+  __device__ uint32_t vp(int t, int s8, int j2) const {
+    const int ks = 8 * (2 * t + s8 / 4) + (s8 & 3);  // key minus 4h
+    return *(const uint32_t*)(sp + Ring<D>::kTensorBytes + vbase + ks * (D * 2) + 4 * j2);
+  }
+};
+
+template <int D>
+__device__ __forceinline__ void slab_from_lds(const SlabView<D>& v, Slab<D>& sl) {
+  constexpr int KK = D / 16, NJ = D / 32;
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) sl.kf[kk] = v.k(kk);
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int s8 = 0; s8 < 8; ++s8)
+#pragma unroll
+      for (int j2 = 0; j2 < NJ / 2; ++j2) sl.v[t][s8][j2] = v.vp(t, s8, j2);
+}
+
+// Deep: two load sets in flight and operands read at their point of use, for
+// contexts streamed from HBM once (latency-bound); otherwise one load set and
+// whole-slab operand reads, for contexts that many tiles re-read from L2
+// (matrix-core-bound).
+template <int D, bool Deep>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void block_attn_mfma(Params p) {
+  using Rg = Ring<D>;
+  constexpr int NJ = D / 32;
+  constexpr int KK = D / 16;
+  __shared__ __align__(16) unsigned char ring[Rg::kBytes];
+
+  // the work item is the same for the whole workgroup: keep it in scalars
+  int wid = __builtin_amdgcn_readfirstlane(p.order ? p.order[blockIdx.x] : (int)blockIdx.x);
   const int kvh = wid % p.Hkv; wid /= p.Hkv;
   const int b = wid % p.B;
   const int tile = wid / p.B;
   int c0, S;
   ctx_range(p, b, c0, S, tile == 0 && kvh == 0 && threadIdx.x == 0);
+  c0 = __builtin_amdgcn_readfirstlane(c0);
+  S = __builtin_amdgcn_readfirstlane(S);
   int L, a_lo, a_hi;
   bool any_kept;
   tile_cost(p, b, tile, L, a_lo, a_hi, any_kept);
+  L = __builtin_amdgcn_readfirstlane(L);
+  a_lo = __builtin_amdgcn_readfirstlane(a_lo);
+  a_hi = __builtin_amdgcn_readfirstlane(a_hi);
+  any_kept = __builtin_amdgcn_readfirstlane((int)any_kept) != 0;
   const int rpb = p.group * p.gamma;
   const int u0 = tile * kTileRows;
 
   const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int rg = wave & 1, par = wave >> 1;
   const int h = lane >> 5, r32 = lane & 31;
-  // this lane's query row (rows past the row space are computed on a clamped
-  // row and not stored)
   const int u = u0 + rg * 32 + r32;
   const bool row_ok = u < p.nrows;
   const int uc = min(u, p.nrows - 1);
@@ -330,8 +415,6 @@ __global__ __launch_bounds__(kThreads) void block_attn_mfma(Params p) {
   const bool kept = row_ok && lim >= 0;
   if (!kept) lim = 0;
   const int64_t qrow = ((int64_t)b * p.A * p.gamma + (int64_t)ua * p.gamma + uk) * p.Hq + qh;
-
-  // Q^T operand pieces: d = 16*kk + 8*h .. +7
   u32x4 qf[KK];
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk) qf[kk] = *(const u32x4*)(p.q + qrow * D + kk * 16 + h * 8);
@@ -345,7 +428,29 @@ __global__ __launch_bounds__(kThreads) void block_attn_mfma(Params p) {
   it.n_own = (a_hi - a_lo + 1) * p.gamma;
   it.kvh = kvh; it.h = h; it.r32 = r32;
   const int nslab = any_kept ? it.n_ctx_slabs + (it.n_own + 31) / 32 : 0;
+  const int npairs = (nslab + 1) / 2;
   const float c = p.scale * kLog2e;
+
+  Stager<D> st;
+  {
+    constexpr int P = Rg::kPieces;
+    const int t = threadIdx.x;
+    st.key_t = t / P;
+    const int piece = t % P;
+    st.piece_b = piece * 16;
+    st.lds_k = (st.key_t * P + (piece ^ (st.key_t % P))) * 16;
+    st.lds_v = (st.key_t * P + piece) * 16;
+    st.kc = (const unsigned char*)p.kc; st.vc = (const unsigned char*)p.vc;
+    st.kb = (const unsigned char*)p.kb; st.vb = (const unsigned char*)p.vb;
+    st.ctx_row0 = (int64_t)c0 + it.cbeg;
+    st.own_row0 = it.own0;
+    st.ctx_keys = S - it.cbeg;  // rows past the context end repeat its last row
+    st.own_keys = it.n_own;
+    st.n_ctx_slabs = it.n_ctx_slabs;
+    st.nslab = nslab;
+    st.row_b = (uint32_t)p.Hkv * D * 2;
+    st.head_b = (uint32_t)kvh * D * 2;
+  }
 
   float m = -INFINITY, l = 0.f;
   f32x16 o[NJ];
@@ -354,33 +459,67 @@ __global__ __launch_bounds__(kThreads) void block_attn_mfma(Params p) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[j][r] = 0.f;
 
-  // ---- slab loop, software-pipelined: the wave's next slab is in flight
-  //      while the current one is computed (the prefetch index is clamped so
-  //      the loads are unconditional)
-  if (par < nslab) {
-    Slab<D> sa, sb;
-    fetch_slab<D>(p, it, par, sa);
-    for (int s = par; s < nslab; s += 4) {
-      fetch_slab<D>(p, it, min(s + 2, nslab - 1), sb);
-      compute_slab<D>(p, it, s, sa, qf, kept, lim, ua, a_lo, c, m, l, o);
-      if (s + 2 >= nslab) break;
-      fetch_slab<D>(p, it, min(s + 4, nslab - 1), sa);
-      compute_slab<D>(p, it, s + 2, sb, qf, kept, lim, ua, a_lo, c, m, l, o);
+  // ---- pair loop: pair i is computed from ring slot i & 1 while pair i + 1
+  //      goes from registers into the other slot and the next pairs are in
+  //      flight.  With two sets the loads are unconditional (past the end
+  //      they repeat the last slab, from L2), so the wait before each store
+  //      counts on exactly the younger set's loads being in flight; a step
+  //      past the end computes nothing.
+  auto step = [&](int i, int ahead, u32x4 (&Rs)[Rg::kChunksPerThread]) {
+    if (i + 1 < npairs) st.store(ring + ((i + 1) & 1) * Rg::kPairBytes, Rs);
+    if (Deep || i + ahead < npairs) st.load(i + ahead, Rs);
+    const int s = 2 * i + par;
+    const SlabView<D> view(ring + (i & 1) * Rg::kPairBytes + par * Rg::kSlabBytes, h, r32);
+    if (s < nslab) {
+      if constexpr (Deep) {
+        compute_slab<D>(p, it, s, view, qf, kept, lim, ua, a_lo, c, m, l, o);
+      } else {
+        Slab<D> sl;
+        slab_from_lds<D>(view, sl);
+        compute_slab<D>(p, it, s, sl, qf, kept, lim, ua, a_lo, c, m, l, o);
+      }
+    }
+    __syncthreads();
+  };
+  if (npairs > 0) {
+    if constexpr (Deep) {
+      // two sets, unrolled by two so each has fixed registers
+      u32x4 Ra[Rg::kChunksPerThread], Rb[Rg::kChunksPerThread];
+      st.load(0, Ra);
+      st.load(1, Rb);
+      st.store(ring, Ra);
+      st.load(2, Ra);
+      __syncthreads();
+      for (int i = 0; i < npairs; i += 2) {
+        step(i, 3, Rb);
+        step(i + 1, 3, Ra);
+      }
+    } else {
+      u32x4 R[Rg::kChunksPerThread];
+      st.load(0, R);
+      st.store(ring, R);
+      st.load(1, R);
+      __syncthreads();
+      for (int i = 0; i < npairs; ++i) step(i, 2, R);
     }
   }
 
-  // ---- merge the two key parities of each row group through LDS
+  // ---- merge the two key parities of each row group through LDS (the ring
+  //      is free after the loop's last barrier)
+  float* mrg = (float*)ring;  // [2 row groups][D + 2][32]
+  auto at = [&](int g, int d, int r) -> float& { return mrg[((size_t)g * (D + 2) + d) * 32 + r]; };
+  if (npairs == 0) __syncthreads();
   if (par == 1) {
 #pragma unroll
     for (int j = 0; j < NJ; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mrg[rg][head_dim<NJ>(r, j, h)][r32] = o[j][r];
-    if (h == 0) { mrg[rg][D][r32] = m; mrg[rg][D + 1][r32] = l; }
+      for (int r = 0; r < 16; ++r) at(rg, head_dim<NJ>(r, j, h), r32) = o[j][r];
+    if (h == 0) { at(rg, D, r32) = m; at(rg, D + 1, r32) = l; }
   }
   __syncthreads();
   if (par == 1 || !row_ok) return;
   {
-    const float m1 = mrg[rg][D][r32], l1 = mrg[rg][D + 1][r32];
+    const float m1 = at(rg, D, r32), l1 = at(rg, D + 1, r32);
     const float mn = fmaxf(m, m1);
     const float mu = mn == -INFINITY ? 0.f : mn;
     const float a0 = __builtin_amdgcn_exp2f((m - mu) * c), a1 = __builtin_amdgcn_exp2f((m1 - mu) * c);
@@ -389,15 +528,12 @@ __global__ __launch_bounds__(kThreads) void block_attn_mfma(Params p) {
 #pragma unroll
     for (int j = 0; j < NJ; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) o[j][r] = o[j][r] * a0 + mrg[rg][head_dim<NJ>(r, j, h)][r32] * a1;
+      for (int r = 0; r < 16; ++r) o[j][r] = o[j][r] * a0 + at(rg, head_dim<NJ>(r, j, h), r32) * a1;
   }
-
-  // ---- final normalisation and store
   const float inv = (kept && l > 0.f) ? 1.f / l : 0.f;
   uint16_t* orow = p.out + qrow * D;
 #pragma unroll
   for (int qd = 0; qd < 4; ++qd) {
-    // 4*NJ consecutive head dims start at NJ*(8*qd + 4h)
     uint32_t w[2 * NJ];
 #pragma unroll
     for (int e = 0; e < 4 * NJ; e += 2) {
@@ -567,10 +703,16 @@ extern "C" int dspark_block_attention(const void* q, const void* k_ctx, const vo
     int32_t* order = (int32_t*)ws;
     hipLaunchKernelGGL(attn_plan_kernel, dim3(1), dim3(1024), 0, s, p, order);
     p.order = order;
-    if (D == 128)
-      hipLaunchKernelGGL(block_attn_mfma<128>, dim3((unsigned)sh.tiles), dim3(kThreads), 0, s, p);
-    else
-      hipLaunchKernelGGL(block_attn_mfma<64>, dim3((unsigned)sh.tiles), dim3(kThreads), 0, s, p);
+    // a context read by at most two tiles per KV head streams from HBM
+    const bool deep = sh.ntiles <= 2;
+    const dim3 grid((unsigned)sh.tiles), block(kThreads);
+    if (D == 128) {
+      if (deep) hipLaunchKernelGGL((block_attn_mfma<128, true>), grid, block, 0, s, p);
+      else hipLaunchKernelGGL((block_attn_mfma<128, false>), grid, block, 0, s, p);
+    } else {
+      if (deep) hipLaunchKernelGGL((block_attn_mfma<64, true>), grid, block, 0, s, p);
+      else hipLaunchKernelGGL((block_attn_mfma<64, false>), grid, block, 0, s, p);
+    }
   } else {
     const int64_t nb = (int64_t)B * A * Hq;
     if (nb >= (1ll << 31)) return fail(DSPARK_ERR_INVALID_ARG, "block_attention: grid too large");
