@@ -88,14 +88,15 @@ __device__ __forceinline__ int visible_ctx(const Params& p, int b, int a, int S,
 }
 
 // One 32-key slab as this lane holds it: K as the A operand of S^T (key slot
-// r32, head dims 16*kk + 8h .. +7) and the V pieces of the 16 keys of its
-// half (key of (t, s8) = 8*(2t + s8/4) + 4h + s8%4, head dims NJ*r32 .. +NJ-1).
+// r32, head dims 16*kk + 8h .. +7) and V^T as the A operand of O^T for key
+// step t and head-dim block j (head dim 32j + r32; keys 16t + 4h + 0..3 and
+// 16t + 8 + 4h + 0..3, the keys whose probabilities this lane holds).
 template <int D>
 struct Slab {
   u32x4 kf[D / 16];
-  uint32_t v[2][8][D / 64];
+  u32x4 vf[2][D / 32];
   __device__ u32x4 k(int kk) const { return kf[kk]; }
-  __device__ uint32_t vp(int t, int s8, int j2) const { return v[t][s8][j2]; }
+  __device__ u32x4 v(int t, int j) const { return vf[t][j]; }
 };
 
 // Per-workgroup constants of a work item.
@@ -108,6 +109,18 @@ struct Item {
   int n_own;         // own-block keys of the tile
   int kvh, h, r32;
 };
+
+// x combined with the value of lane x ^ 32, in every lane: v_permlane32_swap
+// of x with itself leaves the low half's value in one result and the high
+// half's in the other.
+__device__ __forceinline__ float half_combine_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __builtin_elementwise_maximum(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_combine_add(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 // The running maximum of a row is only moved when a slab's maximum exceeds
 // it by more than this many powers of two: the exponentials then stay below
@@ -150,7 +163,7 @@ __device__ __forceinline__ void compute_slab(const Params& p, const Item& it, in
   float smax = sc[0];
 #pragma unroll
   for (int i = 1; i < 16; ++i) smax = fmaxf(smax, sc[i]);
-  smax = fmaxf(smax, __shfl_xor(smax, 32, kWave));
+  smax = half_combine_max(smax);
   // lazy maximum: move it (and rescale) only when this slab would push the
   // exponentials past 2^kLazyMax
   const bool grow = smax > m && (m == -INFINITY || (smax - m) * c > kLazyMax);
@@ -174,26 +187,17 @@ __device__ __forceinline__ void compute_slab(const Params& p, const Item& it, in
     psum += p0 + p1;
     pb[i / 8][(i % 8) / 2] = pack_bf16x2(p0, p1);
   }
-  psum += __shfl_xor(psum, 32, kWave);
+  psum = half_combine_add(psum);
   l += psum;
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      u32x4 va;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const uint32_t lo = sl.vp(t, 2 * w, j / 2), hi = sl.vp(t, 2 * w + 1, j / 2);
-        va[w] = (j & 1) ? pack_hi(lo, hi) : pack_lo(lo, hi);
-      }
-      o[j] = mfma32x32x16(va, pb[t], o[j]);
-    }
+    for (int j = 0; j < NJ; ++j) o[j] = mfma32x32x16(sl.v(t, j), pb[t], o[j]);
   }
 }
 
 // Head dim of accumulator register r of product j for a lane in half h.
-template <int NJ>
-__device__ __forceinline__ int head_dim(int r, int j, int h) { return NJ * (8 * (r / 4) + 4 * h + (r & 3)) + j; }
+__device__ __forceinline__ int head_dim(int r, int j, int h) { return 32 * j + 8 * (r / 4) + 4 * h + (r & 3); }
 
 // Work of a (request, tile) pair in 32-key slabs (context + own keys); -1
 // when none of its blocks is kept.
@@ -282,6 +286,9 @@ struct Ring {
   static constexpr int kPairBytes = 2 * kSlabBytes;      // parity-0 slab then parity-1 slab
   static constexpr int kBytes = 2 * kPairBytes;          // two slots
   static constexpr int kChunksPerThread = kPairBytes / 16 / kThreads;  // 16-byte pieces a thread moves per pair
+  // V pieces: groups of four pieces (32 head dims) XOR-rotated by the key, so
+  // the transposing reads of four consecutive keys hit distinct banks
+  __device__ static int v_piece(int key, int piece) { return piece ^ (4 * (key % (kPieces / 4))); }
 };
 
 // Moves pairs of slabs from HBM/L2 through registers into the LDS ring.
@@ -339,22 +346,38 @@ struct Stager {
   }
 };
 
-// This lane's operand pieces of one staged slab, all read from LDS into
-// registers before the products start.  K piece kk (key r32, head dims
-// 16*kk + 8h .. +7) sits at chunk r32*P + ((2kk + h) ^ (r32 mod P)) =
-// r32*P + (2kk ^ y) with y = h ^ (r32 mod P); V word (key ks, head dims
-// NJ*r32 + 2*j2 .. +1) at a lane constant plus an immediate.
+// This lane's operand pieces of one staged slab in the ring.  K piece kk
+// (key r32, head dims 16*kk + 8h .. +7) sits at chunk r32*P + ((2kk + h) ^
+// (r32 mod P)) = r32*P + (2kk ^ y), y = h ^ (r32 mod P).  V^T comes from
+// ds_read_b64_tr_b16: in each 16-lane group, lane l receives element l mod 4
+// of the 8 bytes addressed by lane 4e + l/4, as its element e.  So when lane
+// l (= r32 mod 16) addresses key kb + l/4, head dims d0 + 4(l mod 4) .. +3,
+// it receives keys kb .. kb+3 of head dim d0 + l: with d0 = 32j + 16(r32/16)
+// and kb = 16t + 4h (+8 for the second read) that is its V^T operand.
 template <int D>
 struct SlabView {
-  static constexpr int P = Ring<D>::kPieces;
+  using Rg = Ring<D>;
+  static constexpr int P = Rg::kPieces;
   const unsigned char* sp;  // slab start in the ring
-  uint32_t kbase, kx, vbase;
-  __device__ SlabView(const unsigned char* slab, int h, int r32)
-      : sp(slab), kbase(r32 * P * 16), kx((h ^ (r32 % P)) * 16), vbase(4 * h * D * 2 + (D / 32) * 2 * r32) {}
+  uint32_t kbase, kx;       // K: lane row, XOR term
+  uint32_t vbase, vx;       // V: lane part of the address, XOR term of the 64-byte group
+  __device__ SlabView(const unsigned char* slab, int h, int r32) : sp(slab) {
+    kbase = r32 * P * 16;
+    kx = (h ^ (r32 % P)) * 16;
+    const int l = r32 % 16, g2 = r32 / 16;
+    const int key = 4 * h + l / 4;  // plus 16t + 8e
+    vbase = Rg::kTensorBytes + key * (D * 2) + 32 * g2 + 8 * (l % 4);
+    vx = 64 * ((l / 4) % (P / 4));  // the piece XOR (4 * (key mod P/4)) in bytes
+  }
   __device__ u32x4 k(int kk) const { return *(const u32x4*)(sp + kbase + ((32 * kk) ^ kx)); }
-  __device__ uint32_t vp(int t, int s8, int j2) const {
-    const int ks = 8 * (2 * t + s8 / 4) + (s8 & 3);  // key minus 4h
-    return *(const uint32_t*)(sp + Ring<D>::kTensorBytes + vbase + ks * (D * 2) + 4 * j2);
+  __device__ u32x4 v(int t, int j) const {
+    typedef short i16x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    const unsigned char* a = sp + vbase + ((64 * j) ^ vx) + 16 * t * (D * 2);
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)a);
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a + 8 * (D * 2)));
+    const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+    return u32x4{l2.x, l2.y, h2.x, h2.y};
   }
 };
 
@@ -366,9 +389,7 @@ __device__ __forceinline__ void slab_from_lds(const SlabView<D>& v, Slab<D>& sl)
 #pragma unroll
   for (int t = 0; t < 2; ++t)
 #pragma unroll
-    for (int s8 = 0; s8 < 8; ++s8)
-#pragma unroll
-      for (int j2 = 0; j2 < NJ / 2; ++j2) sl.v[t][s8][j2] = v.vp(t, s8, j2);
+    for (int j = 0; j < NJ; ++j) sl.vf[t][j] = v.v(t, j);
 }
 
 // Deep: two load sets in flight and operands read at their point of use, for
@@ -439,7 +460,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int piece = t % P;
     st.piece_b = piece * 16;
     st.lds_k = (st.key_t * P + (piece ^ (st.key_t % P))) * 16;
-    st.lds_v = (st.key_t * P + piece) * 16;
+    st.lds_v = (st.key_t * P + Rg::v_piece(st.key_t, piece)) * 16;
     st.kc = (const unsigned char*)p.kc; st.vc = (const unsigned char*)p.vc;
     st.kb = (const unsigned char*)p.kb; st.vb = (const unsigned char*)p.vb;
     st.ctx_row0 = (int64_t)c0 + it.cbeg;
@@ -513,7 +534,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
     for (int j = 0; j < NJ; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) at(rg, head_dim<NJ>(r, j, h), r32) = o[j][r];
+      for (int r = 0; r < 16; ++r) at(rg, head_dim(r, j, h), r32) = o[j][r];
     if (h == 0) { at(rg, D, r32) = m; at(rg, D + 1, r32) = l; }
   }
   __syncthreads();
@@ -528,23 +549,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
     for (int j = 0; j < NJ; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) o[j][r] = o[j][r] * a0 + at(rg, head_dim<NJ>(r, j, h), r32) * a1;
+      for (int r = 0; r < 16; ++r) o[j][r] = o[j][r] * a0 + at(rg, head_dim(r, j, h), r32) * a1;
   }
   const float inv = (kept && l > 0.f) ? 1.f / l : 0.f;
   uint16_t* orow = p.out + qrow * D;
 #pragma unroll
-  for (int qd = 0; qd < 4; ++qd) {
-    uint32_t w[2 * NJ];
+  for (int j = 0; j < NJ; ++j)
 #pragma unroll
-    for (int e = 0; e < 4 * NJ; e += 2) {
-      const int r0 = 4 * qd + e / NJ, j0 = e % NJ;
-      const int r1 = 4 * qd + (e + 1) / NJ, j1 = (e + 1) % NJ;
-      w[e / 2] = pack_bf16x2(o[j0][r0] * inv, o[j1][r1] * inv);
-    }
-    uint16_t* dst = orow + NJ * (8 * qd + 4 * h);
-    *(u32x4*)dst = u32x4{w[0], w[1], w[2], w[3]};
-    if constexpr (NJ == 4) *(u32x4*)(dst + 8) = u32x4{w[4], w[5], w[6], w[7]};
-  }
+    for (int qd = 0; qd < 4; ++qd)  // head dims 32j + 8qd + 4h .. +3
+      *(u32x2*)(orow + head_dim(4 * qd, j, h)) =
+          u32x2{pack_bf16x2(o[j][4 * qd] * inv, o[j][4 * qd + 1] * inv),
+                pack_bf16x2(o[j][4 * qd + 2] * inv, o[j][4 * qd + 3] * inv)};
   if (p.lse && h == 0) {
     const int64_t li = ((int64_t)b * p.Hq + qh) * ((int64_t)p.A * p.gamma) + (int64_t)ua * p.gamma + uk;
     p.lse[li] = (kept && l > 0.f) ? m * p.scale + kLn2 * __builtin_amdgcn_logf(l) : -INFINITY;
