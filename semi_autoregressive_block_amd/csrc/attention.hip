@@ -10,10 +10,10 @@
 // gfx950 design (bf16 in, fp32 accumulate):
 // * Row space.  For request b and key/value head kvh the query rows of all
 //   blocks and of the Hq/Hkv query heads sharing kvh are laid out as
-//   u = (a * group + hg) * gamma + k and cut into 64-row tiles, so one tile
-//   packs several heads (and, for short blocks, several consecutive blocks)
-//   against the same keys: the MFMA M/N extent is filled by GQA packing, not
-//   by padding gamma.
+//   u = (a * group + hg) * gamma + k and cut into tiles of 64 or 128 rows,
+//   so one tile packs several heads (and, for short blocks, several
+//   consecutive blocks) against the same keys: the MFMA M/N extent is
+//   filled by GQA packing, not by padding gamma.
 // * One workgroup owns one tile for its whole key range: no split across
 //   workgroups, so no partial results, counters or cache-maintenance fences.
 //   A tile's context length is the largest anchor of its kept blocks; the
@@ -25,26 +25,27 @@
 //   longest-processing-time schedule.  Within one rank the KV heads are
 //   adjacent, so with 8 KV heads workgroup i runs on XCD i % 8 = kvh and
 //   each XCD keeps one head's context K/V in its L2.
-// * Four waves per workgroup: two 32-row groups x two key parities.  Per
-//   32-key slab a wave computes S^T = K Q^T (v_mfma_f32_32x32x16_bf16; K rows
-//   and Q rows are loaded as 16-byte row pieces), so each lane owns ONE query
-//   row: the online-softmax max, sum and rescale are lane-local plus a single
-//   cross-half exchange.  The probabilities feed O^T = V^T P^T straight from
-//   the S^T accumulator layout (no transpose of P); V's head dimension is
-//   permuted (slot m of product j is d = NJ*m + j) so every lane loads
-//   NJ*2-byte pieces of key rows and transposes them in registers.
-// * The slab loop is software-pipelined: the wave's next slab is loaded
-//   (unconditionally, from clamped addresses, so the loads stay in flight
-//   across the MFMA work) while the current one is computed.  Parities merge
-//   through LDS at the end.
+// * Two tile heights.  When a context is read by at most two 64-row tiles
+//   per KV head (serving: one block per request) it streams from HBM once:
+//   64-row tiles, two workgroups per compute unit.  When many tiles re-read
+//   it (all-anchor training) it comes from L2: 128-row tiles, so each staged
+//   slab serves twice the rows.  Either way eight waves share a compute unit.
+// * Waves: 32-row groups x two key parities.  Per 32-key slab a wave
+//   computes S^T = K Q^T (v_mfma_f32_32x32x16_bf16), so each lane owns ONE
+//   query row: the online-softmax max, sum and rescale are lane-local plus a
+//   single cross-half exchange (v_permlane32_swap).  The probabilities feed
+//   O^T = V^T P^T straight from the S^T accumulator layout (no transpose of
+//   P); V^T operands come from transposing LDS reads.
+// * K/V staging: pairs of slabs (one per parity) go global -> registers ->
+//   a two-slot LDS ring, with two register sets of loads in flight; parities
+//   merge through LDS at the end.
 #include "common.h"
 
 using namespace dspark;
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kTileRows = 64;
+constexpr int kTileRows = 64;  // rows per tile of the streaming kernel and of the workspace
 constexpr int kPlanBins = 4096;  // cost buckets of the planner's counting sort
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.69314718055994531f;
@@ -63,6 +64,7 @@ struct Params {
   const int32_t* order;  // launch order of tile ids (planner output)
   int32_t* status;
   int B, A, gamma, Hq, Hkv, group, ntiles, nrows;  // nrows = A * group * gamma
+  int tile_rows;                                    // rows per tile (64 or 128)
   int total_ctx, max_ctx;
   float scale;
 };
@@ -87,17 +89,6 @@ __device__ __forceinline__ int visible_ctx(const Params& p, int b, int a, int S,
   return clampi(an, 0, S);
 }
 
-// One 32-key slab as this lane holds it: K as the A operand of S^T (key slot
-// r32, head dims 16*kk + 8h .. +7) and V^T as the A operand of O^T for key
-// step t and head-dim block j (head dim 32j + r32; keys 16t + 4h + 0..3 and
-// 16t + 8 + 4h + 0..3, the keys whose probabilities this lane holds).
-template <int D>
-struct Slab {
-  u32x4 kf[D / 16];
-  u32x4 vf[2][D / 32];
-  __device__ u32x4 k(int kk) const { return kf[kk]; }
-  __device__ u32x4 v(int t, int j) const { return vf[t][j]; }
-};
 
 // Per-workgroup constants of a work item.
 struct Item {
@@ -128,20 +119,27 @@ __device__ __forceinline__ float half_combine_add(float x) {
 // and most slabs skip the rescale of the accumulators entirely.
 constexpr float kLazyMax = 8.f;
 
-// Online-softmax update of this lane's row with one slab.
+// S^T of one slab: key slot i of accumulator register i's row, this lane's
+// query row as the column.
 template <int D, class Src>
-__device__ __forceinline__ void compute_slab(const Params& p, const Item& it, int s, const Src& sl,
-                                             const u32x4* qf, bool kept, int lim, int ua, int a_lo,
-                                             float c, float& m, float& l, f32x16* o) {
-  constexpr int KK = D / 16, NJ = D / 32;
-  const bool own = s >= it.n_ctx_slabs;
-  const int j0 = own ? 0 : it.cbeg + s * 32;
-  const int os = own ? (s - it.n_ctx_slabs) * 32 : 0;
+__device__ __forceinline__ f32x16 qk_slab(const Src& sl, const u32x4* qf) {
   f32x16 sc;
 #pragma unroll
   for (int i = 0; i < 16; ++i) sc[i] = 0.f;
 #pragma unroll
-  for (int kk = 0; kk < KK; ++kk) sc = mfma32x32x16(sl.k(kk), qf[kk], sc);
+  for (int kk = 0; kk < D / 16; ++kk) sc = mfma32x32x16(sl.k(kk), qf[kk], sc);
+  return sc;
+}
+
+// Online-softmax update of this lane's row with the scores sc of slab s.
+template <int D, class Src>
+__device__ __forceinline__ void softmax_pv(const Params& p, const Item& it, int s, f32x16 sc, const Src& sl,
+                                           bool kept, int lim, int ua, int a_lo, float c, float& m, float& l,
+                                           f32x16* o) {
+  constexpr int NJ = D / 32;
+  const bool own = s >= it.n_ctx_slabs;
+  const int j0 = own ? 0 : it.cbeg + s * 32;
+  const int os = own ? (s - it.n_ctx_slabs) * 32 : 0;
   // visible keys of this lane's row in this slab: context keys below
   // min(chunk end, anchor), own keys of its block only (one gamma range)
   int vlo, vhi;
@@ -196,6 +194,13 @@ __device__ __forceinline__ void compute_slab(const Params& p, const Item& it, in
   }
 }
 
+template <int D, class Src>
+__device__ __forceinline__ void compute_slab(const Params& p, const Item& it, int s, const Src& sl,
+                                             const u32x4* qf, bool kept, int lim, int ua, int a_lo,
+                                             float c, float& m, float& l, f32x16* o) {
+  softmax_pv<D>(p, it, s, qk_slab<D>(sl, qf), sl, kept, lim, ua, a_lo, c, m, l, o);
+}
+
 // Head dim of accumulator register r of product j for a lane in half h.
 __device__ __forceinline__ int head_dim(int r, int j, int h) { return 32 * j + 8 * (r / 4) + 4 * h + (r & 3); }
 
@@ -206,9 +211,9 @@ __device__ __forceinline__ int tile_cost(const Params& p, int b, int tile, int& 
   int c0, S;
   ctx_range(p, b, c0, S, false);
   const int rpb = p.group * p.gamma;
-  const int u0 = tile * kTileRows;
+  const int u0 = tile * p.tile_rows;
   a_lo = u0 / rpb;
-  a_hi = min(p.A - 1, (u0 + kTileRows - 1) / rpb);
+  a_hi = min(p.A - 1, (u0 + p.tile_rows - 1) / rpb);
   L = 0;
   any_kept = false;
   for (int a = a_lo; a <= a_hi; ++a) {
@@ -270,46 +275,48 @@ __global__ __launch_bounds__(1024) void attn_plan_kernel(Params p, int32_t* __re
 // ------------------------------------------------------------ MFMA kernel
 // K and V reach the waves through LDS: the workgroup's four waves load each
 // pair of 32-key slabs (one per key parity) together, as 16-byte pieces,
-// into a two-slot ring, so a slab is fetched once per workgroup and read by
-// both row groups.  Loads in flight live in 32-register sets, which keeps a
-// wave within 256 registers: two workgroups share a compute unit and each
-// SIMD interleaves two waves' matrix-core and softmax work.  K rows are
-// stored with their 16-byte pieces XOR-swizzled by the key index, so the
-// MFMA-operand reads (one piece of 32 different keys) hit distinct LDS
-// banks; V rows are stored plainly (its reads are 32 consecutive pieces of
-// one key row).
+// into two-slot rings (one for K, one for V), so a slab is fetched once per
+// workgroup and read by both row groups.  Loads in flight live in
+// 32-register sets, which keeps a wave within 256 registers: two
+// workgroups share a compute unit and each SIMD interleaves two waves'
+// matrix-core and softmax work.  K rows are stored with their 16-byte
+// pieces XOR-swizzled by the key index, so the MFMA-operand reads (one
+// piece of 32 different keys) hit distinct LDS banks; V rows have their
+// 64-byte groups XOR-rotated by the key, for the transposing reads.
 template <int D>
 struct Ring {
   static constexpr int kPieces = D * 2 / 16;             // 16-byte pieces per key row
-  static constexpr int kTensorBytes = 32 * D * 2;        // one tensor of one slab
-  static constexpr int kSlabBytes = 2 * kTensorBytes;    // K then V
-  static constexpr int kPairBytes = 2 * kSlabBytes;      // parity-0 slab then parity-1 slab
-  static constexpr int kBytes = 2 * kPairBytes;          // two slots
-  static constexpr int kChunksPerThread = kPairBytes / 16 / kThreads;  // 16-byte pieces a thread moves per pair
+  static constexpr int kTensorBytes = 32 * D * 2;        // K (or V) of one slab
+  static constexpr int kSlotBytes = 2 * kTensorBytes;    // parity-0 slab then parity-1 slab
+  static constexpr int kVRing = 2 * kSlotBytes;          // the V ring follows the two K slots
+  static constexpr int kBytes = 2 * kVRing;
   // V pieces: groups of four pieces (32 head dims) XOR-rotated by the key, so
   // the transposing reads of four consecutive keys hit distinct banks
   __device__ static int v_piece(int key, int piece) { return piece ^ (4 * (key % (kPieces / 4))); }
+  __device__ static unsigned char* k_slot(unsigned char* ring, int i) { return ring + (i & 1) * kSlotBytes; }
+  __device__ static unsigned char* v_slot(unsigned char* ring, int i) { return ring + kVRing + (i & 1) * kSlotBytes; }
 };
 
-// Moves pairs of slabs from HBM/L2 through registers into the LDS ring.
-// Piece c = threadIdx.x + kThreads*j of a pair is 16 bytes of tensor
-// T = c / (32P) (slab T/2, K for even T, V for odd) of key (c mod 32P) / P,
-// head dims 8*(c mod P) .. +7 (P pieces per key row).  Since kThreads is a
-// multiple of P, a thread keeps one piece index and one key offset for all
-// j and the rest is a compile-time constant per j: LDS stores take
-// immediate offsets and a load is a wave-uniform slab base plus one 32-bit
-// lane offset.  Keys past a source's last row are read from that last row
-// (they are masked in the scores).
-template <int D>
+// Moves the K or V half of a slab pair from HBM/L2 through registers into
+// a ring slot.  Piece c = threadIdx.x + NT*j of a slot (NT threads) is 16
+// bytes of slab c / (32P) (parity), key (c mod 32P) / P, head dims
+// 8*(c mod P) .. +7 (P pieces per key row).  Since NT is a multiple of P and
+// NT and 32P divide one another, a thread keeps one slab, key and piece
+// offset for all j and the rest is a compile-time constant per j: LDS stores
+// take immediate offsets and a load is a wave-uniform slab base plus one
+// 32-bit lane offset.  Keys past a source's last row are read from that last
+// row (they are masked in the scores).
+template <int D, int NT>
 struct Stager {
   using Rg = Ring<D>;
   static constexpr int P = Rg::kPieces;
-  static constexpr int N = Rg::kChunksPerThread;
-  static_assert(kThreads % P == 0 && ((kThreads / P) % P == 0 || kThreads / P >= 32), "piece layout");
+  static constexpr int N = Rg::kSlotBytes / 16 / NT;  // pieces a thread moves per slot
+  static_assert(NT % P == 0 && (NT % (32 * P) == 0 || (32 * P) % NT == 0) && N >= 1, "piece layout");
   // per-thread constants
+  int slab_t;          // slab of piece j = 0 (wave-uniform)
   int key_t;           // key of piece j = 0
   uint32_t piece_b;    // byte offset of the piece inside a key row
-  uint32_t lds_k, lds_v;  // LDS byte offset of piece j = 0 in a K / V tensor
+  uint32_t lds_k, lds_v;  // ring byte offset of piece j = 0 in a K / V slab
   // wave-uniform
   const unsigned char *kc, *vc, *kb, *vb;
   int64_t ctx_row0, own_row0;  // first row of the context chunk / of the tile's own keys
@@ -317,63 +324,62 @@ struct Stager {
   uint32_t row_b;              // bytes between consecutive rows (all heads)
   uint32_t head_b;             // byte offset of this KV head inside a row
 
-  static constexpr int tensor_of(int j) { return (kThreads * j) / (32 * P); }
-  static constexpr int keyoff_of(int j) { return ((kThreads * j) % (32 * P)) / P; }
+  static constexpr int slab_of(int j) { return (NT * j) / (32 * P); }
+  static constexpr int keyoff_of(int j) { return ((NT * j) % (32 * P)) / P; }
 
+  template <bool kV>
   __device__ void load(int pair, u32x4 (&R)[N]) const {
 #pragma unroll
     for (int j = 0; j < N; ++j) {
-      const int T = tensor_of(j);
       // an odd last pair repeats a slab (not computed)
-      const int s = min(2 * pair + T / 2, nslab - 1);
+      const int s = min(2 * pair + slab_t + slab_of(j), nslab - 1);
       const bool own = s >= n_ctx_slabs;
       const int k0 = own ? (s - n_ctx_slabs) * 32 : s * 32;
       const int nvalid = (own ? own_keys : ctx_keys) - k0;
-      const unsigned char* src = (T & 1) ? (own ? vb : vc) : (own ? kb : kc);
+      const unsigned char* src = kV ? (own ? vb : vc) : (own ? kb : kc);
       src += ((own ? own_row0 : ctx_row0) + k0) * (int64_t)row_b + head_b;
-      const uint32_t off = (uint32_t)min(key_t + keyoff_of(j), nvalid - 1) * row_b + piece_b;
+      const uint32_t off = __umul24((uint32_t)min(key_t + keyoff_of(j), nvalid - 1), row_b) + piece_b;
       R[j] = *(const u32x4*)(src + off);
     }
   }
 
+  template <bool kV>
   __device__ void store(unsigned char* slot, const u32x4 (&R)[N]) const {
 #pragma unroll
-    for (int j = 0; j < N; ++j) {
-      const int T = tensor_of(j);
-      const uint32_t off = T * Rg::kTensorBytes + keyoff_of(j) * P * 16;
-      *(u32x4*)(slot + ((T & 1) ? lds_v : lds_k) + off) = R[j];
-    }
+    for (int j = 0; j < N; ++j)
+      *(u32x4*)(slot + (kV ? lds_v : lds_k) + slab_of(j) * Rg::kTensorBytes + keyoff_of(j) * P * 16) = R[j];
   }
 };
 
-// This lane's operand pieces of one staged slab in the ring.  K piece kk
-// (key r32, head dims 16*kk + 8h .. +7) sits at chunk r32*P + ((2kk + h) ^
-// (r32 mod P)) = r32*P + (2kk ^ y), y = h ^ (r32 mod P).  V^T comes from
-// ds_read_b64_tr_b16: in each 16-lane group, lane l receives element l mod 4
-// of the 8 bytes addressed by lane 4e + l/4, as its element e.  So when lane
-// l (= r32 mod 16) addresses key kb + l/4, head dims d0 + 4(l mod 4) .. +3,
-// it receives keys kb .. kb+3 of head dim d0 + l: with d0 = 32j + 16(r32/16)
-// and kb = 16t + 4h (+8 for the second read) that is its V^T operand.
+// This lane's operand pieces of one staged slab.  K piece kk (key r32, head
+// dims 16*kk + 8h .. +7) sits at chunk r32*P + ((2kk + h) ^ (r32 mod P)) =
+// r32*P + (2kk ^ y), y = h ^ (r32 mod P).  V^T comes from ds_read_b64_tr_b16:
+// in each 16-lane group, lane l receives element l mod 4 of the 8 bytes
+// addressed by lane 4e + l/4, as its element e.  So when lane l (= r32 mod
+// 16) addresses key kb + l/4, head dims d0 + 4(l mod 4) .. +3, it receives
+// keys kb .. kb+3 of head dim d0 + l: with d0 = 32j + 16(r32/16) and
+// kb = 16t + 4h (+8 for the second read) that is its V^T operand.
 template <int D>
 struct SlabView {
   using Rg = Ring<D>;
   static constexpr int P = Rg::kPieces;
-  const unsigned char* sp;  // slab start in the ring
-  uint32_t kbase, kx;       // K: lane row, XOR term
-  uint32_t vbase, vx;       // V: lane part of the address, XOR term of the 64-byte group
-  __device__ SlabView(const unsigned char* slab, int h, int r32) : sp(slab) {
+  const unsigned char *kp, *vp;  // this slab's K and V in the rings
+  uint32_t kbase, kx;            // K: lane row, XOR term
+  uint32_t vbase, vx;            // V: lane part of the address, XOR term of the 64-byte group
+  __device__ SlabView(const unsigned char* kslab, const unsigned char* vslab, int h, int r32)
+      : kp(kslab), vp(vslab) {
     kbase = r32 * P * 16;
     kx = (h ^ (r32 % P)) * 16;
     const int l = r32 % 16, g2 = r32 / 16;
     const int key = 4 * h + l / 4;  // plus 16t + 8e
-    vbase = Rg::kTensorBytes + key * (D * 2) + 32 * g2 + 8 * (l % 4);
+    vbase = key * (D * 2) + 32 * g2 + 8 * (l % 4);
     vx = 64 * ((l / 4) % (P / 4));  // the piece XOR (4 * (key mod P/4)) in bytes
   }
-  __device__ u32x4 k(int kk) const { return *(const u32x4*)(sp + kbase + ((32 * kk) ^ kx)); }
+  __device__ u32x4 k(int kk) const { return *(const u32x4*)(kp + kbase + ((32 * kk) ^ kx)); }
   __device__ u32x4 v(int t, int j) const {
     typedef short i16x4 __attribute__((ext_vector_type(4)));
     typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-    const unsigned char* a = sp + vbase + ((64 * j) ^ vx) + 16 * t * (D * 2);
+    const unsigned char* a = vp + vbase + ((64 * j) ^ vx) + 16 * t * (D * 2);
     const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)a);
     const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(a + 8 * (D * 2)));
     const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
@@ -381,27 +387,17 @@ struct SlabView {
   }
 };
 
-template <int D>
-__device__ __forceinline__ void slab_from_lds(const SlabView<D>& v, Slab<D>& sl) {
-  constexpr int KK = D / 16, NJ = D / 32;
-#pragma unroll
-  for (int kk = 0; kk < KK; ++kk) sl.kf[kk] = v.k(kk);
-#pragma unroll
-  for (int t = 0; t < 2; ++t)
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) sl.vf[t][j] = v.v(t, j);
-}
-
-// Deep: two load sets in flight and operands read at their point of use, for
-// contexts streamed from HBM once (latency-bound); otherwise one load set and
-// whole-slab operand reads, for contexts that many tiles re-read from L2
-// (matrix-core-bound).
-template <int D, bool Deep>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void block_attn_mfma(Params p) {
+// One workgroup per tile of 32*RG query rows and one (request, KV head):
+// RG row groups x two key parities, one wave each.  NSETS register sets of
+// K/V loads are in flight while a pair is computed.
+template <int D, int NSETS, int RG>
+__global__ __launch_bounds__(64 * 2 * RG) __attribute__((amdgpu_waves_per_eu(2, 2))) void block_attn_mfma(Params p) {
   using Rg = Ring<D>;
   constexpr int NJ = D / 32;
   constexpr int KK = D / 16;
-  __shared__ __align__(16) unsigned char ring[Rg::kBytes];
+  constexpr int NT = 64 * 2 * RG;  // RG row groups x two key parities, one wave each
+  constexpr int kMergeBytes = RG * (D + 2) * 32 * 4;
+  __shared__ __align__(16) unsigned char ring[Rg::kBytes > kMergeBytes ? Rg::kBytes : kMergeBytes];
 
   // the work item is the same for the whole workgroup: keep it in scalars
   int wid = __builtin_amdgcn_readfirstlane(p.order ? p.order[blockIdx.x] : (int)blockIdx.x);
@@ -420,11 +416,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   a_hi = __builtin_amdgcn_readfirstlane(a_hi);
   any_kept = __builtin_amdgcn_readfirstlane((int)any_kept) != 0;
   const int rpb = p.group * p.gamma;
-  const int u0 = tile * kTileRows;
+  const int u0 = tile * p.tile_rows;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int rg = wave & 1, par = wave >> 1;
+  const int rg = wave % RG, par = wave / RG;
   const int h = lane >> 5, r32 = lane & 31;
   const int u = u0 + rg * 32 + r32;
   const bool row_ok = u < p.nrows;
@@ -452,15 +448,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int npairs = (nslab + 1) / 2;
   const float c = p.scale * kLog2e;
 
-  Stager<D> st;
+  Stager<D, NT> st;
   {
     constexpr int P = Rg::kPieces;
     const int t = threadIdx.x;
-    st.key_t = t / P;
+    st.slab_t = (64 * wave) / (32 * P);  // 0 unless NT > 32P
+    st.key_t = (t % (32 * P)) / P;
     const int piece = t % P;
     st.piece_b = piece * 16;
-    st.lds_k = (st.key_t * P + (piece ^ (st.key_t % P))) * 16;
-    st.lds_v = (st.key_t * P + Rg::v_piece(st.key_t, piece)) * 16;
+    st.lds_k = st.slab_t * Rg::kTensorBytes + (st.key_t * P + (piece ^ (st.key_t % P))) * 16;
+    st.lds_v = st.slab_t * Rg::kTensorBytes + (st.key_t * P + Rg::v_piece(st.key_t, piece)) * 16;
     st.kc = (const unsigned char*)p.kc; st.vc = (const unsigned char*)p.vc;
     st.kb = (const unsigned char*)p.kb; st.vb = (const unsigned char*)p.vb;
     st.ctx_row0 = (int64_t)c0 + it.cbeg;
@@ -486,48 +483,51 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   //      they repeat the last slab, from L2), so the wait before each store
   //      counts on exactly the younger set's loads being in flight; a step
   //      past the end computes nothing.
-  auto step = [&](int i, int ahead, u32x4 (&Rs)[Rg::kChunksPerThread]) {
-    if (i + 1 < npairs) st.store(ring + ((i + 1) & 1) * Rg::kPairBytes, Rs);
-    if (Deep || i + ahead < npairs) st.load(i + ahead, Rs);
-    const int s = 2 * i + par;
-    const SlabView<D> view(ring + (i & 1) * Rg::kPairBytes + par * Rg::kSlabBytes, h, r32);
-    if (s < nslab) {
-      if constexpr (Deep) {
-        compute_slab<D>(p, it, s, view, qf, kept, lim, ua, a_lo, c, m, l, o);
-      } else {
-        Slab<D> sl;
-        slab_from_lds<D>(view, sl);
-        compute_slab<D>(p, it, s, sl, qf, kept, lim, ua, a_lo, c, m, l, o);
-      }
-    }
-    __syncthreads();
+  auto view = [&](int ik, int iv) {
+    return SlabView<D>(Rg::k_slot(ring, ik) + par * Rg::kTensorBytes,
+                       Rg::v_slot(ring, iv) + par * Rg::kTensorBytes, h, r32);
   };
+  constexpr int N = Stager<D, NT>::N;
+  // ---- pair i is computed from ring slot i & 1 while pair i + 1 goes from
+  //      registers into the other slot and pairs i + 2 .. i + NSETS are in
+  //      flight in the register sets (the loop is unrolled by NSETS so each
+  //      set has fixed registers).  The loads are unconditional (past the
+  //      end they repeat the last slab, from L2), so the wait before each
+  //      store counts on exactly the younger sets' loads being in flight; a
+  //      step past the end computes nothing.
   if (npairs > 0) {
-    if constexpr (Deep) {
-      // two sets, unrolled by two so each has fixed registers
-      u32x4 Ra[Rg::kChunksPerThread], Rb[Rg::kChunksPerThread];
-      st.load(0, Ra);
-      st.load(1, Rb);
-      st.store(ring, Ra);
-      st.load(2, Ra);
-      __syncthreads();
-      for (int i = 0; i < npairs; i += 2) {
-        step(i, 3, Rb);
-        step(i + 1, 3, Ra);
+    u32x4 Rk[NSETS][N], Rv[NSETS][N];
+#pragma unroll
+    for (int q = 0; q < NSETS; ++q) {
+      st.template load<false>(q, Rk[q]);
+      st.template load<true>(q, Rv[q]);
+    }
+    st.template store<false>(Rg::k_slot(ring, 0), Rk[0]);
+    st.template store<true>(Rg::v_slot(ring, 0), Rv[0]);
+    st.template load<false>(NSETS, Rk[0]);
+    st.template load<true>(NSETS, Rv[0]);
+    __syncthreads();
+    for (int i0 = 0; i0 < npairs; i0 += NSETS) {
+#pragma unroll
+      for (int q = 0; q < NSETS; ++q) {
+        const int i = i0 + q;
+        const int set = (q + 1) % NSETS;
+        if (i + 1 < npairs) {
+          st.template store<false>(Rg::k_slot(ring, i + 1), Rk[set]);
+          st.template store<true>(Rg::v_slot(ring, i + 1), Rv[set]);
+        }
+        st.template load<false>(i + 1 + NSETS, Rk[set]);
+        st.template load<true>(i + 1 + NSETS, Rv[set]);
+        const int s = 2 * i + par;
+        if (s < nslab) compute_slab<D>(p, it, s, view(i, i), qf, kept, lim, ua, a_lo, c, m, l, o);
+        __syncthreads();
       }
-    } else {
-      u32x4 R[Rg::kChunksPerThread];
-      st.load(0, R);
-      st.store(ring, R);
-      st.load(1, R);
-      __syncthreads();
-      for (int i = 0; i < npairs; ++i) step(i, 2, R);
     }
   }
 
   // ---- merge the two key parities of each row group through LDS (the ring
   //      is free after the loop's last barrier)
-  float* mrg = (float*)ring;  // [2 row groups][D + 2][32]
+  float* mrg = (float*)ring;  // [RG row groups][D + 2][32]
   auto at = [&](int g, int d, int r) -> float& { return mrg[((size_t)g * (D + 2) + d) * 32 + r]; };
   if (npairs == 0) __syncthreads();
   if (par == 1) {
@@ -655,11 +655,11 @@ struct Shape {
   int64_t tiles;  // B * ntiles * Hkv
 };
 
-Shape make_shape(int B, int A, int gamma, int Hq, int Hkv) {
+Shape make_shape(int B, int A, int gamma, int Hq, int Hkv, int rows = kTileRows) {
   Shape s{};
   s.group = Hq / Hkv;
   s.nrows = A * s.group * gamma;
-  s.ntiles = (s.nrows + kTileRows - 1) / kTileRows;
+  s.ntiles = (s.nrows + rows - 1) / rows;
   s.tiles = (int64_t)s.ntiles * B * Hkv;
   return s;
 }
@@ -699,14 +699,19 @@ extern "C" int dspark_block_attention(const void* q, const void* k_ctx, const vo
       (total_ctx > 0 && (!k_ctx || !v_ctx)))
     return fail(DSPARK_ERR_INVALID_ARG, "block_attention: null required pointer");
   hipStream_t s = (hipStream_t)stream;
-  const Shape sh = make_shape(B, A, gamma, Hq, Hkv);
+  // a context read by at most two 64-row tiles per KV head streams from HBM
+  // (64-row tiles, two load sets in flight); otherwise tiles of 128 rows
+  // halve the K/V traffic per product
+  const bool deep = make_shape(B, A, gamma, Hq, Hkv).ntiles <= 2;
+  const int rows = deep ? 64 : 128;
+  const Shape sh = make_shape(B, A, gamma, Hq, Hkv, rows);
   Params p{};
   p.q = (const uint16_t*)q; p.kc = (const uint16_t*)k_ctx; p.vc = (const uint16_t*)v_ctx;
   p.offs = ctx_offsets; p.kb = (const uint16_t*)k_blk; p.vb = (const uint16_t*)v_blk;
   p.anchor = anchor_pos; p.keep = keep_mask; p.out = (uint16_t*)out; p.lse = lse;
   p.status = dev_status;
   p.B = B; p.A = A; p.gamma = gamma; p.Hq = Hq; p.Hkv = Hkv; p.group = sh.group;
-  p.ntiles = sh.ntiles; p.nrows = sh.nrows; p.total_ctx = total_ctx; p.max_ctx = max_ctx;
+  p.ntiles = sh.ntiles; p.nrows = sh.nrows; p.tile_rows = rows; p.total_ctx = total_ctx; p.max_ctx = max_ctx;
   p.scale = scale;
   const bool aligned = ((uintptr_t)q | (uintptr_t)k_ctx | (uintptr_t)v_ctx | (uintptr_t)k_blk |
                         (uintptr_t)v_blk | (uintptr_t)out) % 16 == 0;
@@ -718,15 +723,13 @@ extern "C" int dspark_block_attention(const void* q, const void* k_ctx, const vo
     int32_t* order = (int32_t*)ws;
     hipLaunchKernelGGL(attn_plan_kernel, dim3(1), dim3(1024), 0, s, p, order);
     p.order = order;
-    // a context read by at most two tiles per KV head streams from HBM
-    const bool deep = sh.ntiles <= 2;
-    const dim3 grid((unsigned)sh.tiles), block(kThreads);
+    const dim3 grid((unsigned)sh.tiles), block(deep ? 256 : 512);
     if (D == 128) {
-      if (deep) hipLaunchKernelGGL((block_attn_mfma<128, true>), grid, block, 0, s, p);
-      else hipLaunchKernelGGL((block_attn_mfma<128, false>), grid, block, 0, s, p);
+      if (deep) hipLaunchKernelGGL((block_attn_mfma<128, 2, 2>), grid, block, 0, s, p);
+      else hipLaunchKernelGGL((block_attn_mfma<128, 2, 4>), grid, block, 0, s, p);
     } else {
-      if (deep) hipLaunchKernelGGL((block_attn_mfma<64, true>), grid, block, 0, s, p);
-      else hipLaunchKernelGGL((block_attn_mfma<64, false>), grid, block, 0, s, p);
+      if (deep) hipLaunchKernelGGL((block_attn_mfma<64, 2, 2>), grid, block, 0, s, p);
+      else hipLaunchKernelGGL((block_attn_mfma<64, 2, 4>), grid, block, 0, s, p);
     }
   } else {
     const int64_t nb = (int64_t)B * A * Hq;
