@@ -87,19 +87,30 @@ __device__ __forceinline__ void fold_key_global(uint64_t* keys, int row, int R, 
 
 // ----------------------------------------------------------------- MFMA path
 // NW waves per workgroup, 16 rows per wave (row group = 16*NW rows), KS
-// maximum 32-wide rank steps.  The vocabulary is cut into 64-column tiles
-// handed out interleaved: at step t of its loop workgroup w owns tile
-// t*grid + w, so the workgroups running side by side read one contiguous
-// span of every W2 row and every base row.  W2[0:r, tile] is staged through
-// a double-buffered LDS tile while the next TWO tiles' W2 and base slices are
-// in flight (two register staging sets).  Every global load is unconditional from a
-// clamped, always-valid address (invalid lanes are zeroed after the load),
-// so the loads stay in flight across the MFMA work instead of serialising
-// behind branches.
+// 32-wide rank steps (rank padded with zeros to 32*KS).  The vocabulary is
+// cut into 64-column tiles handed out interleaved: at step t of its loop
+// workgroup w owns tile t*grid + w, so the workgroups running side by side
+// read one contiguous span of every W2 row and every base row.
+//
+// The product is computed transposed, out^T = W2^T E^T: W2^T is the A operand
+// (v_mfma_f32_16x16x32_bf16), read from the LDS copy of the tile with
+// ds_read_b64_tr_b16, and E^T = W1[prev]^T is the B operand, held in
+// registers.  Lane (n, g) of a wave then owns row n of the wave's 16 and,
+// for product j, columns 16j + 4g .. +3 of the tile: its base logits are
+// four 16-byte loads and its argmax is lane-local until the final fold.
+//
+// Loads: NS register sets hold tiles t .. t+NS-1 (W2 pieces and the lane's
+// base logits).  Iteration t computes tile t from LDS, issues tile t + NS's
+// loads into the freed set and moves tile t + 1's W2 into the other LDS
+// buffer, so every load has about NS - 1 iterations to arrive.  Every global
+// load is unconditional from a clamped, always-valid address (invalid lanes
+// are zeroed after the load).  The step's dependent reads (the previous
+// step's keys, then the W1 rows they select) go out before the tile loads,
+// so they do not queue behind them.
 constexpr int kTileCols = 64;
-constexpr int kLdsRow = kTileCols * 2 + 8;  // bytes per staged W2 row (+8: spreads banks)
+constexpr int kLdsRow = 144;  // bytes per staged W2 row of a tile (128 + 16: spreads LDS banks)
 
-template <int NW, int KS>
+template <int NW, int KS, int NS>
 __global__ __launch_bounds__(64 * NW) void markov_step_mfma(
     const float* __restrict__ base, const uint16_t* __restrict__ w1,
     const uint16_t* __restrict__ w2, const int32_t* __restrict__ first_prev,
@@ -107,173 +118,144 @@ __global__ __launch_bounds__(64 * NW) void markov_step_mfma(
     float* __restrict__ step_logits, int R, int gamma, int V, int r, int step, float invT,
     int greedy, uint32_t seed_lo, uint32_t seed_hi, int32_t* __restrict__ status) {
   extern __shared__ __align__(16) unsigned char smem[];
-  constexpr int NT = 64 * NW;                       // threads
-  constexpr int STG = (KS * 32 * 8 + NT - 1) / NT;  // 16-byte W2 pieces per thread per tile
-  const int rpad = ((r + 31) / 32) * 32;
-  const int ks = rpad / 32;
-  unsigned char* buf0 = smem;
-  unsigned char* buf1 = smem + (size_t)rpad * kLdsRow;
+  constexpr int NT = 64 * NW;                // threads
+  constexpr int KR = 32 * KS;                // padded rank
+  constexpr int STG = (KR * 8 + NT - 1) / NT;  // 16-byte W2 pieces per thread per tile
+  constexpr int kBuf = KR * kLdsRow;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, g = lane >> 4;
-  const int rowbase = blockIdx.y * 16 * NW + wave * 16;
+  const int row = blockIdx.y * 16 * NW + wave * 16 + n;  // this lane's row
+  const int rowc = min(row, R - 1);
 
   const int ntiles_all = (V + kTileCols - 1) / kTileCols;
   const int ntile = ntiles_all > (int)blockIdx.x ? (ntiles_all - 1 - (int)blockIdx.x) / (int)gridDim.x + 1 : 0;
   auto tile_col = [&](int t) -> int64_t { return ((int64_t)t * gridDim.x + blockIdx.x) * kTileCols; };
 
-  // ---- E = W1[prev] as MFMA A operands: row rowbase + n, rank 32kk + 8g .. +7
-  // (gathered after the first tiles' loads are in flight; see below)
-  u32x4 ea[KS];
-  auto gather_e = [&]() {
-    const int row = rowbase + n;
-    const int pv = decode_prev(keys_prev, first_prev, min(row, R - 1), R, V,
-                               blockIdx.x == 0 && g == 0 && row < R ? status : nullptr);
+  // ---- E^T operands: rank 32kk + 8g .. +7 of W1[prev(row)]
+  u32x4 eb[KS];
+  auto gather_e = [&](int pv) {
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
-      if (kk < ks) {
-        const int k = kk * 32 + g * 8;
-        const u32x4 v = *(const u32x4*)(w1 + (int64_t)pv * r + min(k, r - 8));
-        ea[kk] = (row < R && k < r) ? v : u32x4{0u, 0u, 0u, 0u};
-      } else {
-        ea[kk] = u32x4{0u, 0u, 0u, 0u};
-      }
+      const int k = kk * 32 + g * 8;
+      const u32x4 v = *(const u32x4*)(w1 + (int64_t)pv * r + min(k, r - 8));
+      eb[kk] = (row < R && k < r) ? v : u32x4{0u, 0u, 0u, 0u};
     }
   };
 
-  // staging of one tile's W2 rows: piece i of thread t is row (t + i*NT) / 8,
-  // octet (t + i*NT) % 8 of the tile
-  auto stage_load = [&](int t, u32x4* st) {
-    const int64_t tc = tile_col(t);
+  // ---- staging: W2 piece i of thread t is rank row (t + i*NT) / 8, octet
+  //      (t + i*NT) % 8 of the tile; base: the lane's row, columns 16j + 4g
+  struct Set {
+    u32x4 w[STG];
+    f32x4 b[4];
+  };
+  auto load_set = [&](int t, Set& st) {
+    const int64_t tc = tile_col(max(min(t, ntile - 1), 0));
 #pragma unroll
     for (int i = 0; i < STG; ++i) {
       const int pc = threadIdx.x + i * NT;
       const int k = pc >> 3, oc = pc & 7;
       const int64_t col = tc + oc * 8;
       const u32x4 v = *(const u32x4*)(w2 + (int64_t)min(k, r - 1) * V + min(col, (int64_t)V - 8));
-      st[i] = (k < r && col < V) ? v : u32x4{0u, 0u, 0u, 0u};
+      st.w[i] = (k < r && col < V) ? v : u32x4{0u, 0u, 0u, 0u};
     }
+    const float* brow = base + ((int64_t)rowc * gamma + step) * V;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) st.b[j] = *(const f32x4*)(brow + min(tc + 16 * j + 4 * g, (int64_t)V - 4));
   };
-  auto stage_store = [&](unsigned char* bufp, const u32x4* st) {
+  auto store_w2 = [&](unsigned char* bufp, const Set& st) {
 #pragma unroll
     for (int i = 0; i < STG; ++i) {
       const int pc = threadIdx.x + i * NT;
-      const int k = pc >> 3, oc = pc & 7;
-      if (KS * 32 == rpad || k < rpad) *(u32x4*)(bufp + k * kLdsRow + oc * 16) = st[i];
-    }
-  };
-  // base slices of the lane's four rows (4g + i) at columns tile + 4n .. +3
-  auto base_load = [&](int t, f32x4* bs) {
-    const int64_t col = min(tile_col(t) + 4 * n, (int64_t)V - 4);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = min(rowbase + 4 * g + i, R - 1);
-      bs[i] = *(const f32x4*)(base + ((int64_t)row * gamma + step) * V + col);
+      if (KR * 8 % NT == 0 || pc < KR * 8) *(u32x4*)(bufp + (pc >> 3) * kLdsRow + (pc & 7) * 16) = st.w[i];
     }
   };
 
-  float best_z[4];
-  uint32_t best_v[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) { best_z[i] = -INFINITY; best_v[i] = 0xffffffffu; }
+  float best_z = -INFINITY;
+  uint32_t best_v = 0xffffffffu;
 
-  // MFMA over one staged tile, then the fused epilogue
-  auto compute_tile = [&](int t, const unsigned char* cur, const f32x4* bs) {
+  // A operand of product j, rank step kk: the lane (as source of the
+  // transposing read) addresses rank row 32kk + 8g + s/4 (+4 for the second
+  // read) and columns 16j + 4(s mod 4) .. +3, s = lane mod 16; it receives
+  // W2[32kk + 8g + e][16j + s] for e = 0..7.
+  typedef short i16x4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  const uint32_t a_lane = (uint32_t)(8 * g + n / 4) * kLdsRow + 8 * (n % 4);
+  auto compute_tile = [&](int t, const unsigned char* cur, const Set& st) {
     f32x4 acc[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
-      if (kk < ks) {
-        u32x2 raw[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) raw[i] = *(const u32x2*)(cur + (kk * 32 + g * 8 + i) * kLdsRow + n * 8);
-        u32x4 b[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          b[0][q] = pack_lo(raw[2 * q].x, raw[2 * q + 1].x);
-          b[1][q] = pack_hi(raw[2 * q].x, raw[2 * q + 1].x);
-          b[2][q] = pack_lo(raw[2 * q].y, raw[2 * q + 1].y);
-          b[3][q] = pack_hi(raw[2 * q].y, raw[2 * q + 1].y);
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[j] = mfma16x16x32(ea[kk], b[j], acc[j]);
-      }
-    }
-    const int64_t v0 = tile_col(t) + 4 * n;
-    const bool colok = v0 < V;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = rowbase + 4 * g + i;
-      f32x4 l;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) l[j] = acc[j][i] + bs[i][j];
-      if (step_logits && colok && row < R)
-        *(f32x4*)(step_logits + ((int64_t)row * gamma + step) * V + v0) = l;
-      f32x4 z = l;
-      if (!greedy) {
-        const u32x4 x = philox4x32_10(u32x4{(uint32_t)(v0 >> 2), (uint32_t)step, (uint32_t)row, 0u},
-                                      seed_lo, seed_hi);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) z[j] = fmaf(l[j], invT, gumbel_from_bits(x[j]));
-      }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const bool better = colok && z[j] > best_z[i];
-        best_z[i] = better ? z[j] : best_z[i];
-        best_v[i] = better ? (uint32_t)(v0 + j) : best_v[i];
+        const unsigned char* ap = cur + a_lane + kk * 32 * kLdsRow + 32 * j;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)ap);
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(ap + 4 * kLdsRow));
+        const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+        acc[j] = mfma16x16x32(u32x4{l2.x, l2.y, h2.x, h2.y}, eb[kk], acc[j]);
+      }
+    }
+    // epilogue: lane owns row `row`, columns v0 + 16j .. +3
+    const int64_t v0 = tile_col(t) + 4 * g;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t vj = v0 + 16 * j;
+      const bool colok = t < ntile && vj < V;
+      const f32x4 l = acc[j] + st.b[j];
+      if (step_logits && colok && row < R)
+        *(f32x4*)(step_logits + ((int64_t)row * gamma + step) * V + vj) = l;
+      f32x4 z = l;
+      if (!greedy) {
+        const u32x4 x = philox4x32_10(u32x4{(uint32_t)(vj >> 2), (uint32_t)step, (uint32_t)row, 0u},
+                                      seed_lo, seed_hi);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) z[e] = fmaf(l[e], invT, gumbel_from_bits(x[e]));
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool better = colok && z[e] > best_z;
+        best_z = better ? z[e] : best_z;
+        best_v = better ? (uint32_t)(vj + e) : best_v;
       }
     }
   };
 
-  // Two tiles in flight: staging set A/B alternate, LDS buffers 0/1 alternate.
-  u32x4 stA[STG], stB[STG];
-  f32x4 bA[4], bB[4], bs[4];
-  // the first two tiles do not depend on the previous step's tokens: their
-  // loads go out before the dependent key -> W1 row gather
-  if (ntile > 0) {
-    stage_load(0, stA);
-    base_load(0, bA);
-    stage_load(min(1, ntile - 1), stB);
-    base_load(min(1, ntile - 1), bB);
-  }
-  gather_e();
-  if (ntile > 0) {
-    stage_store(buf0, stA);
+  // prologue: tile 0's loads, then the dependent chain (previous keys, then
+  // the W1 rows they select), then the other sets: tile 0 arrives while the
+  // chain runs and the chain's reads do not queue behind the bulk prefetch
+  Set sets[NS];
+  load_set(0, sets[0]);
+  const int pv = decode_prev(keys_prev, first_prev, rowc, R, V,
+                             blockIdx.x == 0 && g == 0 && row < R ? status : nullptr);
+  gather_e(pv);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) bs[i] = bA[i];
-  }
+  for (int q = 1; q < NS; ++q) load_set(q, sets[q]);
+  store_w2(smem, sets[0]);
   __syncthreads();
-  for (int t = 0; t < ntile; t += 2) {
-    stage_load(min(t + 2, ntile - 1), stA);
-    base_load(min(t + 2, ntile - 1), bA);
-    compute_tile(t, buf0, bs);
-    stage_store(buf1, stB);
+  // iteration t: compute tile t (LDS buffer t & 1, base from its set), load
+  // tile t + NS into that set, move tile t + 1's W2 into the other buffer
+  // (unrolled by NS so every set has fixed registers)
+  for (int t0 = 0; t0 < ntile; t0 += NS) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) bs[i] = bB[i];
-    __syncthreads();
-    if (t + 1 >= ntile) break;
-    stage_load(min(t + 3, ntile - 1), stB);
-    base_load(min(t + 3, ntile - 1), bB);
-    compute_tile(t + 1, buf1, bs);
-    stage_store(buf0, stA);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) bs[i] = bA[i];
-    __syncthreads();
+    for (int q = 0; q < NS; ++q) {
+      const int t = t0 + q;
+      if (t >= ntile) break;
+      compute_tile(t, smem + (t & 1) * kBuf, sets[q]);
+      load_set(t + NS, sets[q]);
+      store_w2(smem + ((t + 1) & 1) * kBuf, sets[(q + 1) % NS]);
+      __syncthreads();
+    }
   }
 
-  // ---- fold: the 16 lanes sharing a row, then the grid
+  // ---- fold: the 4 lanes sharing a row, then the grid
+  uint64_t key = best_v == 0xffffffffu ? 0ull : argmax_key(best_z, best_v);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    uint64_t key = best_v[i] == 0xffffffffu ? 0ull : argmax_key(best_z[i], best_v[i]);
-#pragma unroll
-    for (int m = 1; m < 16; m <<= 1) {
-      const uint64_t o = shfl_xor_u64(key, m);
-      key = o > key ? o : key;
-    }
-    const int row = rowbase + 4 * g + i;
-    if (n == 0 && key && row < R) fold_key_global(keys_out, row, R, key);
+  for (int m = 16; m < 64; m <<= 1) {
+    const uint64_t o = shfl_xor_u64(key, m);
+    key = o > key ? o : key;
   }
+  if (g == 0 && key && row < R) fold_key_global(keys_out, row, R, key);
 }
 
 // ------------------------------------------------------------- vector path
@@ -403,14 +385,14 @@ hipError_t allow_lds_once(K kern, size_t bytes) {
   return e;
 }
 
-template <int NW, int KS>
+template <int NW, int KS, int NS>
 hipError_t launch_mfma(int grid_x, int grid_y, hipStream_t s, const float* base, const uint16_t* w1,
                        const uint16_t* w2, const int32_t* first_prev, const uint64_t* kp,
                        uint64_t* ko, float* step_logits, int R, int gamma, int V, int r, int step,
                        float invT, int greedy, uint32_t slo, uint32_t shi, int32_t* st) {
-  const int rpad = ((r + 31) / 32) * 32;
-  const size_t shm = (size_t)2 * rpad * kLdsRow;
-  auto kern = markov_step_mfma<NW, KS>;
+  (void)r;
+  const size_t shm = (size_t)2 * 32 * KS * kLdsRow;
+  auto kern = markov_step_mfma<NW, KS, NS>;
   hipError_t e = allow_lds_once(kern, shm);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(grid_x, grid_y), dim3(64 * NW), shm, s, base, w1, w2, first_prev,
@@ -476,11 +458,11 @@ extern "C" int dspark_markov_sample(const float* base_logits, const void* w1, co
       if (gx > tiles) gx = (int)tiles;
       if (gx < 1) gx = 1;
       if (wide)
-        e = r <= 256 ? launch_mfma<8, 8>(gx, gy, s, base_logits, (const uint16_t*)w1, (const uint16_t*)w2, first_prev, kp, ko, step_logits, R, gamma, V, r, step, invT, greedy, slo, shi, dev_status)
-                     : launch_mfma<8, 16>(gx, gy, s, base_logits, (const uint16_t*)w1, (const uint16_t*)w2, first_prev, kp, ko, step_logits, R, gamma, V, r, step, invT, greedy, slo, shi, dev_status);
+        e = r <= 256 ? launch_mfma<8, 8, 3>(gx, gy, s, base_logits, (const uint16_t*)w1, (const uint16_t*)w2, first_prev, kp, ko, step_logits, R, gamma, V, r, step, invT, greedy, slo, shi, dev_status)
+                     : launch_mfma<8, 16, 2>(gx, gy, s, base_logits, (const uint16_t*)w1, (const uint16_t*)w2, first_prev, kp, ko, step_logits, R, gamma, V, r, step, invT, greedy, slo, shi, dev_status);
       else
-        e = r <= 256 ? launch_mfma<4, 8>(gx, gy, s, base_logits, (const uint16_t*)w1, (const uint16_t*)w2, first_prev, kp, ko, step_logits, R, gamma, V, r, step, invT, greedy, slo, shi, dev_status)
-                     : launch_mfma<4, 16>(gx, gy, s, base_logits, (const uint16_t*)w1, (const uint16_t*)w2, first_prev, kp, ko, step_logits, R, gamma, V, r, step, invT, greedy, slo, shi, dev_status);
+        e = r <= 256 ? launch_mfma<4, 8, 2>(gx, gy, s, base_logits, (const uint16_t*)w1, (const uint16_t*)w2, first_prev, kp, ko, step_logits, R, gamma, V, r, step, invT, greedy, slo, shi, dev_status)
+                     : launch_mfma<4, 16, 2>(gx, gy, s, base_logits, (const uint16_t*)w1, (const uint16_t*)w2, first_prev, kp, ko, step_logits, R, gamma, V, r, step, invT, greedy, slo, shi, dev_status);
     } else {
       const int gy = (R + kRowChunk - 1) / kRowChunk;
       int gx = 2 * cus;
