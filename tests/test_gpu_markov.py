@@ -58,6 +58,8 @@ def test_config1_fp32(dsp):
     (20, 4, 2048, 512, 0.0),      # rank 512
     (9, 3, 1001, 40, 1.3),        # V not a multiple of 8: vector-ALU path, bf16 weights
     (64, 2, 4104, 72, 0.5),       # rank not a multiple of 32: zero-padded rank step
+    (37, 3, 16384, 256, 0.0),     # one launch for all steps (resident W2), ragged row blocks
+    (37, 3, 16384, 256, 0.9),     # the same with Gumbel noise
 ])
 def test_bf16_variants(dsp, R, G, V, r, T):
     mk = W.markov_case(R * 1000 + V, R, G, V, r, "bf16", base_std=2.0, w1_std=1.0,
