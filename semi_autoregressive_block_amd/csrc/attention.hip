@@ -47,6 +47,7 @@ namespace {
 
 constexpr int kTileRows = 64;  // rows per tile of the streaming kernel and of the workspace
 constexpr int kPlanBins = 4096;  // cost buckets of the planner's counting sort
+constexpr int kPlanCache = 16384;  // (request, tile) pairs whose bins the planner keeps in LDS
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.69314718055994531f;
 
@@ -83,8 +84,10 @@ __device__ __forceinline__ void ctx_range(const Params& p, int b, int& c0, int& 
 }
 
 __device__ __forceinline__ int visible_ctx(const Params& p, int b, int a, int S, bool flag) {
-  if (!p.keep[(int64_t)b * p.A + a]) return -1;  // masked block
+  // both loads go out together (one round trip, not two)
+  const uint8_t kp = p.keep[(int64_t)b * p.A + a];
   const int an = p.anchor[(int64_t)b * p.A + a];
+  if (!kp) return -1;  // masked block
   if (flag && (an < 0 || an > S)) status_or(p.status, DSPARK_STATUS_BAD_ANCHOR);
   return clampi(an, 0, S);
 }
@@ -216,9 +219,20 @@ __device__ __forceinline__ int tile_cost(const Params& p, int b, int tile, int& 
   a_hi = min(p.A - 1, (u0 + p.tile_rows - 1) / rpb);
   L = 0;
   any_kept = false;
-  for (int a = a_lo; a <= a_hi; ++a) {
-    const int v = visible_ctx(p, b, a, S, false);
-    if (v >= 0) { any_kept = true; L = max(L, v); }
+  // four blocks' keep flags and anchors per round trip
+  const int64_t r0 = (int64_t)b * p.A;
+  for (int a0 = a_lo; a0 <= a_hi; a0 += 4) {
+    uint8_t kp[4];
+    int an[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int a = min(a0 + j, a_hi);
+      kp[j] = p.keep[r0 + a];
+      an[j] = p.anchor[r0 + a];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (a0 + j <= a_hi && kp[j]) { any_kept = true; L = max(L, clampi(an[j], 0, S)); }
   }
   const int n_own = (a_hi - a_lo + 1) * p.gamma;
   return any_kept ? (L + 31) / 32 + (n_own + 31) / 32 : 0;
@@ -230,29 +244,37 @@ __device__ __forceinline__ int tile_cost(const Params& p, int b, int tile, int& 
 // on the order, only the schedule does).
 __global__ __launch_bounds__(1024) void attn_plan_kernel(Params p, int32_t* __restrict__ order) {
   __shared__ int hist[kPlanBins];
-  __shared__ int part[1024];
+  __shared__ int wsum[16];
+  __shared__ uint16_t cached[kPlanCache];  // bin of pair q (when npairs <= kPlanCache)
   const int npairs = p.B * p.ntiles;
+  const bool cache = npairs <= kPlanCache;
   for (int i = threadIdx.x; i < kPlanBins; i += 1024) hist[i] = 0;
   __syncthreads();
   for (int q = threadIdx.x; q < npairs; q += 1024) {
     int L, a_lo, a_hi;
     bool any;
-    const int cost = tile_cost(p, q % p.B, q / p.B, L, a_lo, a_hi, any);
-    atomicAdd(&hist[min(cost, kPlanBins - 1)], 1);
+    const int bin = min(tile_cost(p, q % p.B, q / p.B, L, a_lo, a_hi, any), kPlanBins - 1);
+    if (cache) cached[q] = (uint16_t)bin;
+    atomicAdd(&hist[bin], 1);
   }
   __syncthreads();
-  // exclusive scan in descending bin order: thread t owns bins 4095-4t .. 4092-4t
+  // exclusive scan in descending bin order: thread t owns bins 4095-4t ..
+  // 4092-4t; wave prefix sums, then the 16 wave totals
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int local = 0;
 #pragma unroll
   for (int k = 0; k < 4; ++k) local += hist[kPlanBins - 1 - 4 * threadIdx.x - k];
-  part[threadIdx.x] = local;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int run = 0;
-    for (int t = 0; t < 1024; ++t) { const int v = part[t]; part[t] = run; run += v; }
+  int incl = local;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += y;
   }
+  if (lane == 63) wsum[wave] = incl;
   __syncthreads();
-  int run = part[threadIdx.x];
+  int before = 0;
+  for (int w = 0; w < wave; ++w) before += wsum[w];
+  int run = before + incl - local;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int bin = kPlanBins - 1 - 4 * threadIdx.x - k;
@@ -262,10 +284,15 @@ __global__ __launch_bounds__(1024) void attn_plan_kernel(Params p, int32_t* __re
   }
   __syncthreads();
   for (int q = threadIdx.x; q < npairs; q += 1024) {
-    int L, a_lo, a_hi;
-    bool any;
-    const int cost = tile_cost(p, q % p.B, q / p.B, L, a_lo, a_hi, any);
-    const int pos = atomicAdd(&hist[min(cost, kPlanBins - 1)], 1);
+    int bin;
+    if (cache) {
+      bin = cached[q];
+    } else {
+      int L, a_lo, a_hi;
+      bool any;
+      bin = min(tile_cost(p, q % p.B, q / p.B, L, a_lo, a_hi, any), kPlanBins - 1);
+    }
+    const int pos = atomicAdd(&hist[bin], 1);
     const int b = q % p.B, tile = q / p.B;
     for (int kvh = 0; kvh < p.Hkv; ++kvh)
       order[(int64_t)pos * p.Hkv + kvh] = ((tile * p.B) + b) * p.Hkv + kvh;
