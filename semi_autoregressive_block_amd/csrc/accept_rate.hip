@@ -383,22 +383,40 @@ __global__ __launch_bounds__(kThreads) void tv_cluster_kernel(
 
 // accept[row] = clamp(sum_g share[row][g], 0, 1) in fixed order, and tau per
 // block of gamma rows (page 1 §3.10); one thread per block.
+// One thread per row: the row's G shares in a fixed order (four independent
+// partial sums, so the loads go out together; results are deterministic),
+// clamped.  When gamma divides the wave width, a block's rows sit in gamma
+// consecutive lanes and tau = 1 + sum_k prod_{i<=k} a_i m_i is a segmented
+// prefix product and sum over them; otherwise tau_kernel runs afterwards.
 __global__ void tv_finalize_kernel(const float* __restrict__ share, int G,
                                    float* __restrict__ accept, const uint8_t* __restrict__ m,
-                                   float* __restrict__ tau, int64_t nblocks, int gamma) {
-  const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (b >= nblocks) return;
-  float run = 1.f, s = 0.f;
-  for (int k = 0; k < gamma; ++k) {
-    const int64_t row = b * gamma + k;
-    float a = 0.f;
-    for (int j = 0; j < G; ++j) a += share[row * G + j];
-    a = fminf(fmaxf(a, 0.f), 1.f);
+                                   float* __restrict__ tau, int64_t rows, int gamma) {
+  const int64_t row = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  float a = 0.f;
+  if (row < rows) {
+    const float* sp = share + row * G;
+    float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+    int j = 0;
+    for (; j + 4 <= G; j += 4) {
+      s0 += sp[j];
+      s1 += sp[j + 1];
+      s2 += sp[j + 2];
+      s3 += sp[j + 3];
+    }
+    for (; j < G; ++j) s0 += sp[j];
+    a = fminf(fmaxf((s0 + s1) + (s2 + s3), 0.f), 1.f);
     accept[row] = a;
-    run *= a * (m ? (float)(m[row] != 0) : 1.f);
-    s += run;
   }
-  if (tau) tau[b] = 1.f + s;
+  if (!tau || kWave % gamma != 0) return;
+  const int k = (int)(threadIdx.x % gamma);  // rows of a block are consecutive lanes
+  float run = (row < rows) ? a * (m ? (float)(m[row] != 0) : 1.f) : 0.f;
+  for (int off = 1; off < gamma; off <<= 1) {
+    const float y = __shfl_up(run, off, kWave);
+    if (k >= off) run *= y;
+  }
+  float sum = run;
+  for (int off = gamma >> 1; off > 0; off >>= 1) sum += __shfl_xor(sum, off, kWave);
+  if (k == 0 && row < rows) tau[row / gamma] = 1.f + sum;
 }
 
 __global__ void zero_u32_kernel(unsigned* p, int n) {
@@ -599,8 +617,11 @@ extern "C" int dspark_accept_rate(const void* draft_logits, const void* target_l
                                               args, 0, s);
     if (e != hipSuccess)
       return fail(DSPARK_ERR_HIP, "accept_rate: cooperative launch: %s", hipGetErrorString(e));
-    hipLaunchKernelGGL(tv_finalize_kernel, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, s,
-                       (const float*)share, G, accept, eval_mask, tau, nb, gamma);
+    hipLaunchKernelGGL(tv_finalize_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s,
+                       (const float*)share, G, accept, eval_mask, tau, rows, gamma);
+    if (tau && kWave % gamma != 0)
+      hipLaunchKernelGGL(tau_kernel, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, s, accept,
+                         eval_mask, tau, nb, gamma);
   } else {
     int64_t grid = rows < 65536 ? rows : 65536;
     if (bf)
