@@ -37,7 +37,9 @@
 //   O^T = V^T P^T straight from the S^T accumulator layout (no transpose of
 //   P); V^T operands come from transposing LDS reads.
 // * K/V staging: pairs of slabs (one per parity) go global -> registers ->
-//   a two-slot LDS ring, with two register sets of loads in flight; parities
+//   a two-slot LDS ring, with two register sets of loads in flight (64-row
+//   tiles); for 128-row tiles they go straight from global memory into a
+//   four-slot LDS ring (direct LDS loads, three pairs in flight).  Parities
 //   merge through LDS at the end.
 #include "common.h"
 
@@ -414,17 +416,72 @@ struct SlabView {
   }
 };
 
+// K/V staging straight from global memory into LDS (global_load_lds_dwordx4,
+// no register round trip): one instruction moves 64 lanes x 16 bytes into
+// 1 KB of LDS, lane l to chunk base + l, so each lane fetches the piece
+// that the K or V swizzle puts at that chunk.  A ring slot holds one pair:
+// K of both parities, then V of both parities.  The compiler does not
+// order these LDS writes against LDS reads: the consumer waits for its own
+// copies with an explicit vmcnt and then meets the other waves at a plain
+// s_barrier (no fence, which would wait for every copy in flight).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  // gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[15:14]
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+__device__ __forceinline__ void block_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int D, int NT>
+struct DmaPair {
+  using Rg = Ring<D>;
+  static constexpr int P = Rg::kPieces;
+  static constexpr int kInst = Rg::kSlotBytes / 1024;  // 1 KB copies per half (K or V) of a pair
+  static constexpr int kPerWave = kInst / (NT / 64);
+  static constexpr int kPerPair = 2 * kPerWave;         // copies per wave per pair
+  static_assert(kInst % (NT / 64) == 0 && (32 * P) % 64 == 0, "copy layout");
+  __device__ static void issue(const Stager<D, NT>& st, int pair, unsigned char* slot, int wave, int lane) {
+#pragma unroll
+    for (int hv = 0; hv < 2; ++hv)
+#pragma unroll
+      for (int j = 0; j < kPerWave; ++j) {
+        const int inst = wave * kPerWave + j;     // wave-uniform
+        const int q = (inst * 64) / (32 * P);     // slab parity of this copy
+        const int cc = (inst * 64) % (32 * P) + lane;  // chunk within the slab
+        const int key = cc / P;
+        const int piece = (cc % P) ^ (hv ? 4 * (key % (P / 4)) : key % P);
+        const int s = min(2 * pair + q, st.nslab - 1);
+        const bool own = s >= st.n_ctx_slabs;
+        const int k0 = own ? (s - st.n_ctx_slabs) * 32 : s * 32;
+        const int nvalid = (own ? st.own_keys : st.ctx_keys) - k0;
+        const unsigned char* src = hv ? (own ? st.vb : st.vc) : (own ? st.kb : st.kc);
+        src += ((own ? st.own_row0 : st.ctx_row0) + k0) * (int64_t)st.row_b + st.head_b;
+        const uint32_t off = __umul24((uint32_t)min(key, nvalid - 1), st.row_b) + piece * 16;
+        __builtin_amdgcn_global_load_lds((const void*)(src + off),
+                                         (__attribute__((address_space(3))) void*)(slot + hv * Rg::kSlotBytes + inst * 1024),
+                                         16, 0, 0);
+      }
+  }
+};
+
 // One workgroup per tile of 32*RG query rows and one (request, KV head):
-// RG row groups x two key parities, one wave each.  NSETS register sets of
-// K/V loads are in flight while a pair is computed.
-template <int D, int NSETS, int RG>
+// RG row groups x two key parities, one wave each.  NSLOT == 0: NSETS
+// register sets of K/V loads are in flight while a pair is computed (two
+// LDS slots); NSLOT > 0: direct-to-LDS copies into an NSLOT-slot ring, the
+// next NSLOT - 1 pairs in flight.
+template <int D, int NSETS, int RG, int NSLOT>
 __global__ __launch_bounds__(64 * 2 * RG) __attribute__((amdgpu_waves_per_eu(2, 2))) void block_attn_mfma(Params p) {
   using Rg = Ring<D>;
   constexpr int NJ = D / 32;
   constexpr int KK = D / 16;
   constexpr int NT = 64 * 2 * RG;  // RG row groups x two key parities, one wave each
   constexpr int kMergeBytes = RG * (D + 2) * 32 * 4;
-  __shared__ __align__(16) unsigned char ring[Rg::kBytes > kMergeBytes ? Rg::kBytes : kMergeBytes];
+  constexpr int kRingBytes = NSLOT > 0 ? NSLOT * 2 * Rg::kSlotBytes : Rg::kBytes;
+  __shared__ __align__(16) unsigned char ring[kRingBytes > kMergeBytes ? kRingBytes : kMergeBytes];
 
   // the work item is the same for the whole workgroup: keep it in scalars
   int wid = __builtin_amdgcn_readfirstlane(p.order ? p.order[blockIdx.x] : (int)blockIdx.x);
@@ -515,6 +572,33 @@ __global__ __launch_bounds__(64 * 2 * RG) __attribute__((amdgpu_waves_per_eu(2, 
                        Rg::v_slot(ring, iv) + par * Rg::kTensorBytes, h, r32);
   };
   constexpr int N = Stager<D, NT>::N;
+  if constexpr (NSLOT > 0) {
+    // ---- pair i is computed from slot i mod NSLOT while pairs i+1 ..
+    //      i+NSLOT-1 are being copied in.  Iteration i: wait for this wave's
+    //      copies of pair i, meet the other waves (their copies of pair i
+    //      are in, and they are done with pair i-1, whose slot is refilled
+    //      next), issue pair i+NSLOT-1, compute pair i.  Copies past the end
+    //      repeat the last slab (from L2), so the count is exact.
+    using Dp = DmaPair<D, NT>;
+    auto dslot = [&](int i) { return ring + (i % NSLOT) * 2 * Rg::kSlotBytes; };
+    auto dview = [&](int i) {
+      unsigned char* sl = dslot(i);
+      return SlabView<D>(sl + par * Rg::kTensorBytes, sl + Rg::kSlotBytes + par * Rg::kTensorBytes, h, r32);
+    };
+    if (npairs > 0) {
+#pragma unroll
+      for (int q = 0; q < NSLOT - 1; ++q) Dp::issue(st, q, dslot(q), wave, lane);
+      for (int i = 0; i < npairs; ++i) {
+        wait_vmcnt<Dp::kPerPair * (NSLOT - 2)>();
+        block_barrier();
+        Dp::issue(st, i + NSLOT - 1, dslot(i + NSLOT - 1), wave, lane);
+        const int s = 2 * i + par;
+        if (s < nslab) compute_slab<D>(p, it, s, dview(i), qf, kept, lim, ua, a_lo, c, m, l, o);
+      }
+      wait_vmcnt<0>();
+      block_barrier();  // every copy has landed and every wave is done with the ring
+    }
+  } else {
   // ---- pair i is computed from ring slot i & 1 while pair i + 1 goes from
   //      registers into the other slot and pairs i + 2 .. i + NSETS are in
   //      flight in the register sets (the loop is unrolled by NSETS so each
@@ -550,6 +634,7 @@ __global__ __launch_bounds__(64 * 2 * RG) __attribute__((amdgpu_waves_per_eu(2, 
         __syncthreads();
       }
     }
+  }
   }
 
   // ---- merge the two key parities of each row group through LDS (the ring
@@ -752,11 +837,11 @@ extern "C" int dspark_block_attention(const void* q, const void* k_ctx, const vo
     p.order = order;
     const dim3 grid((unsigned)sh.tiles), block(deep ? 256 : 512);
     if (D == 128) {
-      if (deep) hipLaunchKernelGGL((block_attn_mfma<128, 2, 2>), grid, block, 0, s, p);
-      else hipLaunchKernelGGL((block_attn_mfma<128, 2, 4>), grid, block, 0, s, p);
+      if (deep) hipLaunchKernelGGL((block_attn_mfma<128, 2, 2, 0>), grid, block, 0, s, p);
+      else hipLaunchKernelGGL((block_attn_mfma<128, 2, 4, 4>), grid, block, 0, s, p);
     } else {
-      if (deep) hipLaunchKernelGGL((block_attn_mfma<64, 2, 2>), grid, block, 0, s, p);
-      else hipLaunchKernelGGL((block_attn_mfma<64, 2, 4>), grid, block, 0, s, p);
+      if (deep) hipLaunchKernelGGL((block_attn_mfma<64, 2, 2, 0>), grid, block, 0, s, p);
+      else hipLaunchKernelGGL((block_attn_mfma<64, 2, 4, 4>), grid, block, 0, s, p);
     }
   } else {
     const int64_t nb = (int64_t)B * A * Hq;
