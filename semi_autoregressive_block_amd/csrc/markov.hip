@@ -7,24 +7,21 @@
 // the token forward.  Each step is one kernel launch:
 //
 // * The rank-r x V product is an MFMA contraction over the rank (bf16 in,
-//   fp32 accumulate, v_mfma_f32_16x16x32_bf16).  W2 is stored [r, V] with the
-//   vocabulary contiguous, so each lane loads an 8 (rank) x 4 (vocab) bf16
-//   block with 8-byte coalesced loads and transposes it in registers
-//   (v_perm); MFMA column slot n of product j then stands for vocabulary
-//   index tile + 4n + j.  E = W1[prev] (the A operand) is gathered once per
-//   step into LDS and shared by the workgroup's four waves.
-// * Every wave owns a balanced contiguous vocabulary range (the step streams
-//   W2 exactly once), all rows of its row group, and keeps a running
-//   (value, index) best per row in registers: the base add, the optional
+//   fp32 accumulate, v_mfma_f32_16x16x32_bf16), computed transposed so that
+//   each lane owns one row and four columns per 16-column product; W2 tiles
+//   are staged in LDS and read with the transposing LDS read, E = W1[prev]
+//   stays in registers.
+// * 64-column tiles are handed out interleaved over the workgroups (the step
+//   streams W2 and its base slice exactly once); the base add, the optional
 //   step-logit store, the Philox Gumbel perturbation and the argmax are fused
-//   into the epilogue of each 64-column sub-tile.
+//   into each tile's epilogue, with a running (value, index) best per row.
 // * Row maxima are folded with 64-bit keys (order-preserving float bits,
-//   then the inverted index so ties go to the lowest index): 16-lane
-//   shuffles, then one device-scope atomic max per row and workgroup into
-//   one of 16 replica slots of the row (memory-side atomics on one address
-//   serialise; replicas spread them).  The next step decodes prev from the
-//   maximum over the replicas on the device; there is no host round trip
-//   inside the gamma loop.
+//   then the inverted index so ties go to the lowest index): shuffles, then
+//   one device-scope atomic max per row and workgroup into one of 16 replica
+//   slots of the row (memory-side atomics on one address serialise; replicas
+//   spread them).  The next step decodes prev from the maximum over the
+//   replicas on the device; there is no host round trip inside the gamma
+//   loop.
 #include <atomic>
 #include <map>
 #include <mutex>
@@ -102,15 +99,19 @@ __device__ __forceinline__ void fold_key_global(uint64_t* keys, int row, int R, 
 // Loads: NS register sets hold tiles t .. t+NS-1 (W2 pieces and the lane's
 // base logits).  Iteration t computes tile t from LDS, issues tile t + NS's
 // loads into the freed set and moves tile t + 1's W2 into the other LDS
-// buffer, so every load has about NS - 1 iterations to arrive.  Every global
-// load is unconditional from a clamped, always-valid address (invalid lanes
-// are zeroed after the load).  The step's dependent reads (the previous
-// step's keys, then the W1 rows they select) go out before the tile loads,
-// so they do not queue behind them.
+// buffer.  A compute unit accepts only a few tens of KB of outstanding loads
+// and a wave stalls at a load it cannot issue, so more sets mostly delay the
+// first tile; two sets are used for 128-row workgroups.  Every global load is
+// unconditional from a clamped, always-valid address (invalid lanes are
+// zeroed after the load).  With FL the base logits are fetched as whole
+// 128-byte lines (the request count, not only the bytes, bounds a compute
+// unit's streaming rate) and regathered into the MFMA layout through LDS.
+// The step's dependent reads (the previous step's keys, then the W1 rows
+// they select) go out right after tile 0, ahead of the other tiles.
 constexpr int kTileCols = 64;
 constexpr int kLdsRow = 144;  // bytes per staged W2 row of a tile (128 + 16: spreads LDS banks)
 
-template <int NW, int KS, int NS>
+template <int NW, int KS, int NS, bool FL>
 __global__ __launch_bounds__(64 * NW) void markov_step_mfma(
     const float* __restrict__ base, const uint16_t* __restrict__ w1,
     const uint16_t* __restrict__ w2, const int32_t* __restrict__ first_prev,
@@ -159,9 +160,19 @@ __global__ __launch_bounds__(64 * NW) void markov_step_mfma(
       const u32x4 v = *(const u32x4*)(w2 + (int64_t)min(k, r - 1) * V + min(col, (int64_t)V - 8));
       st.w[i] = (k < r && col < V) ? v : u32x4{0u, 0u, 0u, 0u};
     }
-    const float* brow = base + ((int64_t)rowc * gamma + step) * V;
+    if constexpr (FL) {
+      // whole 128-byte lines: load j covers rows 4j + lane/16 of the wave's 16,
+      // 16-byte chunk lane % 16 of the tile's 256 bytes per row
 #pragma unroll
-    for (int j = 0; j < 4; ++j) st.b[j] = *(const f32x4*)(brow + min(tc + 16 * j + 4 * g, (int64_t)V - 4));
+      for (int j = 0; j < 4; ++j) {
+        const int rj = min(blockIdx.y * 16 * NW + wave * 16 + 4 * j + (lane >> 4), R - 1);
+        st.b[j] = *(const f32x4*)(base + ((int64_t)rj * gamma + step) * V + min(tc + 4 * (lane & 15), (int64_t)V - 4));
+      }
+    } else {
+      const float* brow = base + ((int64_t)rowc * gamma + step) * V;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) st.b[j] = *(const f32x4*)(brow + min(tc + 16 * j + 4 * g, (int64_t)V - 4));
+    }
   };
   auto store_w2 = [&](unsigned char* bufp, const Set& st) {
 #pragma unroll
@@ -181,7 +192,30 @@ __global__ __launch_bounds__(64 * NW) void markov_step_mfma(
   typedef short i16x4 __attribute__((ext_vector_type(4)));
   typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
   const uint32_t a_lane = (uint32_t)(8 * g + n / 4) * kLdsRow + 8 * (n % 4);
+  // FL: the lane's base logits (row n, columns 16j + 4g .. +3) arrive spread
+  // over the wave and are regathered through the wave's own 4 KB of LDS (row
+  // q, 16-byte chunk c stored at chunk c ^ q: both passes conflict-free)
+  unsigned char* const wave_lds = smem + 2 * kBuf + wave * 4096;
+  auto regather = [&](const Set& in, f32x4* b) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int q = 4 * j + (lane >> 4), c = lane & 15;
+      *(f32x4*)(wave_lds + q * 256 + ((c ^ q) << 4)) = in.b[j];
+    }
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_wave_barrier();
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int j = 0; j < 4; ++j) b[j] = *(const f32x4*)(wave_lds + n * 256 + (((4 * j + g) ^ n) << 4));
+  };
   auto compute_tile = [&](int t, const unsigned char* cur, const Set& st) {
+    f32x4 bl[4];
+    if constexpr (FL) {
+      regather(st, bl);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bl[j] = st.b[j];
+    }
     f32x4 acc[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -202,7 +236,7 @@ __global__ __launch_bounds__(64 * NW) void markov_step_mfma(
     for (int j = 0; j < 4; ++j) {
       const int64_t vj = v0 + 16 * j;
       const bool colok = t < ntile && vj < V;
-      const f32x4 l = acc[j] + st.b[j];
+      const f32x4 l = acc[j] + bl[j];
       if (step_logits && colok && row < R)
         *(f32x4*)(step_logits + ((int64_t)row * gamma + step) * V + vj) = l;
       f32x4 z = l;
@@ -385,14 +419,14 @@ hipError_t allow_lds_once(K kern, size_t bytes) {
   return e;
 }
 
-template <int NW, int KS, int NS>
+template <int NW, int KS, int NS, bool FL>
 hipError_t launch_mfma(int grid_x, int grid_y, hipStream_t s, const float* base, const uint16_t* w1,
                        const uint16_t* w2, const int32_t* first_prev, const uint64_t* kp,
                        uint64_t* ko, float* step_logits, int R, int gamma, int V, int r, int step,
                        float invT, int greedy, uint32_t slo, uint32_t shi, int32_t* st) {
   (void)r;
-  const size_t shm = (size_t)2 * 32 * KS * kLdsRow;
-  auto kern = markov_step_mfma<NW, KS, NS>;
+  const size_t shm = (size_t)2 * 32 * KS * kLdsRow + (FL ? (size_t)NW * 4096 : 0);
+  auto kern = markov_step_mfma<NW, KS, NS, FL>;
   hipError_t e = allow_lds_once(kern, shm);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(grid_x, grid_y), dim3(64 * NW), shm, s, base, w1, w2, first_prev,
@@ -458,11 +492,11 @@ extern "C" int dspark_markov_sample(const float* base_logits, const void* w1, co
       if (gx > tiles) gx = (int)tiles;
       if (gx < 1) gx = 1;
       if (wide)
-        e = r <= 256 ? launch_mfma<8, 8, 3>(gx, gy, s, base_logits, (const uint16_t*)w1, (const uint16_t*)w2, first_prev, kp, ko, step_logits, R, gamma, V, r, step, invT, greedy, slo, shi, dev_status)
-                     : launch_mfma<8, 16, 2>(gx, gy, s, base_logits, (const uint16_t*)w1, (const uint16_t*)w2, first_prev, kp, ko, step_logits, R, gamma, V, r, step, invT, greedy, slo, shi, dev_status);
+        e = r <= 256 ? launch_mfma<8, 8, 2, true>(gx, gy, s, base_logits, (const uint16_t*)w1, (const uint16_t*)w2, first_prev, kp, ko, step_logits, R, gamma, V, r, step, invT, greedy, slo, shi, dev_status)
+                     : launch_mfma<8, 16, 2, false>(gx, gy, s, base_logits, (const uint16_t*)w1, (const uint16_t*)w2, first_prev, kp, ko, step_logits, R, gamma, V, r, step, invT, greedy, slo, shi, dev_status);
       else
-        e = r <= 256 ? launch_mfma<4, 8, 2>(gx, gy, s, base_logits, (const uint16_t*)w1, (const uint16_t*)w2, first_prev, kp, ko, step_logits, R, gamma, V, r, step, invT, greedy, slo, shi, dev_status)
-                     : launch_mfma<4, 16, 2>(gx, gy, s, base_logits, (const uint16_t*)w1, (const uint16_t*)w2, first_prev, kp, ko, step_logits, R, gamma, V, r, step, invT, greedy, slo, shi, dev_status);
+        e = r <= 256 ? launch_mfma<4, 8, 2, false>(gx, gy, s, base_logits, (const uint16_t*)w1, (const uint16_t*)w2, first_prev, kp, ko, step_logits, R, gamma, V, r, step, invT, greedy, slo, shi, dev_status)
+                     : launch_mfma<4, 16, 2, false>(gx, gy, s, base_logits, (const uint16_t*)w1, (const uint16_t*)w2, first_prev, kp, ko, step_logits, R, gamma, V, r, step, invT, greedy, slo, shi, dev_status);
     } else {
       const int gy = (R + kRowChunk - 1) / kRowChunk;
       int gx = 2 * cus;
