@@ -424,18 +424,6 @@ struct SlabView {
 // order these LDS writes against LDS reads: the consumer waits for its own
 // copies with an explicit vmcnt and then meets the other waves at a plain
 // s_barrier (no fence, which would wait for every copy in flight).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  // gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[15:14]
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-__device__ __forceinline__ void block_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
 template <int D, int NT>
 struct DmaPair {
   using Rg = Ring<D>;

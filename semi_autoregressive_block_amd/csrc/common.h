@@ -89,6 +89,23 @@ __device__ __forceinline__ void status_or(int32_t* st, int32_t bits) {
   if (st) atomicOr(st, bits);
 }
 
+// Wait until at most N of this wave's vector memory operations are pending
+// (they complete in issue order).  Needed for global -> LDS copies, which the
+// compiler does not track against later LDS reads.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  // gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[15:14]
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+// Workgroup barrier without the waits __syncthreads() adds: the caller has
+// made its own writes visible (wait_vmcnt for copies into LDS).
+__device__ __forceinline__ void block_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 }  // namespace dspark
 
 // ---------------------------------------------------------------- host side

@@ -58,8 +58,13 @@ def test_config1_fp32(dsp):
     (20, 4, 2048, 512, 0.0),      # rank 512
     (9, 3, 1001, 40, 1.3),        # V not a multiple of 8: vector-ALU path, bf16 weights
     (64, 2, 4104, 72, 0.5),       # rank not a multiple of 32: zero-padded rank step
-    (37, 3, 16384, 256, 0.0),     # one launch for all steps (resident W2), ragged row blocks
+    (37, 3, 16384, 256, 0.0),     # one launch per step, ragged row blocks
     (37, 3, 16384, 256, 0.9),     # the same with Gumbel noise
+    (37, 3, 49160, 256, 0.0),     # several tiles per workgroup, one partial tile
+    (37, 4, 49160, 256, 0.9),     # the same with Gumbel noise
+    (64, 4, 65536, 72, 0.5),      # rank zero-padded to 256, 64-row workgroups
+    (128, 1, 60000, 256, 0.0),    # a single step
+    (100, 6, 52000, 128, 1.0),    # rank 128, ragged last tile
 ])
 def test_bf16_variants(dsp, R, G, V, r, T):
     mk = W.markov_case(R * 1000 + V, R, G, V, r, "bf16", base_std=2.0, w1_std=1.0,
@@ -165,3 +170,4 @@ def test_config5_markov_full_size(dsp):
     inp = W.config5_device(torch, torch.device("cuda:0"))
     rows = list(np.random.default_rng(2).choice(128, size=12, replace=False))
     _full_size_check(dsp, inp, 0.0, 0, rows)
+
