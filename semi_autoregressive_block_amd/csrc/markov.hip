@@ -86,8 +86,9 @@ __device__ __forceinline__ void fold_key_global(uint64_t* keys, int row, int R, 
 // NW waves per workgroup, 16 rows per wave (row group = 16*NW rows), KS
 // 32-wide rank steps (rank padded with zeros to 32*KS).  The vocabulary is
 // cut into 64-column tiles handed out interleaved: at step t of its loop
-// workgroup w owns tile t*grid + w, so the workgroups running side by side
-// read one contiguous span of every W2 row and every base row.
+// each workgroup owns one tile of round t*grid .. t*grid + grid-1, so the
+// workgroups running side by side read one contiguous span of every W2 row
+// and every base row.
 //
 // The product is computed transposed, out^T = W2^T E^T: W2^T is the A operand
 // (v_mfma_f32_16x16x32_bf16), read from the LDS copy of the tile with
@@ -129,9 +130,17 @@ __global__ __launch_bounds__(64 * NW) void markov_step_mfma(
   const int row = blockIdx.y * 16 * NW + wave * 16 + n;  // this lane's row
   const int rowc = min(row, R - 1);
 
+  // round t covers tiles t*G .. t*G + G-1 (G workgroups side by side: one
+  // contiguous span of every W2 and base row); workgroup w takes slot
+  // (w + 3t) mod G of it, so its tiles alternate in address parity (a fixed
+  // slot leaves half the workgroups on odd 128-byte lines only, which stream
+  // measurably slower)
+  const int G = (int)gridDim.x;
   const int ntiles_all = (V + kTileCols - 1) / kTileCols;
-  const int ntile = ntiles_all > (int)blockIdx.x ? (ntiles_all - 1 - (int)blockIdx.x) / (int)gridDim.x + 1 : 0;
-  auto tile_col = [&](int t) -> int64_t { return ((int64_t)t * gridDim.x + blockIdx.x) * kTileCols; };
+  auto slot = [&](int t) -> int { return (int)(((int64_t)blockIdx.x + 3 * (int64_t)t) % G); };
+  const int full = ntiles_all / G;
+  const int ntile = full + (slot(full) < ntiles_all - full * G ? 1 : 0);
+  auto tile_col = [&](int t) -> int64_t { return ((int64_t)t * G + slot(t)) * kTileCols; };
 
   // ---- E^T operands: rank 32kk + 8g .. +7 of W1[prev(row)]
   u32x4 eb[KS];
