@@ -53,8 +53,8 @@ def parse():
 
 
 KERNEL_SOURCES = {
-    "block_attn_mfma<128,2,2>": "semi_autoregressive_block_amd/csrc/attention.hip",
-    "markov_step_mfma<8,8,3>": "semi_autoregressive_block_amd/csrc/markov.hip",
+    "block_attn_mfma<128,2,2,0>": "semi_autoregressive_block_amd/csrc/attention.hip",
+    "markov_step_mfma<8,8,2,true>": "semi_autoregressive_block_amd/csrc/markov.hip",
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 
@@ -280,13 +280,13 @@ def main():
     mk_launch_ms = r["markov_ms"] / r["markov_steps"]
     mk_gbs = r["markov_step_bytes"] / mk_launch_ms / 1e6
     if r["attn_ms"] >= r["markov_ms"]:
-        k = "block_attn_mfma<128,2,2>"
+        k = "block_attn_mfma<128,2,2,0>"
         roof = dict(kernel=k, bound="hbm", achieved=attn_gbs,
                     peak=HBM_PEAK_GBS, unit="GB/s", frac=attn_gbs / HBM_PEAK_GBS,
                     traffic=measured_traffic(k), bytes_per_launch=r["attn_bytes"],
                     launch_ms=r["attn_ms"])
     else:
-        k = "markov_step_mfma<8,8,3>"
+        k = "markov_step_mfma<8,8,2,true>"
         roof = dict(kernel=k, bound="hbm", achieved=mk_gbs, peak=HBM_PEAK_GBS,
                     unit="GB/s", frac=mk_gbs / HBM_PEAK_GBS, traffic=measured_traffic(k),
                     bytes_per_launch=r["markov_step_bytes"], launch_ms=mk_launch_ms)
