@@ -17,8 +17,9 @@
 // loads, so its polls never queue behind the data waves' streaming loads.
 // The exchange is pipelined: while it runs, the data waves park the row's
 // exponentials in LDS and go on with pass one of the next row; pass two of
-// a row (one multiply, one min and one add per element pair, no second
-// exponential) runs one iteration later.  Cluster members may therefore drift
+// a row (one fused multiply-add and one add per element pair through
+// sum min = (sum p + sum q - sum |p - q|) / 2, no second exponential) runs
+// one iteration later.  Cluster members may therefore drift
 // apart by up to an iteration without stalling one another.  The next row's
 // slice streams in (16-byte buffer loads; a row past the end reads through an
 // empty buffer range, so the tail costs no traffic) while the current one is
@@ -51,10 +52,9 @@ constexpr int kNonTemporal = 2;             // streaming loads
 constexpr int kLdsBytesPerCU = 160 * 1024;
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
-// IEEE-754-2019 maximum / minimum (NaN-propagating): one v_maximum3 /
-// v_minimum3 each on gfx950, with no operand canonicalisation.
+// IEEE-754-2019 maximum (NaN-propagating): one v_maximum3 on gfx950, with no
+// operand canonicalisation.
 __device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
-__device__ __forceinline__ float vmin(float a, float b) { return __builtin_elementwise_minimum(a, b); }
 
 // ---- wave reductions: DPP inside each row of 16 lanes, then the four row
 // results through scalar registers.  Every lane returns the same value, and
@@ -204,11 +204,13 @@ __global__ __launch_bounds__(kThreads) void tv_cluster_kernel(
       }
     };
     issue(cl);
+    float psd = 0.f, pst = 0.f;  // this wave's sums of the previous row's exponentials
     for (int64_t k = 0; k <= nk; ++k) {
       const int64_t row = cl + k * nclusters;
       const bool have = k < nk;  // iteration nk only finishes the last row
       const int par = (int)(k & 1);
       float xd[kN], xt[kN];
+      float csd = 0.f, cst = 0.f;
       if (have) {
 #pragma unroll
         for (int i = 0; i < kVec; ++i) {
@@ -250,34 +252,46 @@ __global__ __launch_bounds__(kThreads) void tv_cluster_kernel(
         }
         const float wsd = wave_sum(sd0 + sd1), wst = wave_sum(st0 + st1);
         if (lane == 0) { red_sum[par][0][w] = wsd; red_sum[par][1][w] = wst; }
+        csd = wsd;
+        cst = wst;
       }
       __syncthreads();  // B: sums of row k; the exchange wave has the offsets of row k-1
       if (k >= 1) {
         // pass two of row k-1 on its parked exponentials:
         // p_v = ed_v * 2^{eD}, q_v = et_v * 2^{eT}; the side with the smaller
-        // exponent is scaled down (never up: no overflow, and 0 * c stays 0)
+        // exponent is scaled down (never up: no overflow, and 0 * c stays 0).
+        // With u the unscaled side and v the scaled one,
+        //   sum min(u, v) = (sum u + sum v - sum |u - v|) / 2,
+        // where both sums are this wave's pass-one sums of the row: one fma
+        // (|.| is a free source modifier of the add) and one add per pair.
         const float eD = uniform(glob[(k - 1) & 1][0]), eT = uniform(glob[(k - 1) & 1][1]);
-        float p0 = 0.f, p1 = 0.f;
+        float p0 = 0.f, p1 = 0.f, su, sv;
         if (eD >= eT) {
           const float c = exp2_fast(eT - eD);
+          su = psd;
+          sv = pst * c;
 #pragma unroll
           for (int j = 0; j < kN / 4; ++j) {
             const f32x4 a = park[j][tid], b = park[kN / 4 + j][tid];
-            p0 += vmin(a[0], b[0] * c); p1 += vmin(a[1], b[1] * c);
-            p0 += vmin(a[2], b[2] * c); p1 += vmin(a[3], b[3] * c);
+            p0 += fabsf(fmaf(b[0], c, -a[0])); p1 += fabsf(fmaf(b[1], c, -a[1]));
+            p0 += fabsf(fmaf(b[2], c, -a[2])); p1 += fabsf(fmaf(b[3], c, -a[3]));
           }
         } else {
           const float c = exp2_fast(eD - eT);
+          su = pst;
+          sv = psd * c;
 #pragma unroll
           for (int j = 0; j < kN / 4; ++j) {
             const f32x4 a = park[j][tid], b = park[kN / 4 + j][tid];
-            p0 += vmin(a[0] * c, b[0]); p1 += vmin(a[1] * c, b[1]);
-            p0 += vmin(a[2] * c, b[2]); p1 += vmin(a[3] * c, b[3]);
+            p0 += fabsf(fmaf(a[0], c, -b[0])); p1 += fabsf(fmaf(a[1], c, -b[1]));
+            p0 += fabsf(fmaf(a[2], c, -b[2])); p1 += fabsf(fmaf(a[3], c, -b[3]));
           }
         }
-        const float wp = wave_sum(p0 + p1);
+        const float wp = 0.5f * ((su + sv) - wave_sum(p0 + p1));
         if (lane == 0) red_part[w] = wp;  // times 2^{max(eD, eT)}: applied by the exchange wave
       }
+      psd = csd;
+      pst = cst;
       if (have) {
 #pragma unroll
         for (int j = 0; j < kN / 4; ++j) {
