@@ -36,11 +36,10 @@
 //   single cross-half exchange (v_permlane32_swap).  The probabilities feed
 //   O^T = V^T P^T straight from the S^T accumulator layout (no transpose of
 //   P); V^T operands come from transposing LDS reads.
-// * K/V staging: pairs of slabs (one per parity) go global -> registers ->
-//   a two-slot LDS ring, with two register sets of loads in flight (64-row
-//   tiles); for 128-row tiles they go straight from global memory into a
-//   four-slot LDS ring (direct LDS loads, three pairs in flight).  Parities
-//   merge through LDS at the end.
+// * K/V staging: pairs of slabs (one per parity) go straight from global
+//   memory into a ring of LDS slots (direct LDS loads: no register round
+//   trip), two slots for 64-row tiles (two workgroups per compute unit),
+//   four for 128-row tiles.  Parities merge through LDS at the end.
 #include "common.h"
 
 using namespace dspark;
@@ -302,82 +301,30 @@ __global__ __launch_bounds__(1024) void attn_plan_kernel(Params p, int32_t* __re
 }
 
 // ------------------------------------------------------------ MFMA kernel
-// K and V reach the waves through LDS: the workgroup's four waves load each
-// pair of 32-key slabs (one per key parity) together, as 16-byte pieces,
-// into two-slot rings (one for K, one for V), so a slab is fetched once per
-// workgroup and read by both row groups.  Loads in flight live in
-// 32-register sets, which keeps a wave within 256 registers: two
-// workgroups share a compute unit and each SIMD interleaves two waves'
-// matrix-core and softmax work.  K rows are stored with their 16-byte
-// pieces XOR-swizzled by the key index, so the MFMA-operand reads (one
-// piece of 32 different keys) hit distinct LDS banks; V rows have their
-// 64-byte groups XOR-rotated by the key, for the transposing reads.
+// K and V reach the waves through LDS: the workgroup's waves copy each pair
+// of 32-key slabs (one per key parity) together, as 16-byte pieces, into a
+// ring slot, so a slab is fetched once per workgroup and read by all its row
+// groups.  K rows are stored with their 16-byte pieces XOR-swizzled by the
+// key index, so the MFMA-operand reads (one piece of 32 different keys) hit
+// distinct LDS banks; V rows have their 64-byte groups XOR-rotated by the
+// key, for the transposing reads.
 template <int D>
 struct Ring {
   static constexpr int kPieces = D * 2 / 16;             // 16-byte pieces per key row
   static constexpr int kTensorBytes = 32 * D * 2;        // K (or V) of one slab
   static constexpr int kSlotBytes = 2 * kTensorBytes;    // parity-0 slab then parity-1 slab
-  static constexpr int kVRing = 2 * kSlotBytes;          // the V ring follows the two K slots
-  static constexpr int kBytes = 2 * kVRing;
-  // V pieces: groups of four pieces (32 head dims) XOR-rotated by the key, so
-  // the transposing reads of four consecutive keys hit distinct banks
-  __device__ static int v_piece(int key, int piece) { return piece ^ (4 * (key % (kPieces / 4))); }
-  __device__ static unsigned char* k_slot(unsigned char* ring, int i) { return ring + (i & 1) * kSlotBytes; }
-  __device__ static unsigned char* v_slot(unsigned char* ring, int i) { return ring + kVRing + (i & 1) * kSlotBytes; }
 };
 
-// Moves the K or V half of a slab pair from HBM/L2 through registers into
-// a ring slot.  Piece c = threadIdx.x + NT*j of a slot (NT threads) is 16
-// bytes of slab c / (32P) (parity), key (c mod 32P) / P, head dims
-// 8*(c mod P) .. +7 (P pieces per key row).  Since NT is a multiple of P and
-// NT and 32P divide one another, a thread keeps one slab, key and piece
-// offset for all j and the rest is a compile-time constant per j: LDS stores
-// take immediate offsets and a load is a wave-uniform slab base plus one
-// 32-bit lane offset.  Keys past a source's last row are read from that last
-// row (they are masked in the scores).
-template <int D, int NT>
-struct Stager {
-  using Rg = Ring<D>;
-  static constexpr int P = Rg::kPieces;
-  static constexpr int N = Rg::kSlotBytes / 16 / NT;  // pieces a thread moves per slot
-  static_assert(NT % P == 0 && (NT % (32 * P) == 0 || (32 * P) % NT == 0) && N >= 1, "piece layout");
-  // per-thread constants
-  int slab_t;          // slab of piece j = 0 (wave-uniform)
-  int key_t;           // key of piece j = 0
-  uint32_t piece_b;    // byte offset of the piece inside a key row
-  uint32_t lds_k, lds_v;  // ring byte offset of piece j = 0 in a K / V slab
-  // wave-uniform
+// Where a workgroup's slabs come from (wave-uniform): slab s < n_ctx_slabs
+// is context keys 32s .. 32s+31 from ctx_row0, later slabs are the tile's
+// own block keys from own_row0.  Keys past a source's last row are read
+// from that last row (they are masked in the scores).
+struct SlabSource {
   const unsigned char *kc, *vc, *kb, *vb;
   int64_t ctx_row0, own_row0;  // first row of the context chunk / of the tile's own keys
   int ctx_keys, own_keys, n_ctx_slabs, nslab;
   uint32_t row_b;              // bytes between consecutive rows (all heads)
   uint32_t head_b;             // byte offset of this KV head inside a row
-
-  static constexpr int slab_of(int j) { return (NT * j) / (32 * P); }
-  static constexpr int keyoff_of(int j) { return ((NT * j) % (32 * P)) / P; }
-
-  template <bool kV>
-  __device__ void load(int pair, u32x4 (&R)[N]) const {
-#pragma unroll
-    for (int j = 0; j < N; ++j) {
-      // an odd last pair repeats a slab (not computed)
-      const int s = min(2 * pair + slab_t + slab_of(j), nslab - 1);
-      const bool own = s >= n_ctx_slabs;
-      const int k0 = own ? (s - n_ctx_slabs) * 32 : s * 32;
-      const int nvalid = (own ? own_keys : ctx_keys) - k0;
-      const unsigned char* src = kV ? (own ? vb : vc) : (own ? kb : kc);
-      src += ((own ? own_row0 : ctx_row0) + k0) * (int64_t)row_b + head_b;
-      const uint32_t off = __umul24((uint32_t)min(key_t + keyoff_of(j), nvalid - 1), row_b) + piece_b;
-      R[j] = *(const u32x4*)(src + off);
-    }
-  }
-
-  template <bool kV>
-  __device__ void store(unsigned char* slot, const u32x4 (&R)[N]) const {
-#pragma unroll
-    for (int j = 0; j < N; ++j)
-      *(u32x4*)(slot + (kV ? lds_v : lds_k) + slab_of(j) * Rg::kTensorBytes + keyoff_of(j) * P * 16) = R[j];
-  }
 };
 
 // This lane's operand pieces of one staged slab.  K piece kk (key r32, head
@@ -432,7 +379,7 @@ struct DmaPair {
   static constexpr int kPerWave = kInst / (NT / 64);
   static constexpr int kPerPair = 2 * kPerWave;         // copies per wave per pair
   static_assert(kInst % (NT / 64) == 0 && (32 * P) % 64 == 0, "copy layout");
-  __device__ static void issue(const Stager<D, NT>& st, int pair, unsigned char* slot, int wave, int lane) {
+  __device__ static void issue(const SlabSource& st, int pair, unsigned char* slot, int wave, int lane) {
 #pragma unroll
     for (int hv = 0; hv < 2; ++hv)
 #pragma unroll
@@ -457,18 +404,17 @@ struct DmaPair {
 };
 
 // One workgroup per tile of 32*RG query rows and one (request, KV head):
-// RG row groups x two key parities, one wave each.  NSLOT == 0: NSETS
-// register sets of K/V loads are in flight while a pair is computed (two
-// LDS slots); NSLOT > 0: direct-to-LDS copies into an NSLOT-slot ring, the
-// next NSLOT - 1 pairs in flight.
-template <int D, int NSETS, int RG, int NSLOT>
+// RG row groups x two key parities, one wave each; direct-to-LDS copies into
+// an NSLOT-slot ring keep the next NSLOT - 1 slab pairs in flight.
+template <int D, int RG, int NSLOT>
 __global__ __launch_bounds__(64 * 2 * RG) __attribute__((amdgpu_waves_per_eu(2, 2))) void block_attn_mfma(Params p) {
   using Rg = Ring<D>;
   constexpr int NJ = D / 32;
   constexpr int KK = D / 16;
   constexpr int NT = 64 * 2 * RG;  // RG row groups x two key parities, one wave each
   constexpr int kMergeBytes = RG * (D + 2) * 32 * 4;
-  constexpr int kRingBytes = NSLOT > 0 ? NSLOT * 2 * Rg::kSlotBytes : Rg::kBytes;
+  static_assert(NSLOT >= 2, "at least one pair in flight");
+  constexpr int kRingBytes = NSLOT * 2 * Rg::kSlotBytes;
   __shared__ __align__(16) unsigned char ring[kRingBytes > kMergeBytes ? kRingBytes : kMergeBytes];
 
   // the work item is the same for the whole workgroup: keep it in scalars
@@ -520,16 +466,8 @@ __global__ __launch_bounds__(64 * 2 * RG) __attribute__((amdgpu_waves_per_eu(2, 
   const int npairs = (nslab + 1) / 2;
   const float c = p.scale * kLog2e;
 
-  Stager<D, NT> st;
+  SlabSource st;
   {
-    constexpr int P = Rg::kPieces;
-    const int t = threadIdx.x;
-    st.slab_t = (64 * wave) / (32 * P);  // 0 unless NT > 32P
-    st.key_t = (t % (32 * P)) / P;
-    const int piece = t % P;
-    st.piece_b = piece * 16;
-    st.lds_k = st.slab_t * Rg::kTensorBytes + (st.key_t * P + (piece ^ (st.key_t % P))) * 16;
-    st.lds_v = st.slab_t * Rg::kTensorBytes + (st.key_t * P + Rg::v_piece(st.key_t, piece)) * 16;
     st.kc = (const unsigned char*)p.kc; st.vc = (const unsigned char*)p.vc;
     st.kb = (const unsigned char*)p.kb; st.vb = (const unsigned char*)p.vb;
     st.ctx_row0 = (int64_t)c0 + it.cbeg;
@@ -549,18 +487,7 @@ __global__ __launch_bounds__(64 * 2 * RG) __attribute__((amdgpu_waves_per_eu(2, 
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[j][r] = 0.f;
 
-  // ---- pair loop: pair i is computed from ring slot i & 1 while pair i + 1
-  //      goes from registers into the other slot and the next pairs are in
-  //      flight.  With two sets the loads are unconditional (past the end
-  //      they repeat the last slab, from L2), so the wait before each store
-  //      counts on exactly the younger set's loads being in flight; a step
-  //      past the end computes nothing.
-  auto view = [&](int ik, int iv) {
-    return SlabView<D>(Rg::k_slot(ring, ik) + par * Rg::kTensorBytes,
-                       Rg::v_slot(ring, iv) + par * Rg::kTensorBytes, h, r32);
-  };
-  constexpr int N = Stager<D, NT>::N;
-  if constexpr (NSLOT > 0) {
+  {
     // ---- pair i is computed from slot i mod NSLOT while pairs i+1 ..
     //      i+NSLOT-1 are being copied in.  Iteration i: wait for this wave's
     //      copies of pair i, meet the other waves (their copies of pair i
@@ -586,43 +513,6 @@ __global__ __launch_bounds__(64 * 2 * RG) __attribute__((amdgpu_waves_per_eu(2, 
       wait_vmcnt<0>();
       block_barrier();  // every copy has landed and every wave is done with the ring
     }
-  } else {
-  // ---- pair i is computed from ring slot i & 1 while pair i + 1 goes from
-  //      registers into the other slot and pairs i + 2 .. i + NSETS are in
-  //      flight in the register sets (the loop is unrolled by NSETS so each
-  //      set has fixed registers).  The loads are unconditional (past the
-  //      end they repeat the last slab, from L2), so the wait before each
-  //      store counts on exactly the younger sets' loads being in flight; a
-  //      step past the end computes nothing.
-  if (npairs > 0) {
-    u32x4 Rk[NSETS][N], Rv[NSETS][N];
-#pragma unroll
-    for (int q = 0; q < NSETS; ++q) {
-      st.template load<false>(q, Rk[q]);
-      st.template load<true>(q, Rv[q]);
-    }
-    st.template store<false>(Rg::k_slot(ring, 0), Rk[0]);
-    st.template store<true>(Rg::v_slot(ring, 0), Rv[0]);
-    st.template load<false>(NSETS, Rk[0]);
-    st.template load<true>(NSETS, Rv[0]);
-    __syncthreads();
-    for (int i0 = 0; i0 < npairs; i0 += NSETS) {
-#pragma unroll
-      for (int q = 0; q < NSETS; ++q) {
-        const int i = i0 + q;
-        const int set = (q + 1) % NSETS;
-        if (i + 1 < npairs) {
-          st.template store<false>(Rg::k_slot(ring, i + 1), Rk[set]);
-          st.template store<true>(Rg::v_slot(ring, i + 1), Rv[set]);
-        }
-        st.template load<false>(i + 1 + NSETS, Rk[set]);
-        st.template load<true>(i + 1 + NSETS, Rv[set]);
-        const int s = 2 * i + par;
-        if (s < nslab) compute_slab<D>(p, it, s, view(i, i), qf, kept, lim, ua, a_lo, c, m, l, o);
-        __syncthreads();
-      }
-    }
-  }
   }
 
   // ---- merge the two key parities of each row group through LDS (the ring
@@ -825,11 +715,11 @@ extern "C" int dspark_block_attention(const void* q, const void* k_ctx, const vo
     p.order = order;
     const dim3 grid((unsigned)sh.tiles), block(deep ? 256 : 512);
     if (D == 128) {
-      if (deep) hipLaunchKernelGGL((block_attn_mfma<128, 2, 2, 0>), grid, block, 0, s, p);
-      else hipLaunchKernelGGL((block_attn_mfma<128, 2, 4, 4>), grid, block, 0, s, p);
+      if (deep) hipLaunchKernelGGL((block_attn_mfma<128, 2, 2>), grid, block, 0, s, p);
+      else hipLaunchKernelGGL((block_attn_mfma<128, 4, 4>), grid, block, 0, s, p);
     } else {
-      if (deep) hipLaunchKernelGGL((block_attn_mfma<64, 2, 2, 0>), grid, block, 0, s, p);
-      else hipLaunchKernelGGL((block_attn_mfma<64, 2, 4, 4>), grid, block, 0, s, p);
+      if (deep) hipLaunchKernelGGL((block_attn_mfma<64, 2, 2>), grid, block, 0, s, p);
+      else hipLaunchKernelGGL((block_attn_mfma<64, 4, 4>), grid, block, 0, s, p);
     }
   } else {
     const int64_t nb = (int64_t)B * A * Hq;
