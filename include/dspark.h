@@ -64,6 +64,7 @@ extern "C" {
 #define DSPARK_STATUS_BAD_TOKEN   2  /* previous token outside [0, V) */
 #define DSPARK_STATUS_BAD_OFFSETS 4  /* ctx_offsets not non-decreasing, or a context longer than max_ctx */
 #define DSPARK_STATUS_BAD_LABEL   8  /* label index beyond S_stride of the loss mask */
+#define DSPARK_STATUS_WAIT_TIMEOUT 16 /* a workgroup of a cooperative grid gave up waiting on its peers */
 
 /* Library version (major*10000 + minor*100 + patch). */
 int dspark_version(void);
@@ -165,14 +166,28 @@ int dspark_markov_sample(const float* base_logits, const void* w1, const void* w
  *   accept     [B, A, gamma] float32 (out)
  *   eval_mask  [B, A, gamma] uint8 (nullable; only read for tau)
  *   tau        [B, A] float32 (out, nullable)
+ *   dev_status int32 device word (nullable): DSPARK_STATUS_WAIT_TIMEOUT
  * Limits: V >= 2, gamma <= 1024.  Launched cooperatively: the call fails
  * with DSPARK_ERR_HIP if the device cannot host its persistent grid.
+ * Accept values of poisoned rows (see dspark_set_wait_limit) stay NaN
+ * through the clamp.
  * ---------------------------------------------------------------------- */
 size_t dspark_accept_rate_workspace_bytes(int B, int A, int gamma, int V, int dtype);
 int dspark_accept_rate(const void* draft_logits, const void* target_logits, float* accept,
                        const uint8_t* eval_mask, float* tau,
                        int B, int A, int gamma, int V, int dtype,
-                       void* ws, size_t ws_bytes, void* stream);
+                       void* ws, size_t ws_bytes, int32_t* dev_status, void* stream);
+
+/* Poll limit of the bounded waits inside cooperative grids (the accept rate's
+ * exchange of row statistics between the workgroups of a row).  A wait that
+ * exceeds it sets DSPARK_STATUS_WAIT_TIMEOUT and the workgroup goes on without
+ * waiting: the rows it finishes from then on are NaN and every accept / tau
+ * of that call is unreliable.  With a co-resident grid the waits end long
+ * before the default limit (2^20 polls); a smaller limit exists so that
+ * tests can drive the timeout path with every kernel still exiting normally.
+ * polls = 0 restores the default.  Process-wide; takes effect for calls
+ * enqueued afterwards. */
+void dspark_set_wait_limit(uint32_t polls);
 
 /* ------------------------------------------------------------------------
  * Cumulative-product eval mask (page 1 §3.1 and §3.6).  For block (b, a)

@@ -26,7 +26,8 @@ _LIB = _lib.load()
 
 __all__ = ["block_attention", "markov_sample", "accept_rate", "eval_mask",
            "block_attention_workspace_bytes", "markov_sample_workspace_bytes",
-           "accept_rate_workspace_bytes", "last_error", "version", "DSparkError"]
+           "accept_rate_workspace_bytes", "set_wait_limit", "last_error", "version",
+           "DSparkError"]
 
 
 class DSparkError(RuntimeError):
@@ -184,9 +185,10 @@ def accept_rate_workspace_bytes(B, A, gamma, V, dtype=_lib.BF16) -> int:
 
 
 def accept_rate(draft, target, *, eval_mask=None, want_tau=False, accept=None, tau=None,
-                workspace=None):
+                status=None, workspace=None):
     """draft, target [B, A, gamma, V] (bf16 or float32); eval_mask [B, A, gamma]
-    uint8 (optional, used for tau).  Returns (accept [B, A, gamma] float32,
+    uint8 (optional, used for tau); status: int32 device word that receives
+    STATUS_WAIT_TIMEOUT (optional).  Returns (accept [B, A, gamma] float32,
     tau [B, A] float32 or None)."""
     dev = draft.device
     _check(draft, "draft", (torch.bfloat16, torch.float32), ndim=4)
@@ -203,14 +205,23 @@ def accept_rate(draft, target, *, eval_mask=None, want_tau=False, accept=None, t
         tau = torch.empty((B, A), dtype=torch.float32, device=dev)
     if tau is not None:
         _check(tau, "tau", torch.float32, dev, 2)
+    if status is not None:
+        _check(status, "status", torch.int32, dev)
     dt = _dt(draft)
     nbytes = accept_rate_workspace_bytes(B, A, gamma, V, dt)
     ws, wsb = _workspace(nbytes, dev, workspace)
     rc = _LIB.dspark_accept_rate(_ptr(draft), _ptr(target), _ptr(accept), _ptr(eval_mask),
-                                 _ptr(tau), B, A, gamma, V, dt, _ptr(ws), wsb, _stream(dev))
+                                 _ptr(tau), B, A, gamma, V, dt, _ptr(ws), wsb, _ptr(status),
+                                 _stream(dev))
     if rc != 0:
         raise DSparkError(rc, "accept_rate")
     return accept, tau
+
+
+def set_wait_limit(polls: int) -> None:
+    """Poll limit of the cooperative grids' bounded waits (0 = the default).
+    Process-wide; meant for tests of the timeout path."""
+    _LIB.dspark_set_wait_limit(int(polls))
 
 
 def eval_mask(anchor, keep, seq_lens, loss_mask=None, *, gamma, out=None, status=None):

@@ -20,6 +20,7 @@ STATUS_BAD_ANCHOR = 1
 STATUS_BAD_TOKEN = 2
 STATUS_BAD_OFFSETS = 4
 STATUS_BAD_LABEL = 8
+STATUS_WAIT_TIMEOUT = 16
 
 _p = ctypes.c_void_p
 _i = ctypes.c_int
@@ -38,7 +39,8 @@ SIGNATURES = {
     "dspark_markov_sample": (_i, [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _u64,
                                   _p, _sz, _p, _p]),
     "dspark_accept_rate_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
-    "dspark_accept_rate": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _p, _sz, _p]),
+    "dspark_accept_rate": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _p, _sz, _p, _p]),
+    "dspark_set_wait_limit": (None, [ctypes.c_uint32]),
     "dspark_eval_mask": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _p, _p]),
 }
 

@@ -29,6 +29,7 @@
 #include <stdlib.h>
 
 #include <algorithm>
+#include <atomic>
 #include <map>
 #include <mutex>
 #include <utility>
@@ -46,7 +47,7 @@ constexpr int kVec = 3;                           // 16-byte vectors per data th
 constexpr int kChunkVec = kDataThreads * kVec;    // vectors of one tensor per workgroup and row
 constexpr int kMaxG = 2 * kWave;                  // two cluster members per exchange lane
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr unsigned kSpinLimit = 1u << 20;  // bounded wait (well under a second), then flag and go on
+constexpr unsigned kSpinLimit = 1u << 20;  // default poll bound of a wait (well under a second)
 constexpr int kRsrcWord3 = 0x00020000;      // raw 32-bit buffer data format (gfx9 family)
 constexpr int kNonTemporal = 2;             // streaming loads
 constexpr int kLdsBytesPerCU = 160 * 1024;
@@ -167,7 +168,7 @@ template <bool kBf16>
 __global__ __launch_bounds__(kThreads) void tv_cluster_kernel(
     const char* __restrict__ d, const char* __restrict__ t, float* __restrict__ share,
     int64_t rows, int V, int vec_per_row, int G, int nclusters,
-    u32x4* __restrict__ slots, int32_t* __restrict__ err) {
+    u32x4* __restrict__ slots, int32_t* __restrict__ err, unsigned spin_limit) {
   constexpr int kEl = Shape<kBf16>::kEl, kN = Shape<kBf16>::kN, kPark = Shape<kBf16>::kPark;
   __shared__ f32x4 park[kPark][kDataThreads];  // the previous row's exponentials
   __shared__ float red_max[2][2][kDataWaves], red_sum[2][2][kDataWaves], red_part[kDataWaves];
@@ -340,8 +341,8 @@ __global__ __launch_bounds__(kThreads) void tv_cluster_kernel(
               ad[h] = __uint_as_float(v[0]); sd[h] = __uint_as_float(v[1]);
               at[h] = __uint_as_float(v[2]); st[h] = __uint_as_float(v[3]);
               got[h] = true;
-            } else if (!ok || ++n > kSpinLimit) {
-              if (ok) atomicOr(err, 1);
+            } else if (!ok || ++n > spin_limit) {
+              if (ok) atomicOr(err, DSPARK_STATUS_WAIT_TIMEOUT);
               ok = false;
               got[h] = true;  // give up on this member: the row is poisoned below
             }
@@ -418,7 +419,8 @@ __global__ void tv_finalize_kernel(const float* __restrict__ share, int G,
       s3 += sp[j + 3];
     }
     for (; j < G; ++j) s0 += sp[j];
-    a = fminf(fmaxf((s0 + s1) + (s2 + s3), 0.f), 1.f);
+    const float x = (s0 + s1) + (s2 + s3);
+    a = x != x ? x : fminf(fmaxf(x, 0.f), 1.f);  // a poisoned (NaN) row stays NaN
     accept[row] = a;
   }
   if (!tau || kWave % gamma != 0) return;
@@ -576,10 +578,17 @@ extern "C" size_t dspark_accept_rate_workspace_bytes(int B, int A, int gamma, in
   return shares + slots + 64;
 }
 
+// Poll limit of the cooperative waits; 0 selects kSpinLimit.
+static std::atomic<uint32_t> g_wait_limit{0};
+
+extern "C" void dspark_set_wait_limit(uint32_t polls) {
+  g_wait_limit.store(polls, std::memory_order_relaxed);
+}
+
 extern "C" int dspark_accept_rate(const void* draft_logits, const void* target_logits,
                                   float* accept, const uint8_t* eval_mask, float* tau, int B,
                                   int A, int gamma, int V, int dtype, void* ws, size_t ws_bytes,
-                                  void* stream) {
+                                  int32_t* dev_status, void* stream) {
   using namespace dspark_host;
   if (B < 0 || A < 0 || gamma < 0)
     return fail(DSPARK_ERR_INVALID_ARG, "accept_rate: negative dimension");
@@ -612,7 +621,8 @@ extern "C" int dspark_accept_rate(const void* draft_logits, const void* target_l
     float* share = (float*)ws;
     u32x4* slots = (u32x4*)((char*)ws + align_up((size_t)rows * geo.G * sizeof(float), 256));
     const int64_t nslot = ncl * 2 * geo.G;
-    int32_t* err = (int32_t*)(slots + nslot);  // one spare word after the slots
+    // timeouts go to the caller's status word, else to a spare word after the slots
+    int32_t* err = dev_status ? dev_status : (int32_t*)(slots + nslot);
     // slots (epoch 0 = empty) and the error word start at zero: a fill
     // kernel, not a memset node, so the sequence stays safe under graph capture
     const int64_t nwords = nslot * 4 + 1;
@@ -622,8 +632,11 @@ extern "C" int dspark_accept_rate(const void* draft_logits, const void* target_l
     const char* tp = (const char*)target_logits;
     int64_t rows_arg = rows;
     int Varg = V, vpr = geo.vec_per_row, G = geo.G, ncl_arg = (int)ncl;
+    const uint32_t lim = g_wait_limit.load(std::memory_order_relaxed);
+    unsigned spin = lim ? lim : kSpinLimit;
     void* args[] = {(void*)&dp, (void*)&tp, (void*)&share, (void*)&rows_arg, (void*)&Varg,
-                    (void*)&vpr, (void*)&G, (void*)&ncl_arg, (void*)&slots, (void*)&err};
+                    (void*)&vpr, (void*)&G, (void*)&ncl_arg, (void*)&slots, (void*)&err,
+                    (void*)&spin};
     if (getenv("DSPARK_VERBOSE"))
       fprintf(stderr, "[dspark] accept_rate: %d CUs, G=%d, clusters=%lld, vec/row=%d\n",
               device_cus(), G, (long long)ncl, vpr);

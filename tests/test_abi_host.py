@@ -33,7 +33,7 @@ def lib():
 def test_every_declared_symbol_is_exported(lib):
     mod, L = lib
     names = _declared()
-    assert len(names) == 9, names
+    assert len(names) == 10, names
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(mod.SIGNATURES)
@@ -108,11 +108,27 @@ def test_markov_rejects_bad_arguments(lib):
 def test_accept_rate_and_eval_mask_reject_bad_arguments(lib):
     mod, L = lib
     p = ctypes.c_void_p(16)
-    assert L.dspark_accept_rate(p, p, p, NULL, NULL, 1, 1, 1, 1, 1, p, 1 << 20, NULL) == mod.ERR_INVALID_ARG
-    assert L.dspark_accept_rate(p, p, p, NULL, NULL, 1, 1, 1, 64, 3, p, 1 << 20, NULL) == mod.ERR_INVALID_ARG
-    assert L.dspark_accept_rate(p, p, p, NULL, NULL, 1, 1, 1, 64, 1, p, 0, NULL) == mod.ERR_WORKSPACE
-    assert L.dspark_accept_rate(p, p, p, NULL, NULL, 0, 1, 1, 64, 1, NULL, 0, NULL) == mod.OK
+    assert L.dspark_accept_rate(p, p, p, NULL, NULL, 1, 1, 1, 1, 1, p, 1 << 20, NULL, NULL) == mod.ERR_INVALID_ARG
+    assert L.dspark_accept_rate(p, p, p, NULL, NULL, 1, 1, 1, 64, 3, p, 1 << 20, NULL, NULL) == mod.ERR_INVALID_ARG
+    assert L.dspark_accept_rate(p, p, p, NULL, NULL, 1, 1, 1, 64, 1, p, 0, NULL, NULL) == mod.ERR_WORKSPACE
+    assert L.dspark_accept_rate(p, p, p, NULL, NULL, 0, 1, 1, 64, 1, NULL, 0, NULL, NULL) == mod.OK
     assert L.dspark_eval_mask(p, p, p, NULL, p, -1, 1, 1, 0, NULL, NULL) == mod.ERR_INVALID_ARG
     assert L.dspark_eval_mask(NULL, p, p, NULL, p, 1, 1, 1, 0, NULL, NULL) == mod.ERR_INVALID_ARG
     assert L.dspark_eval_mask(p, p, p, p, p, 1, 1, 1, 0, NULL, NULL) == mod.ERR_INVALID_ARG  # S_stride
     assert L.dspark_eval_mask(p, p, p, NULL, p, 0, 1, 1, 0, NULL, NULL) == mod.OK
+
+
+def test_header_constants_match_binding(lib):
+    """Every #define of the header has the same value in the Python binding."""
+    mod, L = lib
+    defs = dict(re.findall(r"#define\s+DSPARK_(\w+)\s+\(?(-?\d+)\)?", open(HEADER).read()))
+    assert defs, "no constants parsed"
+    for name, val in defs.items():
+        assert getattr(mod, name) == int(val), name
+
+
+def test_wait_limit_setter_is_host_only(lib):
+    """Setting the poll limit touches no device; 0 restores the default."""
+    _, L = lib
+    L.dspark_set_wait_limit(5)
+    L.dspark_set_wait_limit(0)

@@ -149,3 +149,28 @@ def test_long_clusters_bf16(dsp):
         dv = W.bf16_to_f32(host_bits(db[r]))
         tv = W.bf16_to_f32(host_bits(tb[r]))
         assert abs(acc_h[r] - OR.accept_rate(dv, tv)) < 2e-5, r
+
+
+def test_wait_timeout_is_flagged_poisons_and_recovers(dsp):
+    """The waits of the cooperative grid are bounded.  A poll limit of one,
+    set from the host, drives the timeout path while every workgroup still
+    exits normally: the call sets STATUS_WAIT_TIMEOUT and the rows a
+    timed-out workgroup finishes read NaN (not clamped to 0).  The next
+    call at the default limit is clean and matches the oracle again."""
+    from semi_autoregressive_block_amd import _lib
+    d, t = _pair(11, (1, 32, 8, 151936), "bf16")
+    db, tb = as_dtype(d, "bf16"), as_dtype(t, "bf16")
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    dsp.set_wait_limit(1)
+    try:
+        acc, _ = dsp.accept_rate(db, tb, status=st)
+        torch.cuda.synchronize()
+    finally:
+        dsp.set_wait_limit(0)
+    assert int(st.item()) == _lib.STATUS_WAIT_TIMEOUT
+    assert np.isnan(acc.cpu().numpy()).any()
+    st.zero_()
+    acc2, _ = dsp.accept_rate(db, tb, status=st)
+    assert int(st.item()) == 0
+    ref = OR.accept_rate(W.bf16_to_f32(d), W.bf16_to_f32(t))
+    assert np.abs(acc2.cpu().numpy() - ref).max() < 2e-5
