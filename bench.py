@@ -53,7 +53,7 @@ def parse():
 
 
 KERNEL_SOURCES = {
-    "block_attn_mfma<128,2,2>": "semi_autoregressive_block_amd/csrc/attention.hip",
+    "block_attn_mfma<128,2,2,2>": "semi_autoregressive_block_amd/csrc/attention.hip",
     "markov_step_mfma<8,8,2,true>": "semi_autoregressive_block_amd/csrc/markov.hip",
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
@@ -280,7 +280,7 @@ def main():
     mk_launch_ms = r["markov_ms"] / r["markov_steps"]
     mk_gbs = r["markov_step_bytes"] / mk_launch_ms / 1e6
     if r["attn_ms"] >= r["markov_ms"]:
-        k = "block_attn_mfma<128,2,2>"
+        k = "block_attn_mfma<128,2,2,2>"
         roof = dict(kernel=k, bound="hbm", achieved=attn_gbs,
                     peak=HBM_PEAK_GBS, unit="GB/s", frac=attn_gbs / HBM_PEAK_GBS,
                     traffic=measured_traffic(k), bytes_per_launch=r["attn_bytes"],

@@ -27,19 +27,22 @@
 //   each XCD keeps one head's context K/V in its L2.
 // * Two tile heights.  When a context is read by at most two 64-row tiles
 //   per KV head (serving: one block per request) it streams from HBM once:
-//   64-row tiles, two workgroups per compute unit.  When many tiles re-read
-//   it (all-anchor training) it comes from L2: 128-row tiles, so each staged
-//   slab serves twice the rows.  Either way eight waves share a compute unit.
-// * Waves: 32-row groups x two key parities.  Per 32-key slab a wave
-//   computes S^T = K Q^T (v_mfma_f32_32x32x16_bf16), so each lane owns ONE
-//   query row: the online-softmax max, sum and rescale are lane-local plus a
-//   single cross-half exchange (v_permlane32_swap).  The probabilities feed
-//   O^T = V^T P^T straight from the S^T accumulator layout (no transpose of
-//   P); V^T operands come from transposing LDS reads.
-// * K/V staging: pairs of slabs (one per parity) go straight from global
-//   memory into a ring of LDS slots (direct LDS loads: no register round
-//   trip), two slots for 64-row tiles (two workgroups per compute unit),
-//   four for 128-row tiles.  Parities merge through LDS at the end.
+//   64-row tiles.  When many tiles re-read it (all-anchor training) it comes
+//   from L2: 128-row tiles, so each staged slab serves twice the rows.
+//   Either way two workgroups of four waves share a compute unit.
+// * Per 32-key slab a wave computes S^T = K Q^T (v_mfma_f32_32x32x16_bf16),
+//   so each lane owns ONE query row: the online-softmax max, sum and rescale
+//   are lane-local plus a single cross-half exchange (v_permlane32_swap).
+//   The probabilities feed O^T = V^T P^T straight from the S^T accumulator
+//   layout (no transpose of P); V^T operands come from transposing LDS reads.
+// * Keys go in pairs of 32-key slabs.  64-row tiles: waves are 32-row groups
+//   x two key parities (one slab of each pair per wave; the parities merge
+//   through LDS at the end), so a streaming tile still has four waves.
+//   128-row tiles: one wave per 32-row group takes both slabs of a pair, as
+//   two independent S^T chains and one 64-key softmax step, with the first
+//   slab's P.V product issued before the second slab's exponentials.
+// * K/V staging: each pair goes straight from global memory into a two-slot
+//   ring in LDS (direct LDS loads: no register round trip).
 #include "common.h"
 
 using namespace dspark;
@@ -135,18 +138,15 @@ __device__ __forceinline__ f32x16 qk_slab(const Src& sl, const u32x4* qf) {
   return sc;
 }
 
-// Online-softmax update of this lane's row with the scores sc of slab s.
-template <int D, class Src>
-__device__ __forceinline__ void softmax_pv(const Params& p, const Item& it, int s, f32x16 sc, const Src& sl,
-                                           bool kept, int lim, int ua, int a_lo, float c, float& m, float& l,
-                                           f32x16* o) {
-  constexpr int NJ = D / 32;
+// Scores of slab s that this lane's row may not see become -inf: context
+// keys below min(chunk end, anchor), own keys of its block only (one gamma
+// range).  Slabs that every row of the wave sees whole are left alone.
+__device__ __forceinline__ void mask_scores(const Params& p, const Item& it, int s, bool kept, int lim, int ua,
+                                            int a_lo, f32x16& sc) {
   const bool own = s >= it.n_ctx_slabs;
   const int j0 = own ? 0 : it.cbeg + s * 32;
   const int os = own ? (s - it.n_ctx_slabs) * 32 : 0;
-  // visible keys of this lane's row in this slab: context keys below
-  // min(chunk end, anchor), own keys of its block only (one gamma range)
-  int vlo, vhi;
+  int vlo, vhi;  // visible key slots: vlo <= slot < vhi
   if (!own) {
     vlo = -1 - j0;
     vhi = kept ? min(it.cend, lim) - j0 : 0;
@@ -154,7 +154,6 @@ __device__ __forceinline__ void softmax_pv(const Params& p, const Item& it, int 
     vlo = (ua - a_lo) * p.gamma - os;
     vhi = kept ? vlo + p.gamma : vlo;
   }
-  // slabs that every row of the wave sees whole need no masking
   if (!__all(vlo <= 0 && vhi >= 32)) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -162,6 +161,15 @@ __device__ __forceinline__ void softmax_pv(const Params& p, const Item& it, int 
       sc[i] = (ks >= vlo && ks < vhi) ? sc[i] : -INFINITY;
     }
   }
+}
+
+// Online-softmax update of this lane's row with the scores sc of slab s.
+template <int D, class Src>
+__device__ __forceinline__ void softmax_pv(const Params& p, const Item& it, int s, f32x16 sc, const Src& sl,
+                                           bool kept, int lim, int ua, int a_lo, float c, float& m, float& l,
+                                           f32x16* o) {
+  constexpr int NJ = D / 32;
+  mask_scores(p, it, s, kept, lim, ua, a_lo, sc);
   float smax = sc[0];
 #pragma unroll
   for (int i = 1; i < 16; ++i) smax = fmaxf(smax, sc[i]);
@@ -203,6 +211,94 @@ __device__ __forceinline__ void compute_slab(const Params& p, const Item& it, in
                                              const u32x4* qf, bool kept, int lim, int ua, int a_lo,
                                              float c, float& m, float& l, f32x16* o) {
   softmax_pv<D>(p, it, s, qk_slab<D>(sl, qf), sl, kept, lim, ua, a_lo, c, m, l, o);
+}
+
+// Both slabs of a pair (s0 and s0 + 1) for one wave: the two S^T products
+// are independent chains, one online-softmax step covers all 64 keys (one
+// maximum exchange and one rescale decision), and the P.V product of the
+// first slab is issued before the exponentials of the second, so the matrix
+// cores work while the vector ALU does.  A pair past the last slab (odd slab
+// count) is fully masked; its ring copy repeats the last slab, so its
+// operands are finite.
+template <int D, class Src>
+__device__ __forceinline__ void compute_pair(const Params& p, const Item& it, int s0, int nslab, const Src& sa,
+                                             const Src& sb, const u32x4* qf, bool kept, int lim, int ua,
+                                             int a_lo, float c, float& m, float& l, f32x16* o) {
+  constexpr int NJ = D / 32;
+  f32x16 x, y;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) { x[i] = 0.f; y[i] = 0.f; }
+  // K operands are read one rank step ahead of their products (two
+  // operand sets; the scheduling groups below pin that order, which the
+  // scheduler would otherwise fold back to read-wait-multiply)
+  u32x4 ka[2], kb[2];
+  // the S^T products go out at raised priority: when both waves of a SIMD
+  // are ready, the one that feeds the matrix cores issues first
+  __builtin_amdgcn_s_setprio(1);
+  ka[0] = sa.k(0);
+  kb[0] = sb.k(0);
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) {
+    if (kk + 1 < D / 16) {
+      ka[(kk + 1) & 1] = sa.k(kk + 1);
+      kb[(kk + 1) & 1] = sb.k(kk + 1);
+    }
+    x = mfma32x32x16(ka[kk & 1], qf[kk], x);
+    y = mfma32x32x16(kb[kk & 1], qf[kk], y);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // reads of step 0
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) {
+    if (kk + 1 < D / 16) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // reads of step kk + 1
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                       // products of step kk
+  }
+  __builtin_amdgcn_s_setprio(0);
+  mask_scores(p, it, s0, kept, lim, ua, a_lo, x);
+  if (s0 + 1 < nslab) {
+    mask_scores(p, it, s0 + 1, kept, lim, ua, a_lo, y);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) y[i] = -INFINITY;
+  }
+  float smax = fmaxf(x[0], y[0]);
+#pragma unroll
+  for (int i = 1; i < 16; ++i) smax = fmaxf(smax, fmaxf(x[i], y[i]));
+  smax = half_combine_max(smax);
+  const bool grow = smax > m && (m == -INFINITY || (smax - m) * c > kLazyMax);
+  if (__any(grow)) {
+    const float mnew = grow ? smax : m;
+    const float alpha = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m - mnew) * c);
+    l *= alpha;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[j][r] *= alpha;
+    m = mnew;
+  }
+  const float mc = m == -INFINITY ? 0.f : m * c;
+  auto probs = [&](const f32x16& sc, u32x4* pb) -> float {
+    float ps = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) {
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[i], c, -mc));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[i + 1], c, -mc));
+      ps += p0 + p1;
+      pb[i / 8][(i % 8) / 2] = pack_bf16x2(p0, p1);
+    }
+    return ps;
+  };
+  u32x4 pa[2], pb[2];
+  float psum = probs(x, pa);
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) o[j] = mfma32x32x16(sa.v(t, j), pa[t], o[j]);
+  psum += probs(y, pb);
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) o[j] = mfma32x32x16(sb.v(t, j), pb[t], o[j]);
+  l += half_combine_add(psum);
 }
 
 // Head dim of accumulator register r of product j for a lane in half h.
@@ -363,6 +459,7 @@ struct SlabView {
   }
 };
 
+
 // K/V staging straight from global memory into LDS (global_load_lds_dwordx4,
 // no register round trip): one instruction moves 64 lanes x 16 bytes into
 // 1 KB of LDS, lane l to chunk base + l, so each lane fetches the piece
@@ -406,14 +503,15 @@ struct DmaPair {
 // One workgroup per tile of 32*RG query rows and one (request, KV head):
 // RG row groups x two key parities, one wave each; direct-to-LDS copies into
 // an NSLOT-slot ring keep the next NSLOT - 1 slab pairs in flight.
-template <int D, int RG, int NSLOT>
-__global__ __launch_bounds__(64 * 2 * RG) __attribute__((amdgpu_waves_per_eu(2, 2))) void block_attn_mfma(Params p) {
+template <int D, int RG, int NSLOT, int NPAR>
+__global__ __launch_bounds__(64 * NPAR * RG) __attribute__((amdgpu_waves_per_eu(2, 2))) void block_attn_mfma(Params p) {
   using Rg = Ring<D>;
   constexpr int NJ = D / 32;
   constexpr int KK = D / 16;
-  constexpr int NT = 64 * 2 * RG;  // RG row groups x two key parities, one wave each
-  constexpr int kMergeBytes = RG * (D + 2) * 32 * 4;
+  constexpr int NT = 64 * NPAR * RG;  // RG row groups x NPAR key parities, one wave each
+  constexpr int kMergeBytes = NPAR == 2 ? RG * (D + 2) * 32 * 4 : 0;
   static_assert(NSLOT >= 2, "at least one pair in flight");
+  static_assert(NPAR == 1 || NPAR == 2, "one wave per pair or per slab");
   constexpr int kRingBytes = NSLOT * 2 * Rg::kSlotBytes;
   __shared__ __align__(16) unsigned char ring[kRingBytes > kMergeBytes ? kRingBytes : kMergeBytes];
 
@@ -438,7 +536,7 @@ __global__ __launch_bounds__(64 * 2 * RG) __attribute__((amdgpu_waves_per_eu(2, 
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int rg = wave % RG, par = wave / RG;
+  const int rg = wave % RG, par = NPAR == 2 ? wave / RG : 0;
   const int h = lane >> 5, r32 = lane & 31;
   const int u = u0 + rg * 32 + r32;
   const bool row_ok = u < p.nrows;
@@ -496,9 +594,9 @@ __global__ __launch_bounds__(64 * 2 * RG) __attribute__((amdgpu_waves_per_eu(2, 
     //      repeat the last slab (from L2), so the count is exact.
     using Dp = DmaPair<D, NT>;
     auto dslot = [&](int i) { return ring + (i % NSLOT) * 2 * Rg::kSlotBytes; };
-    auto dview = [&](int i) {
+    auto dview = [&](int i, int q) {
       unsigned char* sl = dslot(i);
-      return SlabView<D>(sl + par * Rg::kTensorBytes, sl + Rg::kSlotBytes + par * Rg::kTensorBytes, h, r32);
+      return SlabView<D>(sl + q * Rg::kTensorBytes, sl + Rg::kSlotBytes + q * Rg::kTensorBytes, h, r32);
     };
     if (npairs > 0) {
 #pragma unroll
@@ -507,29 +605,35 @@ __global__ __launch_bounds__(64 * 2 * RG) __attribute__((amdgpu_waves_per_eu(2, 
         wait_vmcnt<Dp::kPerPair * (NSLOT - 2)>();
         block_barrier();
         Dp::issue(st, i + NSLOT - 1, dslot(i + NSLOT - 1), wave, lane);
-        const int s = 2 * i + par;
-        if (s < nslab) compute_slab<D>(p, it, s, dview(i), qf, kept, lim, ua, a_lo, c, m, l, o);
+        if constexpr (NPAR == 2) {
+          const int s = 2 * i + par;
+          if (s < nslab) compute_slab<D>(p, it, s, dview(i, par), qf, kept, lim, ua, a_lo, c, m, l, o);
+        } else {
+          compute_pair<D>(p, it, 2 * i, nslab, dview(i, 0), dview(i, 1), qf, kept, lim, ua, a_lo, c, m, l, o);
+        }
       }
       wait_vmcnt<0>();
       block_barrier();  // every copy has landed and every wave is done with the ring
     }
   }
 
-  // ---- merge the two key parities of each row group through LDS (the ring
-  //      is free after the loop's last barrier)
-  float* mrg = (float*)ring;  // [RG row groups][D + 2][32]
-  auto at = [&](int g, int d, int r) -> float& { return mrg[((size_t)g * (D + 2) + d) * 32 + r]; };
-  if (npairs == 0) __syncthreads();
-  if (par == 1) {
+  if constexpr (NPAR == 1) {
+    if (!row_ok) return;
+  } else {
+    // ---- merge the two key parities of each row group through LDS (the ring
+    //      is free after the loop's last barrier)
+    float* mrg = (float*)ring;  // [RG row groups][D + 2][32]
+    auto at = [&](int g, int d, int r) -> float& { return mrg[((size_t)g * (D + 2) + d) * 32 + r]; };
+    if (npairs == 0) __syncthreads();
+    if (par == 1) {
 #pragma unroll
-    for (int j = 0; j < NJ; ++j)
+      for (int j = 0; j < NJ; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) at(rg, head_dim(r, j, h), r32) = o[j][r];
-    if (h == 0) { at(rg, D, r32) = m; at(rg, D + 1, r32) = l; }
-  }
-  __syncthreads();
-  if (par == 1 || !row_ok) return;
-  {
+        for (int r = 0; r < 16; ++r) at(rg, head_dim(r, j, h), r32) = o[j][r];
+      if (h == 0) { at(rg, D, r32) = m; at(rg, D + 1, r32) = l; }
+    }
+    __syncthreads();
+    if (par == 1 || !row_ok) return;
     const float m1 = at(rg, D, r32), l1 = at(rg, D + 1, r32);
     const float mn = fmaxf(m, m1);
     const float mu = mn == -INFINITY ? 0.f : mn;
@@ -713,13 +817,13 @@ extern "C" int dspark_block_attention(const void* q, const void* k_ctx, const vo
     int32_t* order = (int32_t*)ws;
     hipLaunchKernelGGL(attn_plan_kernel, dim3(1), dim3(1024), 0, s, p, order);
     p.order = order;
-    const dim3 grid((unsigned)sh.tiles), block(deep ? 256 : 512);
+    const dim3 grid((unsigned)sh.tiles), block(256);
     if (D == 128) {
-      if (deep) hipLaunchKernelGGL((block_attn_mfma<128, 2, 2>), grid, block, 0, s, p);
-      else hipLaunchKernelGGL((block_attn_mfma<128, 4, 4>), grid, block, 0, s, p);
+      if (deep) hipLaunchKernelGGL((block_attn_mfma<128, 2, 2, 2>), grid, block, 0, s, p);
+      else hipLaunchKernelGGL((block_attn_mfma<128, 4, 2, 1>), grid, block, 0, s, p);
     } else {
-      if (deep) hipLaunchKernelGGL((block_attn_mfma<64, 2, 2>), grid, block, 0, s, p);
-      else hipLaunchKernelGGL((block_attn_mfma<64, 4, 4>), grid, block, 0, s, p);
+      if (deep) hipLaunchKernelGGL((block_attn_mfma<64, 2, 2, 2>), grid, block, 0, s, p);
+      else hipLaunchKernelGGL((block_attn_mfma<64, 4, 2, 1>), grid, block, 0, s, p);
     }
   } else {
     const int64_t nb = (int64_t)B * A * Hq;
