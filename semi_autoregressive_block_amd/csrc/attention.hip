@@ -38,9 +38,9 @@
 // * Keys go in pairs of 32-key slabs.  64-row tiles: waves are 32-row groups
 //   x two key parities (one slab of each pair per wave; the parities merge
 //   through LDS at the end), so a streaming tile still has four waves.
-//   128-row tiles: one wave per 32-row group takes both slabs of a pair, as
-//   two independent S^T chains and one 64-key softmax step, with the first
-//   slab's P.V product issued before the second slab's exponentials.
+//   128-row tiles: one wave per 32-row group takes both slabs of a pair: two
+//   S^T chains back to back, then a softmax step and P.V product per slab,
+//   so the vector and matrix work of the two slabs overlap within the wave.
 // * K/V staging: each pair goes straight from global memory into a two-slot
 //   ring in LDS (direct LDS loads: no register round trip).
 #include "common.h"
@@ -213,91 +213,86 @@ __device__ __forceinline__ void compute_slab(const Params& p, const Item& it, in
   softmax_pv<D>(p, it, s, qk_slab<D>(sl, qf), sl, kept, lim, ua, a_lo, c, m, l, o);
 }
 
-// Both slabs of a pair (s0 and s0 + 1) for one wave: the two S^T products
-// are independent chains, one online-softmax step covers all 64 keys (one
-// maximum exchange and one rescale decision), and the P.V product of the
-// first slab is issued before the exponentials of the second, so the matrix
-// cores work while the vector ALU does.  A pair past the last slab (odd slab
-// count) is fully masked; its ring copy repeats the last slab, so its
-// operands are finite.
-template <int D, class Src>
+// Both slabs of a pair (s0 and s0 + 1) for one wave.  The two S^T products
+// go out back to back as two chains (slab s0's first), then each slab takes
+// its own online-softmax step and P.V product: slab s0's exponentials run
+// while the matrix cores still work on slab s0 + 1's S^T, and slab s0 + 1's
+// exponentials while they work on slab s0's P.V.  A pair past the last slab
+// (odd slab count) has no second step; its ring copy repeats the last slab.
+// after_qk() runs once the S^T products are issued (the caller's ring refill:
+// a copy that stalls on a full load queue then overlaps matrix work).
+template <int D, class Src, class AfterQK>
 __device__ __forceinline__ void compute_pair(const Params& p, const Item& it, int s0, int nslab, const Src& sa,
                                              const Src& sb, const u32x4* qf, bool kept, int lim, int ua,
-                                             int a_lo, float c, float& m, float& l, f32x16* o) {
+                                             int a_lo, float c, float& m, float& l, f32x16* o,
+                                             AfterQK after_qk) {
   constexpr int NJ = D / 32;
+  constexpr int KK = D / 16;
   f32x16 x, y;
 #pragma unroll
   for (int i = 0; i < 16; ++i) { x[i] = 0.f; y[i] = 0.f; }
-  // K operands are read one rank step ahead of their products (two
-  // operand sets; the scheduling groups below pin that order, which the
-  // scheduler would otherwise fold back to read-wait-multiply)
-  u32x4 ka[2], kb[2];
-  // the S^T products go out at raised priority: when both waves of a SIMD
-  // are ready, the one that feeds the matrix cores issues first
+  // K operands are read one rank step ahead of their products (two operand
+  // sets; the scheduling groups below pin read, product, read, product ...,
+  // which the scheduler would otherwise fold back to read-wait-multiply).
+  // The products go out at raised priority: when both waves of a SIMD are
+  // ready, the one that feeds the matrix cores issues first.
+  u32x4 kx[2], ky[2];
   __builtin_amdgcn_s_setprio(1);
-  ka[0] = sa.k(0);
-  kb[0] = sb.k(0);
+  kx[0] = sa.k(0);
 #pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) {
-    if (kk + 1 < D / 16) {
-      ka[(kk + 1) & 1] = sa.k(kk + 1);
-      kb[(kk + 1) & 1] = sb.k(kk + 1);
-    }
-    x = mfma32x32x16(ka[kk & 1], qf[kk], x);
-    y = mfma32x32x16(kb[kk & 1], qf[kk], y);
+  for (int kk = 0; kk < KK; ++kk) {
+    if (kk + 1 < KK) kx[(kk + 1) & 1] = sa.k(kk + 1);
+    else ky[0] = sb.k(0);
+    x = mfma32x32x16(kx[kk & 1], qf[kk], x);
   }
-  __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // reads of step 0
 #pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) {
-    if (kk + 1 < D / 16) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // reads of step kk + 1
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                       // products of step kk
+  for (int kk = 0; kk < KK; ++kk) {
+    if (kk + 1 < KK) ky[(kk + 1) & 1] = sb.k(kk + 1);
+    y = mfma32x32x16(ky[kk & 1], qf[kk], y);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // first read
+#pragma unroll
+  for (int kk = 0; kk < 2 * KK; ++kk) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // next read (the last group is empty)
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // product
   }
   __builtin_amdgcn_s_setprio(0);
-  mask_scores(p, it, s0, kept, lim, ua, a_lo, x);
-  if (s0 + 1 < nslab) {
-    mask_scores(p, it, s0 + 1, kept, lim, ua, a_lo, y);
-  } else {
+  after_qk();
+  float psum = 0.f;
+  auto step = [&](f32x16& sc, int s, const Src& sl) {
+    mask_scores(p, it, s, kept, lim, ua, a_lo, sc);
+    float smax = sc[0];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) y[i] = -INFINITY;
-  }
-  float smax = fmaxf(x[0], y[0]);
+    for (int i = 1; i < 16; ++i) smax = fmaxf(smax, sc[i]);
+    smax = half_combine_max(smax);
+    const bool grow = smax > m && (m == -INFINITY || (smax - m) * c > kLazyMax);
+    if (__any(grow)) {
+      const float mnew = grow ? smax : m;
+      const float alpha = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m - mnew) * c);
+      l *= alpha;
+      psum *= alpha;
 #pragma unroll
-  for (int i = 1; i < 16; ++i) smax = fmaxf(smax, fmaxf(x[i], y[i]));
-  smax = half_combine_max(smax);
-  const bool grow = smax > m && (m == -INFINITY || (smax - m) * c > kLazyMax);
-  if (__any(grow)) {
-    const float mnew = grow ? smax : m;
-    const float alpha = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m - mnew) * c);
-    l *= alpha;
+      for (int j = 0; j < NJ; ++j)
 #pragma unroll
-    for (int j = 0; j < NJ; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[j][r] *= alpha;
-    m = mnew;
-  }
-  const float mc = m == -INFINITY ? 0.f : m * c;
-  auto probs = [&](const f32x16& sc, u32x4* pb) -> float {
-    float ps = 0.f;
+        for (int r = 0; r < 16; ++r) o[j][r] *= alpha;
+      m = mnew;
+    }
+    const float mc = m == -INFINITY ? 0.f : m * c;
+    u32x4 pb[2];
 #pragma unroll
     for (int i = 0; i < 16; i += 2) {
       const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[i], c, -mc));
       const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[i + 1], c, -mc));
-      ps += p0 + p1;
+      psum += p0 + p1;
       pb[i / 8][(i % 8) / 2] = pack_bf16x2(p0, p1);
     }
-    return ps;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) o[j] = mfma32x32x16(sl.v(t, j), pb[t], o[j]);
   };
-  u32x4 pa[2], pb[2];
-  float psum = probs(x, pa);
-#pragma unroll
-  for (int t = 0; t < 2; ++t)
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) o[j] = mfma32x32x16(sa.v(t, j), pa[t], o[j]);
-  psum += probs(y, pb);
-#pragma unroll
-  for (int t = 0; t < 2; ++t)
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) o[j] = mfma32x32x16(sb.v(t, j), pb[t], o[j]);
+  step(x, s0, sa);
+  if (s0 + 1 < nslab) step(y, s0 + 1, sb);  // uniform
   l += half_combine_add(psum);
 }
 
@@ -590,7 +585,9 @@ __global__ __launch_bounds__(64 * NPAR * RG) __attribute__((amdgpu_waves_per_eu(
     //      i+NSLOT-1 are being copied in.  Iteration i: wait for this wave's
     //      copies of pair i, meet the other waves (their copies of pair i
     //      are in, and they are done with pair i-1, whose slot is refilled
-    //      next), issue pair i+NSLOT-1, compute pair i.  Copies past the end
+    //      next), compute pair i and issue pair i+NSLOT-1 (before the
+    //      products of a parity wave, after the S^T products of a pair
+    //      wave).  Copies past the end
     //      repeat the last slab (from L2), so the count is exact.
     using Dp = DmaPair<D, NT>;
     auto dslot = [&](int i) { return ring + (i % NSLOT) * 2 * Rg::kSlotBytes; };
@@ -604,12 +601,14 @@ __global__ __launch_bounds__(64 * NPAR * RG) __attribute__((amdgpu_waves_per_eu(
       for (int i = 0; i < npairs; ++i) {
         wait_vmcnt<Dp::kPerPair * (NSLOT - 2)>();
         block_barrier();
-        Dp::issue(st, i + NSLOT - 1, dslot(i + NSLOT - 1), wave, lane);
+        auto refill = [&]() { Dp::issue(st, i + NSLOT - 1, dslot(i + NSLOT - 1), wave, lane); };
         if constexpr (NPAR == 2) {
+          refill();
           const int s = 2 * i + par;
           if (s < nslab) compute_slab<D>(p, it, s, dview(i, par), qf, kept, lim, ua, a_lo, c, m, l, o);
         } else {
-          compute_pair<D>(p, it, 2 * i, nslab, dview(i, 0), dview(i, 1), qf, kept, lim, ua, a_lo, c, m, l, o);
+          compute_pair<D>(p, it, 2 * i, nslab, dview(i, 0), dview(i, 1), qf, kept, lim, ua, a_lo, c, m, l, o,
+                          refill);
         }
       }
       wait_vmcnt<0>();
