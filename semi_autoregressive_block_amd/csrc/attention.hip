@@ -231,31 +231,34 @@ __device__ __forceinline__ void compute_pair(const Params& p, const Item& it, in
   f32x16 x, y;
 #pragma unroll
   for (int i = 0; i < 16; ++i) { x[i] = 0.f; y[i] = 0.f; }
-  // K operands are read one rank step ahead of their products (two operand
-  // sets; the scheduling groups below pin read, product, read, product ...,
-  // which the scheduler would otherwise fold back to read-wait-multiply).
+  // Slab s0's K operands are read one rank step ahead of its products (two
+  // operand sets) and slab s0 + 1's all during them; the scheduling groups
+  // below pin that order, which the scheduler would otherwise fold back to
+  // read-wait-multiply.
   // The products go out at raised priority: when both waves of a SIMD are
   // ready, the one that feeds the matrix cores issues first.
-  u32x4 kx[2], ky[2];
+  u32x4 kx[2], ky[KK];
   __builtin_amdgcn_s_setprio(1);
   kx[0] = sa.k(0);
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk) {
     if (kk + 1 < KK) kx[(kk + 1) & 1] = sa.k(kk + 1);
-    else ky[0] = sb.k(0);
     x = mfma32x32x16(kx[kk & 1], qf[kk], x);
+    ky[kk] = sb.k(kk);
   }
+  __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // first read of slab s0
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk) {
-    if (kk + 1 < KK) ky[(kk + 1) & 1] = sb.k(kk + 1);
-    y = mfma32x32x16(ky[kk & 1], qf[kk], y);
+    if (kk + 1 < KK) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // next read of s0
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                   // product kk of s0
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                   // read kk of s0 + 1
   }
-  __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // first read
+  // slab s0's last product is used here, so it cannot sink below slab
+  // s0 + 1's chain (it would delay slab s0's softmax step by a whole chain)
+  asm volatile("" ::"v"(x[0]));
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int kk = 0; kk < 2 * KK; ++kk) {
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // next read (the last group is empty)
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // product
-  }
+  for (int kk = 0; kk < KK; ++kk) y = mfma32x32x16(ky[kk], qf[kk], y);
   __builtin_amdgcn_s_setprio(0);
   after_qk();
   float psum = 0.f;
