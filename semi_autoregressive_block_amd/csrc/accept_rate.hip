@@ -43,7 +43,8 @@ namespace {
 constexpr int kDataWaves = 3;
 constexpr int kDataThreads = kDataWaves * kWave;  // threads that hold the row slice
 constexpr int kThreads = kDataThreads + kWave;    // plus the exchange wave
-constexpr int kVec = 3;                           // 16-byte vectors per data thread per tensor
+constexpr int kVec = 4;                           // 16-byte vectors per data thread per tensor (a 24 KB
+                                                  // slice of both tensors; three workgroups per CU)
 constexpr int kChunkVec = kDataThreads * kVec;    // vectors of one tensor per workgroup and row
 constexpr int kMaxG = 2 * kWave;                  // two cluster members per exchange lane
 constexpr float kLog2e = 1.4426950408889634f;

@@ -56,8 +56,8 @@ def test_workspace_queries(lib):
     assert L.dspark_markov_sample_workspace_bytes(600, 2, 151936, 256, 1) == 2 * 16 * 8192
     # accept rate: one float share per (row, cluster member) + two 16-byte
     # statistics slots per member of every resident cluster + the error word;
-    # V = 151936 bf16 is 18992 vectors per row, 576 per member -> G = 33
-    G, rows = 33, 4 * 512 * 8
+    # V = 151936 bf16 is 18992 vectors per row, 768 per member -> G = 25
+    G, rows = 25, 4 * 512 * 8
     assert L.dspark_accept_rate_workspace_bytes(4, 512, 8, 151936, 1) == \
         rows * G * 4 + (256 * 16 // G) * 2 * G * 16 + 64
     assert L.dspark_accept_rate_workspace_bytes(1, 1, 3, 1001, 1) == 0  # row-wise path
