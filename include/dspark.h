@@ -9,6 +9,11 @@
  *   dspark_accept_rate      TV-distance accept rate (+ optional tau)
  *   dspark_eval_mask        cumulative-product eval mask
  *
+ * and two training-side neighbours of the same steps:
+ *
+ *   dspark_markov_block_logits  teacher-forced Markov logits of a whole block
+ *   dspark_l1_loss              L1 (TV) alignment loss, its gradient, tau_greedy
+ *
  * Sources (cited per entry point): page 1 = "03 · DSpark 建模：Markov 与
  * Confidence" (devpress.csdn.net), page 2 = "从 DFlash 到 dLLM Self-Spec
  * （三）" (r00kie-liu.github.io), page 4 = "DSpark 深度解读" (juejin.cn).
@@ -207,6 +212,53 @@ int dspark_eval_mask(const int32_t* anchor_pos, const uint8_t* keep_mask,
                      const int32_t* seq_lens, const uint8_t* loss_mask, uint8_t* eval_mask,
                      int B, int A, int gamma, int S_stride,
                      int32_t* dev_status, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Teacher-forced Markov block logits (page 1 §3.7: apply_block_logits in
+ * training, every position's bias from its given previous token; page 4
+ * §3.3; optional soft cap from page 1 §3.12).  For rows n = 0 .. N-1:
+ *
+ *     logits[n, v] = base[n, v] + sum_j W1[prev[n], j] * W2[j, v]
+ *     logits       = softcap * tanh(logits / softcap)      if softcap > 0
+ *
+ *   base_logits   [N, V] float32 (N = B * A * gamma for a training batch)
+ *   w1 [V, r], w2 [r, V]   wdtype (bf16 or float32); r <= 1024
+ *   prev          [N] int32 teacher tokens (outside [0, V): row uses token 0
+ *                 and DSPARK_STATUS_BAD_TOKEN is set)
+ *   logits        [N, V] float32 (out)
+ *   argmax_tokens [N] int32 (out, nullable): argmax_v logits, lowest index on ties
+ * Workspace from dspark_markov_block_logits_workspace_bytes (8-byte aligned).
+ * ---------------------------------------------------------------------- */
+size_t dspark_markov_block_logits_workspace_bytes(int N, int V, int r, int wdtype);
+int dspark_markov_block_logits(const float* base_logits, const void* w1, const void* w2,
+                               const int32_t* prev, float* logits, int32_t* argmax_tokens,
+                               int N, int V, int r, int wdtype, float softcap,
+                               void* ws, size_t ws_bytes, int32_t* dev_status, void* stream);
+
+/* ------------------------------------------------------------------------
+ * L1 (total-variation) alignment loss, its gradient and tau_greedy (page 1
+ * §3.9, the paper's Eq. 10, and §3.10; page 4 §4.1).  Row n = position k of
+ * block (b, a); p = softmax(draft[n]), q = softmax(target[n]) in float32:
+ *
+ *     l1[n]   = sum_v |p_v - q_v|
+ *     c[n]    = w_k m[n] / sum_n' w_k' m[n'],  w_k = exp(-k / decay)
+ *     *loss   = sum_n c[n] l1[n]                        (0 if no m[n] is set)
+ *     grad[n, v] = c[n] p_v (s_v - sum_u s_u p_u),  s = sign(p - q)
+ *     tau_greedy[b, a] = 1 + sum_k prod_{i <= k} [argmax draft == argmax target]_i m_i
+ *
+ *   draft_logits, target_logits [B, A, gamma, V] dtype (bf16 or float32)
+ *   eval_mask  [B, A, gamma] uint8 (nullable = all valid)
+ *   loss       device float[1] (out, required)
+ *   row_l1     [B, A, gamma] float32 (out, nullable)
+ *   grad       [B, A, gamma, V] float32 (out, nullable: the backward pass is skipped)
+ *   tau_greedy [B, A] float32 (out, nullable)
+ * Limits: gamma <= 1024, decay > 0.  Workspace from dspark_l1_loss_workspace_bytes.
+ * ---------------------------------------------------------------------- */
+size_t dspark_l1_loss_workspace_bytes(int B, int A, int gamma);
+int dspark_l1_loss(const void* draft_logits, const void* target_logits, const uint8_t* eval_mask,
+                   float decay, float* loss, float* row_l1, float* grad, float* tau_greedy,
+                   int B, int A, int gamma, int V, int dtype,
+                   void* ws, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -12,6 +12,8 @@ Functions (same names and argument meaning as the C entry points):
 * ``markov_sample``    — Markov-head gamma-step sampler
 * ``accept_rate``      — TV accept rate (+ tau)
 * ``eval_mask``        — cumulative-product eval mask
+* ``markov_block_logits`` — teacher-forced Markov logits of a whole block
+* ``l1_loss``          — L1 (TV) alignment loss, its gradient, tau_greedy
 """
 
 from __future__ import annotations
@@ -26,7 +28,8 @@ _LIB = _lib.load()
 
 __all__ = ["block_attention", "markov_sample", "accept_rate", "eval_mask",
            "block_attention_workspace_bytes", "markov_sample_workspace_bytes",
-           "accept_rate_workspace_bytes", "set_wait_limit", "last_error", "version",
+           "accept_rate_workspace_bytes", "markov_block_logits", "markov_block_logits_workspace_bytes",
+           "l1_loss", "l1_loss_workspace_bytes", "set_wait_limit", "last_error", "version",
            "DSparkError"]
 
 
@@ -216,6 +219,85 @@ def accept_rate(draft, target, *, eval_mask=None, want_tau=False, accept=None, t
     if rc != 0:
         raise DSparkError(rc, "accept_rate")
     return accept, tau
+
+
+def markov_block_logits_workspace_bytes(N, V, r, wdtype=_lib.BF16) -> int:
+    return int(_LIB.dspark_markov_block_logits_workspace_bytes(N, V, r, wdtype))
+
+
+def markov_block_logits(base, w1, w2, prev, *, softcap=0.0, logits=None, want_tokens=False, tokens=None,
+                        status=None, workspace=None):
+    """Teacher-forced Markov logits.  base [N, V] float32; w1 [V, r]; w2 [r, V]
+    (bf16 or float32); prev [N] int32.  Returns (logits [N, V] float32,
+    argmax tokens [N] int32 or None)."""
+    dev = base.device
+    _check(base, "base", torch.float32, ndim=2)
+    N, V = base.shape
+    _check(w1, "w1", (torch.bfloat16, torch.float32), dev, 2)
+    _check(w2, "w2", w1.dtype, dev, 2)
+    r = w1.shape[1]
+    if tuple(w1.shape) != (V, r) or tuple(w2.shape) != (r, V):
+        raise ValueError(f"w1 must be [V, r] and w2 [r, V]; got {tuple(w1.shape)}, {tuple(w2.shape)}")
+    _check(prev, "prev", torch.int32, dev, 1)
+    if prev.shape[0] != N:
+        raise ValueError("prev must have N entries")
+    if logits is None:
+        logits = torch.empty_like(base)
+    _check(logits, "logits", torch.float32, dev, 2)
+    if tokens is None and want_tokens:
+        tokens = torch.empty((N,), dtype=torch.int32, device=dev)
+    if tokens is not None:
+        _check(tokens, "tokens", torch.int32, dev, 1)
+    if status is not None:
+        _check(status, "status", torch.int32, dev)
+    wdt = _dt(w1)
+    ws, wsb = _workspace(markov_block_logits_workspace_bytes(N, V, r, wdt), dev, workspace)
+    rc = _LIB.dspark_markov_block_logits(_ptr(base), _ptr(w1), _ptr(w2), _ptr(prev), _ptr(logits), _ptr(tokens),
+                                         N, V, r, wdt, float(softcap), _ptr(ws), wsb, _ptr(status), _stream(dev))
+    if rc != 0:
+        raise DSparkError(rc, "markov_block_logits")
+    return logits, tokens
+
+
+def l1_loss_workspace_bytes(B, A, gamma) -> int:
+    return int(_LIB.dspark_l1_loss_workspace_bytes(B, A, gamma))
+
+
+def l1_loss(draft, target, *, eval_mask=None, decay=4.0, want_grad=False, want_rows=False,
+            want_tau_greedy=False, loss=None, grad=None, row_l1=None, tau_greedy=None, workspace=None):
+    """L1 (TV) alignment loss.  draft, target [B, A, gamma, V] (bf16 or
+    float32); eval_mask [B, A, gamma] uint8 (optional).  Returns (loss [1],
+    grad [B, A, gamma, V] float32 or None, row_l1 [B, A, gamma] or None,
+    tau_greedy [B, A] or None)."""
+    dev = draft.device
+    _check(draft, "draft", (torch.bfloat16, torch.float32), ndim=4)
+    _check(target, "target", draft.dtype, dev, 4)
+    if target.shape != draft.shape:
+        raise ValueError("draft and target shapes differ")
+    B, A, gamma, V = draft.shape
+    if eval_mask is not None:
+        _check(eval_mask, "eval_mask", torch.uint8, dev, 3)
+    if loss is None:
+        loss = torch.empty((1,), dtype=torch.float32, device=dev)
+    _check(loss, "loss", torch.float32, dev, 1)
+    if grad is None and want_grad:
+        grad = torch.empty((B, A, gamma, V), dtype=torch.float32, device=dev)
+    if grad is not None:
+        _check(grad, "grad", torch.float32, dev, 4)
+    if row_l1 is None and want_rows:
+        row_l1 = torch.empty((B, A, gamma), dtype=torch.float32, device=dev)
+    if row_l1 is not None:
+        _check(row_l1, "row_l1", torch.float32, dev, 3)
+    if tau_greedy is None and want_tau_greedy:
+        tau_greedy = torch.empty((B, A), dtype=torch.float32, device=dev)
+    if tau_greedy is not None:
+        _check(tau_greedy, "tau_greedy", torch.float32, dev, 2)
+    ws, wsb = _workspace(l1_loss_workspace_bytes(B, A, gamma), dev, workspace)
+    rc = _LIB.dspark_l1_loss(_ptr(draft), _ptr(target), _ptr(eval_mask), float(decay), _ptr(loss), _ptr(row_l1),
+                             _ptr(grad), _ptr(tau_greedy), B, A, gamma, V, _dt(draft), _ptr(ws), wsb, _stream(dev))
+    if rc != 0:
+        raise DSparkError(rc, "l1_loss")
+    return loss, grad, row_l1, tau_greedy
 
 
 def set_wait_limit(polls: int) -> None:

@@ -112,7 +112,9 @@ __device__ __forceinline__ void fold_key_global(uint64_t* keys, int row, int R, 
 constexpr int kTileCols = 64;
 constexpr int kLdsRow = 144;  // bytes per staged W2 row of a tile (128 + 16: spreads LDS banks)
 
-template <int NW, int KS, int NS, bool FL>
+// SC: soft-capped logits c * tanh(l / c) (block logits only; sampling is then
+// greedy and the temperature argument carries 1 / c).
+template <int NW, int KS, int NS, bool FL, bool SC = false>
 __global__ __launch_bounds__(64 * NW) void markov_step_mfma(
     const float* __restrict__ base, const uint16_t* __restrict__ w1,
     const uint16_t* __restrict__ w2, const int32_t* __restrict__ first_prev,
@@ -245,7 +247,11 @@ __global__ __launch_bounds__(64 * NW) void markov_step_mfma(
     for (int j = 0; j < 4; ++j) {
       const int64_t vj = v0 + 16 * j;
       const bool colok = t < ntile && vj < V;
-      const f32x4 l = acc[j] + bl[j];
+      f32x4 l = acc[j] + bl[j];
+      if constexpr (SC) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) l[e] = tanhf(l[e] * invT) / invT;
+      }
       if (step_logits && colok && row < R)
         *(f32x4*)(step_logits + ((int64_t)row * gamma + step) * V + vj) = l;
       f32x4 z = l;
@@ -306,7 +312,7 @@ __global__ __launch_bounds__(64 * NW) void markov_step_mfma(
 // 16 rows per pass with E in LDS, fp32 FMAs.
 constexpr int kRowChunk = 16;
 
-template <bool kBf16W>
+template <bool kBf16W, bool SC = false>
 __global__ __launch_bounds__(kThreads) void markov_step_valu(
     const float* __restrict__ base, const void* __restrict__ w1v, const void* __restrict__ w2v,
     const int32_t* __restrict__ first_prev, const uint64_t* __restrict__ keys_prev,
@@ -358,7 +364,8 @@ __global__ __launch_bounds__(kThreads) void markov_step_valu(
         const int row = row0 + i;
         if (row >= R) break;
         const int64_t off = ((int64_t)row * gamma + step) * V + v;
-        const float l = base[off] + acc[i];
+        float l = base[off] + acc[i];
+        if constexpr (SC) l = tanhf(l * invT) / invT;
         if (step_logits) step_logits[off] = l;
         float z = l;
         if (!greedy) {
@@ -428,18 +435,59 @@ hipError_t allow_lds_once(K kern, size_t bytes) {
   return e;
 }
 
-template <int NW, int KS, int NS, bool FL>
+template <int NW, int KS, int NS, bool FL, bool SC>
 hipError_t launch_mfma(int grid_x, int grid_y, hipStream_t s, const float* base, const uint16_t* w1,
                        const uint16_t* w2, const int32_t* first_prev, const uint64_t* kp,
                        uint64_t* ko, float* step_logits, int R, int gamma, int V, int r, int step,
                        float invT, int greedy, uint32_t slo, uint32_t shi, int32_t* st) {
   (void)r;
   const size_t shm = (size_t)2 * 32 * KS * kLdsRow + (FL ? (size_t)NW * 4096 : 0);
-  auto kern = markov_step_mfma<NW, KS, NS, FL>;
+  auto kern = markov_step_mfma<NW, KS, NS, FL, SC>;
   hipError_t e = allow_lds_once(kern, shm);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(grid_x, grid_y), dim3(64 * NW), shm, s, base, w1, w2, first_prev,
                      kp, ko, step_logits, R, gamma, V, r, step, invT, greedy, slo, shi, st);
+  return hipGetLastError();
+}
+
+
+// One step over R rows: the MFMA kernel for bf16 weights in aligned buffers
+// (up to 128 rows per workgroup, 8 waves, one compute unit each; up to 64
+// rows use 4 waves and two workgroups per compute unit), else the vector
+// kernel.
+template <bool SC>
+hipError_t launch_step(bool mfma_ok, bool bf, int cus, hipStream_t s, const float* base, const void* w1,
+                       const void* w2, const int32_t* first_prev, const uint64_t* kp, uint64_t* ko,
+                       float* step_logits, int R, int gamma, int V, int r, int step, float invT,
+                       int greedy, uint32_t slo, uint32_t shi, int32_t* st) {
+  if (mfma_ok) {
+    const bool wide = R > 64;
+    const int rows_per = wide ? 128 : 64;
+    const int gy = (R + rows_per - 1) / rows_per;
+    int gx = wide ? cus : 2 * cus;
+    const int64_t tiles = (V + 63) / 64;
+    if (gx > tiles) gx = (int)tiles;
+    if (gx < 1) gx = 1;
+    const uint16_t *a = (const uint16_t*)w1, *b = (const uint16_t*)w2;
+    if (wide)
+      return r <= 256 ? launch_mfma<8, 8, 2, true, SC>(gx, gy, s, base, a, b, first_prev, kp, ko, step_logits, R, gamma, V, r, step, invT, greedy, slo, shi, st)
+                      : launch_mfma<8, 16, 2, false, SC>(gx, gy, s, base, a, b, first_prev, kp, ko, step_logits, R, gamma, V, r, step, invT, greedy, slo, shi, st);
+    return r <= 256 ? launch_mfma<4, 8, 2, false, SC>(gx, gy, s, base, a, b, first_prev, kp, ko, step_logits, R, gamma, V, r, step, invT, greedy, slo, shi, st)
+                    : launch_mfma<4, 16, 2, false, SC>(gx, gy, s, base, a, b, first_prev, kp, ko, step_logits, R, gamma, V, r, step, invT, greedy, slo, shi, st);
+  }
+  const int gy = (R + kRowChunk - 1) / kRowChunk;
+  int gx = 2 * cus;
+  const int64_t quads = (V + 3) / 4;
+  if ((int64_t)gx * kThreads > quads) gx = (int)((quads + kThreads - 1) / kThreads);
+  if (gx < 1) gx = 1;
+  const size_t shm = (size_t)kRowChunk * r * 4 + kRowChunk * 8;
+  if (bf) {
+    (void)allow_lds_once(markov_step_valu<true, SC>, shm);
+    hipLaunchKernelGGL((markov_step_valu<true, SC>), dim3(gx, gy), dim3(kThreads), shm, s, base, w1, w2, first_prev, kp, ko, step_logits, R, gamma, V, r, step, invT, greedy, slo, shi, st);
+  } else {
+    (void)allow_lds_once(markov_step_valu<false, SC>, shm);
+    hipLaunchKernelGGL((markov_step_valu<false, SC>), dim3(gx, gy), dim3(kThreads), shm, s, base, w1, w2, first_prev, kp, ko, step_logits, R, gamma, V, r, step, invT, greedy, slo, shi, st);
+  }
   return hipGetLastError();
 }
 
@@ -489,43 +537,67 @@ extern "C" int dspark_markov_sample(const float* base_logits, const void* w1, co
   for (int step = 0; step < gamma; ++step) {
     const uint64_t* kp = step == 0 ? nullptr : keys + (int64_t)(step - 1) * keys_per_step(R);
     uint64_t* ko = keys + (int64_t)step * keys_per_step(R);
-    hipError_t e = hipSuccess;
-    if (mfma_ok) {
-      // up to 128 rows per workgroup (8 waves, one compute unit each); up to
-      // 64 rows use 4 waves and two workgroups per compute unit
-      const bool wide = R > 64;
-      const int rows_per = wide ? 128 : 64;
-      const int gy = (R + rows_per - 1) / rows_per;
-      int gx = wide ? cus : 2 * cus;
-      const int64_t tiles = (V + 63) / 64;
-      if (gx > tiles) gx = (int)tiles;
-      if (gx < 1) gx = 1;
-      if (wide)
-        e = r <= 256 ? launch_mfma<8, 8, 2, true>(gx, gy, s, base_logits, (const uint16_t*)w1, (const uint16_t*)w2, first_prev, kp, ko, step_logits, R, gamma, V, r, step, invT, greedy, slo, shi, dev_status)
-                     : launch_mfma<8, 16, 2, false>(gx, gy, s, base_logits, (const uint16_t*)w1, (const uint16_t*)w2, first_prev, kp, ko, step_logits, R, gamma, V, r, step, invT, greedy, slo, shi, dev_status);
-      else
-        e = r <= 256 ? launch_mfma<4, 8, 2, false>(gx, gy, s, base_logits, (const uint16_t*)w1, (const uint16_t*)w2, first_prev, kp, ko, step_logits, R, gamma, V, r, step, invT, greedy, slo, shi, dev_status)
-                     : launch_mfma<4, 16, 2, false>(gx, gy, s, base_logits, (const uint16_t*)w1, (const uint16_t*)w2, first_prev, kp, ko, step_logits, R, gamma, V, r, step, invT, greedy, slo, shi, dev_status);
-    } else {
-      const int gy = (R + kRowChunk - 1) / kRowChunk;
-      int gx = 2 * cus;
-      const int64_t quads = (V + 3) / 4;
-      if ((int64_t)gx * kThreads > quads) gx = (int)((quads + kThreads - 1) / kThreads);
-      if (gx < 1) gx = 1;
-      const size_t shm = (size_t)kRowChunk * r * 4 + kRowChunk * 8;
-      if (bf) {
-        (void)allow_lds_once(markov_step_valu<true>, shm);
-        hipLaunchKernelGGL(markov_step_valu<true>, dim3(gx, gy), dim3(kThreads), shm, s, base_logits, w1, w2, first_prev, kp, ko, step_logits, R, gamma, V, r, step, invT, greedy, slo, shi, dev_status);
-      } else {
-        (void)allow_lds_once(markov_step_valu<false>, shm);
-        hipLaunchKernelGGL(markov_step_valu<false>, dim3(gx, gy), dim3(kThreads), shm, s, base_logits, w1, w2, first_prev, kp, ko, step_logits, R, gamma, V, r, step, invT, greedy, slo, shi, dev_status);
-      }
-      e = hipGetLastError();
-    }
+    const hipError_t e = launch_step<false>(mfma_ok, bf, cus, s, base_logits, w1, w2, first_prev, kp, ko,
+                                            step_logits, R, gamma, V, r, step, invT, greedy, slo, shi,
+                                            dev_status);
     if (e != hipSuccess) return fail(DSPARK_ERR_HIP, "markov_sample step %d: %s", step, hipGetErrorString(e));
   }
   const int64_t ntok = (int64_t)R * gamma;
   hipLaunchKernelGGL(finalize_tokens_kernel, dim3((unsigned)((ntok + 255) / 256)), dim3(256), 0, s, keys,
                      tokens, R, gamma, V, dev_status);
   return check_launch("markov_sample");
+}
+
+// Teacher-forced block logits (page 1 §3.7, apply_block_logits in training;
+// page 4 §3.3): every row takes its bias from its own given previous token,
+// so the whole block is one step of the kernels above over all N rows (one
+// pass over W2 per 128-row group), with the base add, the optional soft cap
+// and the logit store fused into the tile epilogue.  The argmax fold of that
+// step gives each row's greedy token for free.
+extern "C" size_t dspark_markov_block_logits_workspace_bytes(int N, int V, int r, int wdtype) {
+  return dspark_markov_sample_workspace_bytes(N, 1, V, r, wdtype);
+}
+
+extern "C" int dspark_markov_block_logits(const float* base_logits, const void* w1, const void* w2,
+                                          const int32_t* prev, float* logits, int32_t* argmax_tokens,
+                                          int N, int V, int r, int wdtype, float softcap, void* ws,
+                                          size_t ws_bytes, int32_t* dev_status, void* stream) {
+  using namespace dspark_host;
+  if (N < 0) return fail(DSPARK_ERR_INVALID_ARG, "markov_block_logits: negative dimension");
+  if (V < 1 || r < 1 || r > 1024)
+    return fail(DSPARK_ERR_INVALID_ARG, "markov_block_logits: need V >= 1 and 1 <= r <= 1024 (V=%d r=%d)", V, r);
+  if (wdtype != DSPARK_BF16 && wdtype != DSPARK_F32)
+    return fail(DSPARK_ERR_INVALID_ARG, "markov_block_logits: unknown wdtype %d", wdtype);
+  if (!(softcap >= 0.f) || softcap == INFINITY)
+    return fail(DSPARK_ERR_INVALID_ARG, "markov_block_logits: softcap must be finite and >= 0");
+  if (N == 0) return ok();
+  if (!base_logits || !w1 || !w2 || !prev || !logits)
+    return fail(DSPARK_ERR_INVALID_ARG, "markov_block_logits: null required pointer");
+  const size_t need = dspark_markov_block_logits_workspace_bytes(N, V, r, wdtype);
+  if (ws_bytes < need || !ws)
+    return fail(DSPARK_ERR_WORKSPACE, "markov_block_logits: workspace %zu bytes < %zu", ws_bytes, need);
+  if ((uintptr_t)ws % 8) return fail(DSPARK_ERR_INVALID_ARG, "markov_block_logits: workspace not 8-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  uint64_t* keys = (uint64_t*)ws;
+  const int64_t nk = keys_per_step(N);
+  hipLaunchKernelGGL(zero_u64_kernel, dim3((unsigned)((nk + 255) / 256)), dim3(256), 0, s, keys, nk);
+  const int cus = cu_count();
+  if (cus <= 0) return fail(DSPARK_ERR_HIP, "markov_block_logits: device query failed");
+  const bool bf = wdtype == DSPARK_BF16;
+  const bool mfma_ok = bf && V % 8 == 0 && r % 8 == 0 && r <= 512 && (uintptr_t)w1 % 16 == 0 &&
+                       (uintptr_t)w2 % 16 == 0 && (uintptr_t)base_logits % 16 == 0 &&
+                       (uintptr_t)logits % 16 == 0;
+  // greedy, prev from the caller (no previous keys); with a soft cap the
+  // temperature slot carries 1 / c
+  const hipError_t e =
+      softcap > 0.f
+          ? launch_step<true>(mfma_ok, bf, cus, s, base_logits, w1, w2, prev, nullptr, keys, logits, N, 1, V, r,
+                              0, 1.f / softcap, 1, 0u, 0u, dev_status)
+          : launch_step<false>(mfma_ok, bf, cus, s, base_logits, w1, w2, prev, nullptr, keys, logits, N, 1, V,
+                               r, 0, 1.f, 1, 0u, 0u, dev_status);
+  if (e != hipSuccess) return fail(DSPARK_ERR_HIP, "markov_block_logits: %s", hipGetErrorString(e));
+  if (argmax_tokens)
+    hipLaunchKernelGGL(finalize_tokens_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, s, keys,
+                       argmax_tokens, N, 1, V, dev_status);
+  return check_launch("markov_block_logits");
 }

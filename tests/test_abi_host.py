@@ -33,7 +33,7 @@ def lib():
 def test_every_declared_symbol_is_exported(lib):
     mod, L = lib
     names = _declared()
-    assert len(names) == 10, names
+    assert len(names) == 14, names
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(mod.SIGNATURES)
@@ -132,3 +132,24 @@ def test_wait_limit_setter_is_host_only(lib):
     _, L = lib
     L.dspark_set_wait_limit(5)
     L.dspark_set_wait_limit(0)
+
+
+def test_block_logits_and_l1_loss_reject_bad_arguments(lib):
+    mod, L = lib
+    p = ctypes.c_void_p(16)
+    # negative N, bad rank, unknown weight dtype, negative soft cap, missing workspace
+    assert L.dspark_markov_block_logits(p, p, p, p, p, NULL, -1, 64, 8, 1, 0.0, p, 1 << 20, NULL, NULL) == mod.ERR_INVALID_ARG
+    assert L.dspark_markov_block_logits(p, p, p, p, p, NULL, 4, 64, 0, 1, 0.0, p, 1 << 20, NULL, NULL) == mod.ERR_INVALID_ARG
+    assert L.dspark_markov_block_logits(p, p, p, p, p, NULL, 4, 64, 8, 7, 0.0, p, 1 << 20, NULL, NULL) == mod.ERR_INVALID_ARG
+    assert L.dspark_markov_block_logits(p, p, p, p, p, NULL, 4, 64, 8, 1, -1.0, p, 1 << 20, NULL, NULL) == mod.ERR_INVALID_ARG
+    assert L.dspark_markov_block_logits(p, p, p, NULL, p, NULL, 4, 64, 8, 1, 0.0, p, 1 << 20, NULL, NULL) == mod.ERR_INVALID_ARG
+    assert L.dspark_markov_block_logits(p, p, p, p, p, NULL, 4, 64, 8, 1, 0.0, p, 0, NULL, NULL) == mod.ERR_WORKSPACE
+    assert L.dspark_markov_block_logits(p, p, p, p, p, NULL, 0, 64, 8, 1, 0.0, NULL, 0, NULL, NULL) == mod.OK
+    assert L.dspark_markov_block_logits_workspace_bytes(16384, 151936, 256, 1) == \
+        L.dspark_markov_sample_workspace_bytes(16384, 1, 151936, 256, 1)
+    # l1 loss: unknown dtype, bad decay, missing loss pointer, too small workspace
+    assert L.dspark_l1_loss(p, p, NULL, 4.0, p, NULL, NULL, NULL, 1, 1, 1, 8, 3, p, 1 << 20, NULL) == mod.ERR_INVALID_ARG
+    assert L.dspark_l1_loss(p, p, NULL, 0.0, p, NULL, NULL, NULL, 1, 1, 1, 8, 1, p, 1 << 20, NULL) == mod.ERR_INVALID_ARG
+    assert L.dspark_l1_loss(p, p, NULL, 4.0, NULL, NULL, NULL, NULL, 1, 1, 1, 8, 1, p, 1 << 20, NULL) == mod.ERR_INVALID_ARG
+    assert L.dspark_l1_loss(p, p, NULL, 4.0, p, NULL, NULL, NULL, 1, 1, 1, 8, 1, p, 0, NULL) == mod.ERR_WORKSPACE
+    assert L.dspark_l1_loss_workspace_bytes(4, 512, 8) == 3 * 4 * 512 * 8 * 4

@@ -1,0 +1,177 @@
+"""Teacher-forced Markov block logits and the L1 (TV) loss, its gradient and
+tau_greedy on the GPU vs the oracle.
+
+Bars: logits within 1e-4 (float32 weights) / 2e-2 (bf16 weights: the device
+multiplies the exact bf16 values with float32 accumulation, asserted far
+tighter below); argmax tokens exact wherever the oracle's top-2 margin
+exceeds 1e-3; loss and per-row L1 distances within 1e-4 (float32 softmaxes);
+gradients within 1e-4 of the row's largest gradient magnitude, except at
+elements whose p and q agree to 1e-5 relative (there the sign of p - q, and
+so the subgradient, may differ between float32 and float64); tau_greedy
+exact (ties between equal logits go to the lowest index on both sides)."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from gpu_util import DEV, as_dtype, dev
+from oracle import accept_rate as OR
+from oracle import tv_loss as OT
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dsp():
+    import semi_autoregressive_block_amd as m
+    return m
+
+
+def _markov_inputs(seed, N, V, r, wdtype, wscale=0.05):
+    rng = np.random.default_rng(seed)
+    base = (rng.standard_normal((N, V)) * 3).astype(np.float32)
+    w1 = (rng.standard_normal((V, r)) * wscale).astype(np.float32)
+    w2 = (rng.standard_normal((r, V)) * wscale).astype(np.float32)
+    if wdtype == "bf16":
+        w1, w2 = W.to_bf16_bits(w1), W.to_bf16_bits(w2)
+    prev = rng.integers(0, V, size=N).astype(np.int32)
+    return base, w1, w2, prev
+
+
+def _check_tokens(tok, ref_logits):
+    top2 = np.sort(ref_logits, axis=-1)[:, -2:]
+    sure = top2[:, 1] - top2[:, 0] > 1e-3
+    np.testing.assert_array_equal(tok[sure], np.argmax(ref_logits, axis=-1)[sure])
+    assert sure.mean() >= 0.75  # most rows have a clear winner
+
+
+@pytest.mark.parametrize("N,V,r,wdtype,softcap", [
+    (37, 4096, 64, "bf16", 0.0),       # ragged rows, several 64-column tiles
+    (200, 20000, 256, "bf16", 0.0),    # two 128-row groups, ragged vocabulary tail
+    (200, 20000, 256, "bf16", 30.0),   # soft cap
+    (45, 2048, 512, "bf16", 0.0),      # rank 512
+    (19, 1001, 40, "bf16", 5.0),       # V not a multiple of 8: vector-ALU path, soft cap
+    (23, 3000, 48, "f32", 0.0),        # float32 weights: vector-ALU path
+])
+def test_block_logits(dsp, N, V, r, wdtype, softcap):
+    base, w1, w2, prev = _markov_inputs(N + V, N, V, r, wdtype, wscale=0.3)
+    logits, tok = dsp.markov_block_logits(dev(base), as_dtype(w1, wdtype), as_dtype(w2, wdtype), dev(prev),
+                                          softcap=softcap, want_tokens=True)
+    ref = OT.block_logits(base, W.values(w1, wdtype), W.values(w2, wdtype), prev, softcap)
+    err = np.abs(logits.cpu().numpy() - ref).max()
+    assert err < (2e-2 if wdtype == "bf16" else 1e-4), err
+    assert err < 2e-4
+    _check_tokens(tok.cpu().numpy(), ref)
+
+
+def test_block_logits_full_vocabulary_sampled_rows(dsp):
+    """V = 151936, r = 256, 384 rows (three row groups), checked on a sample."""
+    N, V, r = 384, 151936, 256
+    base, w1, w2, prev = _markov_inputs(5, N, V, r, "bf16", wscale=0.05)
+    logits, tok = dsp.markov_block_logits(dev(base), as_dtype(w1, "bf16"), as_dtype(w2, "bf16"), dev(prev),
+                                          want_tokens=True)
+    rows = np.array([0, 1, 127, 128, 200, 255, 256, 383])
+    ref = OT.block_logits(base[rows], W.values(w1, "bf16"), W.values(w2, "bf16"), prev[rows])
+    got = logits[torch.as_tensor(rows, device=DEV)].cpu().numpy()
+    assert np.abs(got - ref).max() < 2e-4
+    _check_tokens(tok.cpu().numpy()[rows], ref)
+
+
+def test_block_logits_bad_token_is_clamped_and_flagged(dsp):
+    base, w1, w2, prev = _markov_inputs(9, 10, 2048, 64, "bf16")
+    prev[3] = -5
+    prev[7] = 2048
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    logits, _ = dsp.markov_block_logits(dev(base), as_dtype(w1, "bf16"), as_dtype(w2, "bf16"), dev(prev), status=st)
+    from semi_autoregressive_block_amd import _lib
+    assert int(st.item()) & _lib.STATUS_BAD_TOKEN
+    fixed = prev.copy()
+    fixed[[3, 7]] = 0
+    ref = OT.block_logits(base, W.values(w1, "bf16"), W.values(w2, "bf16"), fixed)
+    assert np.abs(logits.cpu().numpy() - ref).max() < 2e-4
+
+
+def _loss_inputs(seed, B, A, g, V, dtype):
+    rng = np.random.default_rng(seed)
+    d = (rng.standard_normal((B, A, g, V)) * 3).astype(np.float32)
+    t = (d + rng.standard_normal(d.shape) * rng.uniform(0.2, 2.0, size=(B, A, g, 1))).astype(np.float32)
+    # some rows whose argmax agrees, some with tied maxima (lowest index wins)
+    t[0, 0, 0] = d[0, 0, 0]
+    i1, i2 = V // 3, V // 2
+    d[0, 0, 1, i1] = d[0, 0, 1, i2] = d[0, 0, 1].max() + 1.0
+    t[0, 0, 1, i1] = t[0, 0, 1, i2] = t[0, 0, 1].max() + 1.0
+    m = np.ones((B, A, g), dtype=np.uint8)
+    for b in range(B):
+        for a in range(A):
+            m[b, a, rng.integers(1, g + 1):] = 0
+    if dtype == "bf16":
+        d, t = W.to_bf16_bits(d), W.to_bf16_bits(t)
+    return d, t, m
+
+
+def _check_grad(g, d, t, ref):
+    p, q = OR.softmax(d), OR.softmax(t)
+    tie = np.abs(p - q) <= 1e-5 * np.maximum(p, q)
+    scale = np.abs(ref).max(axis=-1, keepdims=True)
+    bad = (np.abs(g - ref) > 1e-4 * scale + 1e-12) & ~tie
+    assert not bad.any(), (int(bad.sum()), np.abs(g - ref)[bad].max())
+
+
+@pytest.mark.parametrize("B,A,g,V,dtype", [
+    (2, 3, 4, 1000, "bf16"),     # V not a multiple of 8: element-wise path
+    (2, 3, 4, 4096, "bf16"),     # 16-byte vectors
+    (1, 5, 8, 3000, "f32"),
+    (1, 2, 3, 7, "f32"),         # tiny vocabulary
+])
+def test_l1_loss_small(dsp, B, A, g, V, dtype):
+    d, t, m = _loss_inputs(B * 100 + V, B, A, g, V, dtype)
+    dv, tv = W.values(d, dtype), W.values(t, dtype)
+    loss, grad, rows, tau = dsp.l1_loss(as_dtype(d, dtype), as_dtype(t, dtype), eval_mask=dev(m), want_grad=True,
+                                        want_rows=True, want_tau_greedy=True)
+    assert abs(loss.item() - OT.l1_loss(dv, tv, m)) < 1e-5
+    assert np.abs(rows.cpu().numpy() - OT.l1_distance(dv, tv)).max() < 1e-5
+    np.testing.assert_array_equal(tau.cpu().numpy(), OT.tau_greedy(dv, tv, m))
+    _check_grad(grad.cpu().numpy(), dv, tv, OT.l1_loss_grad(dv, tv, m))
+
+
+def test_l1_loss_full_vocabulary(dsp):
+    B, A, g, V = 1, 2, 8, 151936
+    d, t, m = _loss_inputs(11, B, A, g, V, "bf16")
+    dv, tv = W.values(d, "bf16"), W.values(t, "bf16")
+    loss, grad, rows, tau = dsp.l1_loss(as_dtype(d, "bf16"), as_dtype(t, "bf16"), eval_mask=dev(m), want_grad=True,
+                                        want_rows=True, want_tau_greedy=True)
+    assert abs(loss.item() - OT.l1_loss(dv, tv, m)) < 1e-5
+    assert np.abs(rows.cpu().numpy() - OT.l1_distance(dv, tv)).max() < 1e-5
+    np.testing.assert_array_equal(tau.cpu().numpy(), OT.tau_greedy(dv, tv, m))
+    _check_grad(grad.cpu().numpy(), dv, tv, OT.l1_loss_grad(dv, tv, m))
+
+
+def test_l1_loss_no_mask_and_all_masked(dsp):
+    d, t, _ = _loss_inputs(3, 1, 2, 4, 512, "f32")
+    loss, grad, _, tau = dsp.l1_loss(as_dtype(d, "f32"), as_dtype(t, "f32"), want_grad=True, want_tau_greedy=True)
+    ones = np.ones((1, 2, 4), dtype=np.uint8)
+    assert abs(loss.item() - OT.l1_loss(d, t, ones)) < 1e-5
+    np.testing.assert_array_equal(tau.cpu().numpy(), OT.tau_greedy(d, t, ones))
+    zeros = np.zeros((1, 2, 4), dtype=np.uint8)
+    loss, grad, _, tau = dsp.l1_loss(as_dtype(d, "f32"), as_dtype(t, "f32"), eval_mask=dev(zeros), want_grad=True,
+                                     want_tau_greedy=True)
+    assert loss.item() == 0.0
+    assert torch.count_nonzero(grad).item() == 0
+    assert np.all(tau.cpu().numpy() == 1.0)
+
+
+def test_l1_loss_identical_is_zero_and_deterministic(dsp):
+    d, _, m = _loss_inputs(4, 2, 2, 4, 4096, "bf16")
+    x = as_dtype(d, "bf16")
+    loss, grad, rows, tau = dsp.l1_loss(x, x, eval_mask=dev(m), want_grad=True, want_rows=True, want_tau_greedy=True)
+    assert loss.item() == 0.0 and torch.count_nonzero(rows).item() == 0
+    np.testing.assert_array_equal(tau.cpu().numpy(), 1.0 + np.cumprod(m, axis=-1).sum(axis=-1))
+    assert torch.count_nonzero(grad).item() == 0
+    _, t, _ = _loss_inputs(5, 2, 2, 4, 4096, "bf16")
+    y = as_dtype(t, "bf16")
+    a = dsp.l1_loss(x, y, eval_mask=dev(m), want_grad=True)
+    b = dsp.l1_loss(x, y, eval_mask=dev(m), want_grad=True)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
