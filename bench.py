@@ -13,14 +13,17 @@ logits and so is not part of a serving round, is timed beside it on the
 4 x 512 x 8-row training-shaped workload and reported under "accept_rate";
 the training-shaped all-anchor attention (1 x 4096 context, 512 anchors,
 gamma = 8; MFMA-bound) is timed too and reported under "attention_training"
-against the bf16 matrix-core peak.
+against the bf16 matrix-core peak.  So are the two training-side neighbours
+on the same 4 x 512 x 8-row shape: the L1 (TV) loss with its float32
+gradient and tau_greedy ("l1_loss") and the teacher-forced Markov block
+logits ("block_logits").
 
 Prints ONE JSON line: metric, value (drafted tokens/s), ms_per_step, the
 per-operation breakdown, the roofline of the dominant kernel (achieved
 algorithmic GB/s from HIP events on the launch stream vs the 8 TB/s HBM
 peak) and the CPU oracle timed on a bounded sample of the same workload.
 
---only {round,attention,markov,accept,train_attention,copy} restricts the run to one part
+--only {round,attention,markov,accept,train_attention,copy,block_logits,l1_loss} restricts the run to one part
 (for profiler runs); --no-cpu skips the CPU baseline.
 """
 
@@ -45,7 +48,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", choices=["round", "attention", "markov", "accept", "train_attention", "copy"],
+    ap.add_argument("--only", choices=["round", "attention", "markov", "accept", "train_attention", "copy",
+                                       "block_logits", "l1_loss"],
                     default=None)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -275,6 +279,45 @@ def main():
         del a4
         torch.cuda.empty_cache()
 
+    if args.only in (None, "l1_loss"):
+        # L1 (TV) loss with its gradient on workload 4's draft / target logits
+        a4 = W.config4_device(torch, dev)
+        m = a4["mask"]
+        em = dsp.eval_mask(torch.from_numpy(m.anchor).to(dev), torch.from_numpy(m.keep).to(dev),
+                           torch.from_numpy(m.seq_lens).to(dev), torch.from_numpy(m.loss_mask).to(dev),
+                           gamma=8)
+        grad = torch.empty(a4["draft"].shape, dtype=torch.float32, device=dev)
+        loss = torch.empty((1,), dtype=torch.float32, device=dev)
+        ws = torch.empty(dsp.l1_loss_workspace_bytes(4, 512, 8), dtype=torch.uint8, device=dev)
+        f_l1 = lambda: dsp.l1_loss(a4["draft"], a4["target"], eval_mask=em, loss=loss, grad=grad, workspace=ws)
+        l1_ms = timed(torch, f_l1, K, Wm)
+        l1_bytes = 2 * a4["draft"].numel() * 2 + grad.numel() * 4  # both logit tensors once + the gradient
+        if args.only == "l1_loss":
+            print(json.dumps({"l1_loss_ms": l1_ms, "GBps": l1_bytes / l1_ms / 1e6}))
+            return
+        result["l1_loss"] = dict(ms=l1_ms, bytes=l1_bytes)
+        del a4, grad
+        torch.cuda.empty_cache()
+
+    if args.only in (None, "block_logits"):
+        # teacher-forced Markov block logits, 16384 rows x V = 151936, rank 256
+        bl = W.config4_block_logits_device(torch, dev)
+        out = torch.empty_like(bl["base"])
+        ws = torch.empty(dsp.markov_block_logits_workspace_bytes(bl["N"], bl["V"], bl["r"]), dtype=torch.uint8,
+                         device=dev)
+        f_bl = lambda: dsp.markov_block_logits(bl["base"], bl["w1"], bl["w2"], bl["prev"], logits=out,
+                                               workspace=ws)
+        bl_ms = timed(torch, f_bl, K, Wm)
+        N, V, rr = bl["N"], bl["V"], bl["r"]
+        bl_bytes = 2 * N * V * 4 + rr * V * 2 + N * rr * 2 + N * 4  # base in, logits out, W2, W1 rows, prev
+        bl_flops = 2.0 * N * rr * V
+        if args.only == "block_logits":
+            print(json.dumps({"block_logits_ms": bl_ms, "GBps": bl_bytes / bl_ms / 1e6}))
+            return
+        result["block_logits"] = dict(ms=bl_ms, bytes=bl_bytes, flops=bl_flops)
+        del bl, out
+        torch.cuda.empty_cache()
+
     r = result["round"]
     attn_gbs = r["attn_bytes"] / r["attn_ms"] / 1e6
     mk_launch_ms = r["markov_ms"] / r["markov_steps"]
@@ -316,6 +359,18 @@ def main():
         line["accept_rate"] = {"workload": "4 x 512 x 8 rows, V=151936 bf16, with tau",
                                "ms": a["ms"], "GBps": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
                                "rows_per_s": 16384 / (a["ms"] / 1e3)}
+    if "l1_loss" in result:
+        a = result["l1_loss"]
+        gbs = a["bytes"] / a["ms"] / 1e6
+        line["l1_loss"] = {"workload": "4 x 512 x 8 rows, V=151936 bf16, loss + float32 gradient + tau_greedy",
+                           "ms": a["ms"], "GBps": gbs, "hbm_frac": gbs / HBM_PEAK_GBS}
+    if "block_logits" in result:
+        a = result["block_logits"]
+        gbs = a["bytes"] / a["ms"] / 1e6
+        line["block_logits"] = {"workload": "teacher-forced Markov logits, 16384 rows, V=151936, rank 256, "
+                                            "float32 base and logits, bf16 W1/W2",
+                                "ms": a["ms"], "GBps": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
+                                "TFLOPs": a["flops"] / a["ms"] / 1e9}
     if "train_attention" in result:
         a = result["train_attention"]
         tf = a["flops"] / a["ms"] / 1e9

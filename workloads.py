@@ -368,6 +368,22 @@ def config4_device(torch, device):
     return dict(draft=draft, target=target, mask=mask, sigma=sigma)
 
 
+def config4_block_logits_device(torch, device):
+    """Teacher-forced Markov block logits at the shape of workload 4's training
+    batch: N = 4 x 512 x 8 = 16384 rows, base [N, 151936] float32 N(0, 3^2),
+    W1 [151936, 256] and W2 [256, 151936] bf16 N(0, 0.02^2) (as workload 3),
+    previous tokens uniform in [0, V)."""
+    c = CONFIG4
+    N, V, r = c["B"] * c["A"] * c["gamma"], c["V"], 256
+    g = _gen(torch, device, SEED_BASE + 40)
+    return dict(
+        base=device_normal(torch, g, (N, V), 3.0, torch.float32, device),
+        w1=device_normal(torch, g, (V, r), 0.02, torch.bfloat16, device),
+        w2=device_normal(torch, g, (r, V), 0.02, torch.bfloat16, device),
+        prev=torch.randint(0, V, (N,), generator=g, device=device, dtype=torch.int32),
+        N=N, V=V, r=r)
+
+
 def config5_device(torch, device):
     """Serving round inputs at full size (structure from config5_structure()):
     Q [128, 16, 32, 128], K/V context [sum S_b, 8, 128] and own-block K/V
