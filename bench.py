@@ -231,9 +231,8 @@ def main():
         mk_ms = timed(torch, f_mk, K, Wm)
         mask_ms = timed(torch, f_mask, K, Wm)
         result["round"] = dict(ms=round_ms, attn_ms=attn_ms, markov_ms=mk_ms, mask_ms=mask_ms, **alg)
-        if not args.no_cpu:
-            result["cpu"] = cpu_baseline(W, inp, args.cpu_seconds)
-        del inp, bufs
+        round_inp = inp  # the CPU baseline runs last: seconds of host work would idle the GPU in between
+        del bufs
         torch.cuda.empty_cache()
 
     if args.only in (None, "train_attention"):
@@ -317,6 +316,9 @@ def main():
         result["block_logits"] = dict(ms=bl_ms, bytes=bl_bytes, flops=bl_flops)
         del bl, out
         torch.cuda.empty_cache()
+
+    if not args.no_cpu:
+        result["cpu"] = cpu_baseline(W, round_inp, args.cpu_seconds)
 
     r = result["round"]
     attn_gbs = r["attn_bytes"] / r["attn_ms"] / 1e6
