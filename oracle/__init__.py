@@ -14,7 +14,7 @@ each definition states.  Sources, cited per function:
   sections 3.1–3.13;
 * page 2 — "从 DFlash 到 dLLM Self-Spec（三）" (r00kie-liu.github.io),
   sections 3.4, 3.5, 3.8;
-* page 4 — "DSpark 深度解读" (juejin.cn), sections 3.2–3.3 and 4.1;
+* page 4 — "DSpark 深度解读" (juejin.cn), sections 3.2–3.4, 4.1 and 5.1;
 * Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3"
   (SC'11) for the Philox counter-based generator.
 
@@ -29,6 +29,8 @@ Modules:
 * ``tv_loss``     — teacher-forced Markov block logits, the L1 (TV) loss and
                     its gradient, tau_greedy (page 1 §3.7, §3.9–3.10, §3.12;
                     page 4 §3.3, §4.1).
+* ``scheduler``   — confidence head, prefix survival and the causal-greedy
+                    verify-length scheduler (page 1 §3.8; page 4 §3.4, §5.1).
 * ``philox``      — Philox4x32-10 / 4x64-10 and the Gumbel noise built on it.
 
 Every function here is pinned by a ``-m "not gpu"`` test against something
@@ -36,4 +38,4 @@ other than itself (closed forms, brute force, library routines, published
 known-answer vectors); there is no "parity unpinned" function.
 """
 
-from . import accept_rate, attention, eval_mask, markov, philox, tv_loss  # noqa: F401
+from . import accept_rate, attention, eval_mask, markov, philox, scheduler, tv_loss  # noqa: F401
