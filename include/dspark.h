@@ -13,6 +13,7 @@
  *
  *   dspark_markov_block_logits  teacher-forced Markov logits of a whole block
  *   dspark_l1_loss              L1 (TV) alignment loss, its gradient, tau_greedy
+ *   dspark_confidence_schedule  confidence head, prefix survival, verify length
  *
  * Sources (cited per entry point): page 1 = "03 · DSpark 建模：Markov 与
  * Confidence" (devpress.csdn.net), page 2 = "从 DFlash 到 dLLM Self-Spec
@@ -259,6 +260,34 @@ int dspark_l1_loss(const void* draft_logits, const void* target_logits, const ui
                    float decay, float* loss, float* row_l1, float* grad, float* tau_greedy,
                    int B, int A, int gamma, int V, int dtype,
                    void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Confidence head, prefix survival and the hardware-aware verify-length
+ * scheduler (page 1 §3.8; page 4 §3.4 and §5.1).  Row n = position k
+ * (1-based) of block (b, a):
+ *
+ *     c[n]  = sigmoid(weight_h . hidden[n] + weight_e . W1[prev[n]] + bias)
+ *     a[n]  = prod_{i <= k} c[block, i]
+ *     Theta_l = (1 + sum_{k <= l} a_k) * sps[l],   l = 0 .. gamma
+ *     verify_len[b, a] = the last l before Theta first decreases (gamma if never)
+ *
+ *   hidden     [B, A, gamma, H] hdtype (bf16 or float32)
+ *   weight_h   [H] float32; bias a finite float
+ *   weight_e   [r] float32 (nullable: no Markov input; then w1 / prev are unused)
+ *   w1 [V, r] wdtype, prev [B, A, gamma] int32 (outside [0, V): token 0 and
+ *              DSPARK_STATUS_BAD_TOKEN)
+ *   sps        [gamma + 1] float32: sps[l] = target steps per second when it
+ *              verifies l + 1 tokens
+ *   confidence, survival [B, A, gamma] float32 (out, nullable)
+ *   verify_len [B, A] int32 (out, required)
+ *   theta      [B, A, gamma + 1] float32 (out, nullable)
+ * Limits: gamma <= 1024, H >= 1.
+ * ---------------------------------------------------------------------- */
+int dspark_confidence_schedule(const void* hidden, int hdtype, const float* weight_h, float bias,
+                               const void* w1, int wdtype, const int32_t* prev, const float* weight_e,
+                               int r, int V, const float* sps, float* confidence, float* survival,
+                               int32_t* verify_len, float* theta, int B, int A, int gamma, int H,
+                               int32_t* dev_status, void* stream);
 
 #ifdef __cplusplus
 }

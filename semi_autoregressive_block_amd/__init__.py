@@ -14,6 +14,7 @@ Functions (same names and argument meaning as the C entry points):
 * ``eval_mask``        — cumulative-product eval mask
 * ``markov_block_logits`` — teacher-forced Markov logits of a whole block
 * ``l1_loss``          — L1 (TV) alignment loss, its gradient, tau_greedy
+* ``confidence_schedule`` — confidence head, prefix survival, verify length
 """
 
 from __future__ import annotations
@@ -29,7 +30,7 @@ _LIB = _lib.load()
 __all__ = ["block_attention", "markov_sample", "accept_rate", "eval_mask",
            "block_attention_workspace_bytes", "markov_sample_workspace_bytes",
            "accept_rate_workspace_bytes", "markov_block_logits", "markov_block_logits_workspace_bytes",
-           "l1_loss", "l1_loss_workspace_bytes", "set_wait_limit", "last_error", "version",
+           "l1_loss", "l1_loss_workspace_bytes", "confidence_schedule", "set_wait_limit", "last_error", "version",
            "DSparkError"]
 
 
@@ -298,6 +299,44 @@ def l1_loss(draft, target, *, eval_mask=None, decay=4.0, want_grad=False, want_r
     if rc != 0:
         raise DSparkError(rc, "l1_loss")
     return loss, grad, row_l1, tau_greedy
+
+
+def confidence_schedule(hidden, weight_h, bias, sps, *, w1=None, prev=None, weight_e=None, want_confidence=True,
+                        want_survival=True, want_theta=False, status=None):
+    """hidden [B, A, gamma, H] (bf16 or float32); weight_h [H] float32; bias
+    float; sps [gamma + 1] float32; optional Markov input w1 [V, r], prev
+    [B, A, gamma] int32, weight_e [r] float32.  Returns (verify_len [B, A]
+    int32, confidence, survival [B, A, gamma] float32 or None, theta
+    [B, A, gamma + 1] or None)."""
+    dev = hidden.device
+    _check(hidden, "hidden", (torch.bfloat16, torch.float32), ndim=4)
+    B, A, gamma, H = hidden.shape
+    _check(weight_h, "weight_h", torch.float32, dev, 1)
+    _check(sps, "sps", torch.float32, dev, 1)
+    if weight_h.shape[0] != H or sps.shape[0] != gamma + 1:
+        raise ValueError("weight_h must have H entries and sps gamma + 1")
+    r = V = 0
+    wdt = _lib.BF16
+    if weight_e is not None:
+        _check(weight_e, "weight_e", torch.float32, dev, 1)
+        _check(w1, "w1", (torch.bfloat16, torch.float32), dev, 2)
+        _check(prev, "prev", torch.int32, dev, 3)
+        V, r = w1.shape
+        if weight_e.shape[0] != r or tuple(prev.shape) != (B, A, gamma):
+            raise ValueError("weight_e must have r entries and prev be [B, A, gamma]")
+        wdt = _dt(w1)
+    conf = torch.empty((B, A, gamma), dtype=torch.float32, device=dev) if want_confidence else None
+    surv = torch.empty((B, A, gamma), dtype=torch.float32, device=dev) if want_survival else None
+    theta = torch.empty((B, A, gamma + 1), dtype=torch.float32, device=dev) if want_theta else None
+    vlen = torch.empty((B, A), dtype=torch.int32, device=dev)
+    if status is not None:
+        _check(status, "status", torch.int32, dev)
+    rc = _LIB.dspark_confidence_schedule(_ptr(hidden), _dt(hidden), _ptr(weight_h), float(bias), _ptr(w1), wdt,
+                                         _ptr(prev), _ptr(weight_e), r, V, _ptr(sps), _ptr(conf), _ptr(surv),
+                                         _ptr(vlen), _ptr(theta), B, A, gamma, H, _ptr(status), _stream(dev))
+    if rc != 0:
+        raise DSparkError(rc, "confidence_schedule")
+    return vlen, conf, surv, theta
 
 
 def set_wait_limit(polls: int) -> None:

@@ -46,6 +46,8 @@ SIGNATURES = {
     "dspark_markov_block_logits": (_i, [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _f, _p, _sz, _p, _p]),
     "dspark_l1_loss_workspace_bytes": (_sz, [_i, _i, _i]),
     "dspark_l1_loss": (_i, [_p, _p, _p, _f, _p, _p, _p, _p, _i, _i, _i, _i, _i, _p, _sz, _p]),
+    "dspark_confidence_schedule": (_i, [_p, _i, _p, _f, _p, _i, _p, _p, _i, _i, _p, _p, _p, _p, _p,
+                                        _i, _i, _i, _i, _p, _p]),
 }
 
 

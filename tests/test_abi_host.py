@@ -33,7 +33,7 @@ def lib():
 def test_every_declared_symbol_is_exported(lib):
     mod, L = lib
     names = _declared()
-    assert len(names) == 14, names
+    assert len(names) == 15, names
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(mod.SIGNATURES)
@@ -153,3 +153,21 @@ def test_block_logits_and_l1_loss_reject_bad_arguments(lib):
     assert L.dspark_l1_loss(p, p, NULL, 4.0, NULL, NULL, NULL, NULL, 1, 1, 1, 8, 1, p, 1 << 20, NULL) == mod.ERR_INVALID_ARG
     assert L.dspark_l1_loss(p, p, NULL, 4.0, p, NULL, NULL, NULL, 1, 1, 1, 8, 1, p, 0, NULL) == mod.ERR_WORKSPACE
     assert L.dspark_l1_loss_workspace_bytes(4, 512, 8) == 3 * 4 * 512 * 8 * 4
+
+
+def test_confidence_schedule_rejects_bad_arguments(lib):
+    mod, L = lib
+    p = ctypes.c_void_p(16)
+    args = lambda **k: dict(dict(hidden=p, hd=1, wh=p, bias=0.0, w1=NULL, wd=1, prev=NULL, we=NULL, r=0, V=0,
+                                 sps=p, conf=NULL, surv=NULL, vlen=p, theta=NULL, B=1, A=1, g=4, H=8), **k)
+    call = lambda a: L.dspark_confidence_schedule(a["hidden"], a["hd"], a["wh"], a["bias"], a["w1"], a["wd"],
+                                                  a["prev"], a["we"], a["r"], a["V"], a["sps"], a["conf"],
+                                                  a["surv"], a["vlen"], a["theta"], a["B"], a["A"], a["g"], a["H"],
+                                                  NULL, NULL)
+    assert call(args(g=2000)) == mod.ERR_INVALID_ARG              # gamma > 1024
+    assert call(args(H=0)) == mod.ERR_INVALID_ARG
+    assert call(args(hd=5)) == mod.ERR_INVALID_ARG
+    assert call(args(we=p)) == mod.ERR_INVALID_ARG               # Markov input without w1 / prev
+    assert call(args(bias=float("nan"))) == mod.ERR_INVALID_ARG
+    assert call(args(vlen=NULL)) == mod.ERR_INVALID_ARG
+    assert call(args(B=0)) == mod.OK
