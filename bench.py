@@ -16,14 +16,15 @@ gamma = 8; MFMA-bound) is timed too and reported under "attention_training"
 against the bf16 matrix-core peak.  So are the two training-side neighbours
 on the same 4 x 512 x 8-row shape: the L1 (TV) loss with its float32
 gradient and tau_greedy ("l1_loss") and the teacher-forced Markov block
-logits ("block_logits").
+logits ("block_logits"), and, at the serving shape, the confidence head with
+the verify-length scheduler ("confidence_schedule").
 
 Prints ONE JSON line: metric, value (drafted tokens/s), ms_per_step, the
 per-operation breakdown, the roofline of the dominant kernel (achieved
 algorithmic GB/s from HIP events on the launch stream vs the 8 TB/s HBM
 peak) and the CPU oracle timed on a bounded sample of the same workload.
 
---only {round,attention,markov,accept,train_attention,copy,block_logits,l1_loss} restricts the run to one part
+--only {round,attention,markov,accept,train_attention,copy,block_logits,l1_loss,schedule} restricts the run to one part
 (for profiler runs); --no-cpu skips the CPU baseline.
 """
 
@@ -49,7 +50,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--only", choices=["round", "attention", "markov", "accept", "train_attention", "copy",
-                                       "block_logits", "l1_loss"],
+                                       "block_logits", "l1_loss", "schedule"],
                     default=None)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -317,6 +318,26 @@ def main():
         del bl, out
         torch.cuda.empty_cache()
 
+    if args.only in (None, "schedule"):
+        # confidence head + verify-length scheduler at the serving shape: 128
+        # blocks of 16 positions, hidden size 4096 (32 heads x 128), Markov
+        # input from a rank-256 W1 over V = 151936
+        g = torch.Generator(device=dev).manual_seed(W.SEED_BASE + 50)
+        hid = torch.randn((128, 1, 16, 4096), generator=g, device=dev).to(torch.bfloat16)
+        wh = torch.randn(4096, generator=g, device=dev) / 64
+        w1s = torch.randn((151936, 256), generator=g, device=dev).to(torch.bfloat16) * 0.02
+        prev = torch.randint(0, 151936, (128, 1, 16), generator=g, device=dev, dtype=torch.int32)
+        we = torch.randn(256, generator=g, device=dev)
+        sps = torch.linspace(1.0, 0.4, 17, device=dev)
+        f_s = lambda: dsp.confidence_schedule(hid, wh, 0.5, sps, w1=w1s, prev=prev, weight_e=we)
+        s_ms = timed(torch, f_s, K, Wm)
+        if args.only == "schedule":
+            print(json.dumps({"schedule_ms": s_ms}))
+            return
+        result["schedule"] = dict(ms=s_ms)
+        del hid, w1s
+        torch.cuda.empty_cache()
+
     if not args.no_cpu:
         result["cpu"] = cpu_baseline(W, round_inp, args.cpu_seconds)
 
@@ -373,6 +394,9 @@ def main():
                                             "float32 base and logits, bf16 W1/W2",
                                 "ms": a["ms"], "GBps": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
                                 "TFLOPs": a["flops"] / a["ms"] / 1e9}
+    if "schedule" in result:
+        line["confidence_schedule"] = {"workload": "128 blocks x 16 positions, hidden 4096 bf16, Markov input "
+                                                   "rank 256, verify-length scan", "ms": result["schedule"]["ms"]}
     if "train_attention" in result:
         a = result["train_attention"]
         tf = a["flops"] / a["ms"] / 1e9

@@ -9,18 +9,18 @@
 //   Theta_l = (1 + sum_{k <= l} a_k) * SPS[l],  l = 0 .. gamma
 //   verify length = the last l before Theta first drops    (causal greedy)
 //
-// One workgroup per block: its waves take the block's rows in turn (a
-// coalesced strided dot product over the hidden state and the previous
-// token's Markov embedding, reduced across the wave), then one thread runs
-// the block's prefix product and the early-stopping scan.  The work is a few
-// tens of MB at serving sizes, so the kernel is launch-latency bound.
+// One workgroup of 16 waves per block: its waves take the block's rows in
+// turn (a dot product over the hidden state with 16-byte loads when the row
+// length allows, plus the previous token's Markov embedding, reduced across
+// the wave), then one thread runs the block's prefix product and the
+// early-stopping scan.  The work is a few tens of MB at serving sizes.
 #include "common.h"
 
 using namespace dspark;
 
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 1024;  // one wave per block position up to gamma = 16
 constexpr int kMaxGamma = 1024;
 
 template <bool kBf16>
@@ -28,7 +28,36 @@ __device__ __forceinline__ float ld(const void* p, int64_t i) {
   return kBf16 ? __uint_as_float((uint32_t)((const uint16_t*)p)[i] << 16) : ((const float*)p)[i];
 }
 
-template <bool kBf16H, bool kBf16W>
+// dot(hidden row, w_h) of one wave: 16-byte loads (8 bf16 or 4 fp32 values
+// per lane and step) when VEC, else one element per lane and step.
+template <bool kBf16, bool VEC>
+__device__ __forceinline__ float row_dot(const void* hidden, int64_t row, int H, const float* wh, int lane) {
+  float acc = 0.f;
+  if constexpr (VEC) {
+    constexpr int kEl = kBf16 ? 8 : 4;
+    const u32x4* hp = (const u32x4*)((const char*)hidden + row * (int64_t)H * (kBf16 ? 2 : 4));
+    const f32x4* wp = (const f32x4*)wh;
+    for (int c = lane; c < H / kEl; c += 64) {
+      const u32x4 x = hp[c];
+      if constexpr (kBf16) {
+        const f32x4 w0 = wp[2 * c], w1 = wp[2 * c + 1];
+        acc = fmaf(bf16lo(x[0]), w0[0], acc); acc = fmaf(bf16hi(x[0]), w0[1], acc);
+        acc = fmaf(bf16lo(x[1]), w0[2], acc); acc = fmaf(bf16hi(x[1]), w0[3], acc);
+        acc = fmaf(bf16lo(x[2]), w1[0], acc); acc = fmaf(bf16hi(x[2]), w1[1], acc);
+        acc = fmaf(bf16lo(x[3]), w1[2], acc); acc = fmaf(bf16hi(x[3]), w1[3], acc);
+      } else {
+        const f32x4 w0 = wp[c];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc = fmaf(__uint_as_float(x[e]), w0[e], acc);
+      }
+    }
+  } else {
+    for (int j = lane; j < H; j += 64) acc = fmaf(ld<kBf16>(hidden, row * H + j), wh[j], acc);
+  }
+  return acc;
+}
+
+template <bool kBf16H, bool kBf16W, bool VEC>
 __global__ __launch_bounds__(kThreads) void confidence_schedule_kernel(
     const void* __restrict__ hidden, const float* __restrict__ wh, float bias, const void* __restrict__ w1,
     const int32_t* __restrict__ prev, const float* __restrict__ we, int r, int V, const float* __restrict__ sps,
@@ -39,8 +68,7 @@ __global__ __launch_bounds__(kThreads) void confidence_schedule_kernel(
   for (int64_t blk = blockIdx.x; blk < nblocks; blk += gridDim.x) {
     for (int k = w; k < gamma; k += nw) {
       const int64_t row = blk * gamma + k;
-      float acc = 0.f;
-      for (int j = lane; j < H; j += 64) acc = fmaf(ld<kBf16H>(hidden, row * H + j), wh[j], acc);
+      float acc = row_dot<kBf16H, VEC>(hidden, row, H, wh, lane);
       if (we) {
         int p = prev[row];
         if (p < 0 || p >= V) {
@@ -110,14 +138,22 @@ extern "C" int dspark_confidence_schedule(const void* hidden, int hdtype, const 
   hipStream_t s = (hipStream_t)stream;
   const unsigned grid = (unsigned)(nblocks < 4096 ? nblocks : 4096);
   const bool hb = hdtype == DSPARK_BF16, wb = !markov || wdtype == DSPARK_BF16;
-#define DSPARK_CS_LAUNCH(HB, WB)                                                                                \
-  hipLaunchKernelGGL((confidence_schedule_kernel<HB, WB>), dim3(grid), dim3(kThreads), 0, s, hidden, weight_h, \
-                     bias, w1, prev, weight_e, r, V, sps, confidence, survival, verify_len, theta, nblocks, gamma, \
-                     H, dev_status)
-  if (hb && wb) DSPARK_CS_LAUNCH(true, true);
-  else if (hb) DSPARK_CS_LAUNCH(true, false);
-  else if (wb) DSPARK_CS_LAUNCH(false, true);
-  else DSPARK_CS_LAUNCH(false, false);
+  const bool vec = H % (hb ? 8 : 4) == 0 && (uintptr_t)hidden % 16 == 0 && (uintptr_t)weight_h % 16 == 0;
+#define DSPARK_CS_LAUNCH(HB, WB, VC)                                                                           \
+  hipLaunchKernelGGL((confidence_schedule_kernel<HB, WB, VC>), dim3(grid), dim3(kThreads), 0, s, hidden,      \
+                     weight_h, bias, w1, prev, weight_e, r, V, sps, confidence, survival, verify_len, theta,  \
+                     nblocks, gamma, H, dev_status)
+  if (vec) {
+    if (hb && wb) DSPARK_CS_LAUNCH(true, true, true);
+    else if (hb) DSPARK_CS_LAUNCH(true, false, true);
+    else if (wb) DSPARK_CS_LAUNCH(false, true, true);
+    else DSPARK_CS_LAUNCH(false, false, true);
+  } else {
+    if (hb && wb) DSPARK_CS_LAUNCH(true, true, false);
+    else if (hb) DSPARK_CS_LAUNCH(true, false, false);
+    else if (wb) DSPARK_CS_LAUNCH(false, true, false);
+    else DSPARK_CS_LAUNCH(false, false, false);
+  }
 #undef DSPARK_CS_LAUNCH
   return check_launch("confidence_schedule");
 }
