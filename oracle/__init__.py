@@ -31,6 +31,9 @@ Modules:
                     page 4 §3.3, §4.1).
 * ``scheduler``   — confidence head, prefix survival and the causal-greedy
                     verify-length scheduler (page 1 §3.8; page 4 §3.4, §5.1).
+* ``markov_heads``— gated and recurrent Markov heads: step embedding,
+                    teacher-forced block logits and the stateful sampler
+                    (page 1 §3.7; page 4 §3.3).
 * ``philox``      — Philox4x32-10 / 4x64-10 and the Gumbel noise built on it.
 
 Every function here is pinned by a ``-m "not gpu"`` test against something
@@ -38,4 +41,4 @@ other than itself (closed forms, brute force, library routines, published
 known-answer vectors); there is no "parity unpinned" function.
 """
 
-from . import accept_rate, attention, eval_mask, markov, philox, scheduler, tv_loss  # noqa: F401
+from . import accept_rate, attention, eval_mask, markov, markov_heads, philox, scheduler, tv_loss  # noqa: F401
