@@ -17,14 +17,15 @@ against the bf16 matrix-core peak.  So are the two training-side neighbours
 on the same 4 x 512 x 8-row shape: the L1 (TV) loss with its float32
 gradient and tau_greedy ("l1_loss") and the teacher-forced Markov block
 logits ("block_logits"), and, at the serving shape, the confidence head with
-the verify-length scheduler ("confidence_schedule").
+the verify-length scheduler ("confidence_schedule"), and the gated and
+recurrent Markov-head samplers ("markov_heads").
 
 Prints ONE JSON line: metric, value (drafted tokens/s), ms_per_step, the
 per-operation breakdown, the roofline of the dominant kernel (achieved
 algorithmic GB/s from HIP events on the launch stream vs the 8 TB/s HBM
 peak) and the CPU oracle timed on a bounded sample of the same workload.
 
---only {round,attention,markov,accept,train_attention,copy,block_logits,l1_loss,schedule} restricts the run to one part
+--only {round,attention,markov,accept,train_attention,copy,block_logits,l1_loss,schedule,heads} restricts the run to one part
 (for profiler runs); --no-cpu skips the CPU baseline.
 """
 
@@ -50,7 +51,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--only", choices=["round", "attention", "markov", "accept", "train_attention", "copy",
-                                       "block_logits", "l1_loss", "schedule"],
+                                       "block_logits", "l1_loss", "schedule", "heads"],
                     default=None)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -318,6 +319,32 @@ def main():
         del bl, out
         torch.cuda.empty_cache()
 
+    if args.only in (None, "heads"):
+        # gated and recurrent Markov-head samplers at the serving shape: 128
+        # requests x 16 steps, V = 151936, rank 256, hidden 4096, greedy
+        g = torch.Generator(device=dev).manual_seed(W.SEED_BASE + 60)
+        R, G, V, rr, d = 128, 16, 151936, 256, 4096
+        base = torch.randn((R, G, V), generator=g, device=dev).mul_(3)
+        hid = torch.randn((R, G, d), generator=g, device=dev).to(torch.bfloat16)
+        w1h = (torch.randn((V, rr), generator=g, device=dev) * 0.5).to(torch.bfloat16)
+        w2h = (torch.randn((rr, V), generator=g, device=dev) * 0.3).to(torch.bfloat16)
+        heads = {"gated": (torch.randn((rr, d + rr), generator=g, device=dev) * 1.5 / (d + rr) ** 0.5),
+                 "rnn": (torch.randn((3, rr, 2 * rr + d), generator=g, device=dev) * 1.5 / (2 * rr + d) ** 0.5)}
+        fp = torch.randint(0, V, (R,), generator=g, device=dev, dtype=torch.int32)
+        toks = torch.empty((R, G), dtype=torch.int32, device=dev)
+        h_ms = {}
+        for kind, wt in heads.items():
+            wt = wt.to(torch.bfloat16)
+            ws = torch.empty(dsp.markov_head_sample_workspace_bytes(kind, R, G, V, rr), dtype=torch.uint8, device=dev)
+            f_h = lambda: dsp.markov_head_sample(kind, base, hid, w1h, w2h, wt, fp, tokens=toks, workspace=ws)
+            h_ms[kind] = timed(torch, f_h, K, Wm)
+        if args.only == "heads":
+            print(json.dumps({"heads_ms": h_ms}))
+            return
+        result["heads"] = h_ms
+        del base, hid, w1h, w2h, heads
+        torch.cuda.empty_cache()
+
     if args.only in (None, "schedule"):
         # confidence head + verify-length scheduler at the serving shape: 128
         # blocks of 16 positions, hidden size 4096 (32 heads x 128), Markov
@@ -382,6 +409,10 @@ def main():
         line["accept_rate"] = {"workload": "4 x 512 x 8 rows, V=151936 bf16, with tau",
                                "ms": a["ms"], "GBps": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
                                "rows_per_s": 16384 / (a["ms"] / 1e3)}
+    if "heads" in result:
+        line["markov_heads"] = {"workload": "gamma = 16 sampling steps for 128 requests, V=151936, rank 256, "
+                                            "hidden 4096 bf16, float32 base, greedy",
+                                "gated_ms": result["heads"]["gated"], "rnn_ms": result["heads"]["rnn"]}
     if "l1_loss" in result:
         a = result["l1_loss"]
         gbs = a["bytes"] / a["ms"] / 1e6

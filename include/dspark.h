@@ -12,6 +12,8 @@
  * and two training-side neighbours of the same steps:
  *
  *   dspark_markov_block_logits  teacher-forced Markov logits of a whole block
+ *   dspark_markov_head_sample / dspark_markov_head_block_logits
+ *                               the same for the gated and recurrent heads
  *   dspark_l1_loss              L1 (TV) alignment loss, its gradient, tau_greedy
  *   dspark_confidence_schedule  confidence head, prefix survival, verify length
  *
@@ -235,6 +237,61 @@ int dspark_markov_block_logits(const float* base_logits, const void* w1, const v
                                const int32_t* prev, float* logits, int32_t* argmax_tokens,
                                int N, int V, int r, int wdtype, float softcap,
                                void* ws, size_t ws_bytes, int32_t* dev_status, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Gated and recurrent Markov heads (page 1 §3.7, the paper's Eq. 6; page 4
+ * §3.3, the table of head variants).  They replace the vanilla head's W1[x]
+ * by a rank-r row E of the position that also sees the backbone hidden
+ * state h (length d); the bias is E @ W2 as for the vanilla head:
+ *
+ *   DSPARK_HEAD_GATED (1):  E = sigmoid(W_g [h; W1[x]]) * W1[x]
+ *       whead = W_g [r, d + r] bf16 (input order h, then W1[x])
+ *   DSPARK_HEAD_RNN (2):    z = [s; W1[x]; h],  E = tanh(W_o z),
+ *       s <- sigmoid(W_g z) * s + (1 - sigmoid(W_g z)) * tanh(W_c z)
+ *       whead = [W_g; W_c; W_o] stacked [3, r, 2r + d] bf16
+ *
+ * No bias terms; the state s is zero at the first position of every block
+ * and runs along it.  x is the previous token: for the sampler, the supplied
+ * first previous token at position 0 and the token just sampled after
+ * that; for the block logits, the caller's teacher token of the position.
+ * Precision: the hidden-state part of the maps is a bf16 matrix-core
+ * product with float32 accumulation; the recurrent part, the state and E
+ * are float32; E is rounded to bf16 for the vocabulary product when W2 is
+ * bf16 (float32 W2 uses float32 E).
+ *
+ *   base_logits  [R, gamma, V] float32
+ *   hidden       [R, gamma, d] bf16, 16-byte aligned; d a multiple of 8
+ *   w1 [V, r], w2 [r, V]   wdtype (bf16 or float32); r a multiple of 8, <= 512
+ *   whead        as above, bf16, 16-byte aligned
+ *
+ * dspark_markov_head_sample: the gamma-step sampler with the state carried
+ * between steps; token choice, Gumbel noise (seed, row, step, column) and
+ * the step_logits output exactly as dspark_markov_sample.
+ *   first_prev [R] int32; tokens [R, gamma] int32 (out);
+ *   step_logits [R, gamma, V] float32 (out, nullable)
+ * dspark_markov_head_block_logits: teacher-forced logits of B blocks
+ * (R = B rows of the state, N = B * gamma output rows), soft cap and argmax
+ * as dspark_markov_block_logits.
+ *   prev [B, gamma] int32 (prev[b, k] is x_{k-1} of position k);
+ *   logits [B, gamma, V] float32 (out); argmax_tokens [B, gamma] (out, nullable)
+ * Out-of-range previous tokens are replaced by 0 and set
+ * DSPARK_STATUS_BAD_TOKEN in *dev_status (nullable).  Workspaces from the
+ * matching *_workspace_bytes (256-byte aligned; 0 for an invalid kind).
+ * ---------------------------------------------------------------------- */
+#define DSPARK_HEAD_GATED 1
+#define DSPARK_HEAD_RNN 2
+size_t dspark_markov_head_sample_workspace_bytes(int kind, int R, int gamma, int V, int r);
+int dspark_markov_head_sample(int kind, const float* base_logits, const void* hidden, const void* w1,
+                              const void* w2, const void* whead, const int32_t* first_prev, int32_t* tokens,
+                              float* step_logits, int R, int gamma, int V, int r, int d, int wdtype,
+                              float temperature, uint64_t seed, void* ws, size_t ws_bytes,
+                              int32_t* dev_status, void* stream);
+size_t dspark_markov_head_block_logits_workspace_bytes(int kind, int B, int gamma, int V, int r);
+int dspark_markov_head_block_logits(int kind, const float* base_logits, const void* hidden, const void* w1,
+                                    const void* w2, const void* whead, const int32_t* prev, float* logits,
+                                    int32_t* argmax_tokens, int B, int gamma, int V, int r, int d, int wdtype,
+                                    float softcap, void* ws, size_t ws_bytes, int32_t* dev_status,
+                                    void* stream);
 
 /* ------------------------------------------------------------------------
  * L1 (total-variation) alignment loss, its gradient and tau_greedy (page 1

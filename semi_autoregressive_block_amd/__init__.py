@@ -260,6 +260,105 @@ def markov_block_logits(base, w1, w2, prev, *, softcap=0.0, logits=None, want_to
     return logits, tokens
 
 
+_HEAD_KINDS = {"gated": _lib.HEAD_GATED, "rnn": _lib.HEAD_RNN}
+
+
+def _head_kind(kind):
+    if kind not in _HEAD_KINDS:
+        raise ValueError(f"head kind must be one of {sorted(_HEAD_KINDS)}; got {kind!r}")
+    return _HEAD_KINDS[kind]
+
+
+def _check_head(kind, base, hidden, w1, w2, whead):
+    """Shapes of the gated / recurrent head inputs; returns (R, gamma, V, r, d)."""
+    dev = base.device
+    _check(base, "base", torch.float32, ndim=3)
+    R, gamma, V = base.shape
+    _check(hidden, "hidden", torch.bfloat16, dev, 3)
+    if tuple(hidden.shape[:2]) != (R, gamma):
+        raise ValueError("hidden must be [R, gamma, d] matching base")
+    d = hidden.shape[2]
+    _check(w1, "w1", (torch.bfloat16, torch.float32), dev, 2)
+    _check(w2, "w2", w1.dtype, dev, 2)
+    r = w1.shape[1]
+    if tuple(w1.shape) != (V, r) or tuple(w2.shape) != (r, V):
+        raise ValueError(f"w1 must be [V, r] and w2 [r, V]; got {tuple(w1.shape)}, {tuple(w2.shape)}")
+    want = (r, d + r) if kind == "gated" else (3, r, 2 * r + d)
+    _check(whead, "whead", torch.bfloat16, dev)
+    if tuple(whead.shape) != want:
+        raise ValueError(f"{kind} head weights must be {want}; got {tuple(whead.shape)}")
+    return R, gamma, V, r, d
+
+
+def markov_head_sample_workspace_bytes(kind, R, gamma, V, r) -> int:
+    return int(_LIB.dspark_markov_head_sample_workspace_bytes(_head_kind(kind), R, gamma, V, r))
+
+
+def markov_head_sample(kind, base, hidden, w1, w2, whead, first_prev, *, temperature=0.0, seed=0, tokens=None,
+                       step_logits=None, want_step_logits=False, status=None, workspace=None):
+    """Gated ("gated") or recurrent ("rnn") Markov-head sampler.  base
+    [R, gamma, V] float32; hidden [R, gamma, d] bf16; w1 [V, r], w2 [r, V];
+    whead [r, d + r] (gated) or [3, r, 2r + d] (rnn) bf16; first_prev [R]
+    int32.  Returns (tokens [R, gamma] int32, step_logits or None)."""
+    k = _head_kind(kind)
+    R, gamma, V, r, d = _check_head(kind, base, hidden, w1, w2, whead)
+    dev = base.device
+    _check(first_prev, "first_prev", torch.int32, dev, 1)
+    if first_prev.shape[0] != R:
+        raise ValueError("first_prev must have R entries")
+    if tokens is None:
+        tokens = torch.empty((R, gamma), dtype=torch.int32, device=dev)
+    _check(tokens, "tokens", torch.int32, dev, 2)
+    if step_logits is None and want_step_logits:
+        step_logits = torch.empty_like(base)
+    if step_logits is not None:
+        _check(step_logits, "step_logits", torch.float32, dev, 3)
+    if status is not None:
+        _check(status, "status", torch.int32, dev)
+    ws, wsb = _workspace(markov_head_sample_workspace_bytes(kind, R, gamma, V, r), dev, workspace)
+    rc = _LIB.dspark_markov_head_sample(
+        k, _ptr(base), _ptr(hidden), _ptr(w1), _ptr(w2), _ptr(whead), _ptr(first_prev), _ptr(tokens),
+        _ptr(step_logits), R, gamma, V, r, d, _dt(w1), float(temperature), int(seed) & (2**64 - 1), _ptr(ws), wsb,
+        _ptr(status), _stream(dev))
+    if rc != 0:
+        raise DSparkError(rc, "markov_head_sample")
+    return tokens, step_logits
+
+
+def markov_head_block_logits_workspace_bytes(kind, B, gamma, V, r) -> int:
+    return int(_LIB.dspark_markov_head_block_logits_workspace_bytes(_head_kind(kind), B, gamma, V, r))
+
+
+def markov_head_block_logits(kind, base, hidden, w1, w2, whead, prev, *, softcap=0.0, logits=None,
+                             want_tokens=False, tokens=None, status=None, workspace=None):
+    """Teacher-forced gated / recurrent head logits of B blocks.  base
+    [B, gamma, V] float32; hidden [B, gamma, d] bf16; prev [B, gamma] int32
+    (x_{k-1} of position k).  Returns (logits [B, gamma, V] float32, argmax
+    tokens [B, gamma] int32 or None)."""
+    k = _head_kind(kind)
+    B, gamma, V, r, d = _check_head(kind, base, hidden, w1, w2, whead)
+    dev = base.device
+    _check(prev, "prev", torch.int32, dev, 2)
+    if tuple(prev.shape) != (B, gamma):
+        raise ValueError("prev must be [B, gamma]")
+    if logits is None:
+        logits = torch.empty_like(base)
+    _check(logits, "logits", torch.float32, dev, 3)
+    if tokens is None and want_tokens:
+        tokens = torch.empty((B, gamma), dtype=torch.int32, device=dev)
+    if tokens is not None:
+        _check(tokens, "tokens", torch.int32, dev, 2)
+    if status is not None:
+        _check(status, "status", torch.int32, dev)
+    ws, wsb = _workspace(markov_head_block_logits_workspace_bytes(kind, B, gamma, V, r), dev, workspace)
+    rc = _LIB.dspark_markov_head_block_logits(
+        k, _ptr(base), _ptr(hidden), _ptr(w1), _ptr(w2), _ptr(whead), _ptr(prev), _ptr(logits), _ptr(tokens), B,
+        gamma, V, r, d, _dt(w1), float(softcap), _ptr(ws), wsb, _ptr(status), _stream(dev))
+    if rc != 0:
+        raise DSparkError(rc, "markov_head_block_logits")
+    return logits, tokens
+
+
 def l1_loss_workspace_bytes(B, A, gamma) -> int:
     return int(_LIB.dspark_l1_loss_workspace_bytes(B, A, gamma))
 

@@ -16,6 +16,8 @@ ERR_UNSUPPORTED = -3
 ERR_HIP = -4
 F32 = 0
 BF16 = 1
+HEAD_GATED = 1
+HEAD_RNN = 2
 STATUS_BAD_ANCHOR = 1
 STATUS_BAD_TOKEN = 2
 STATUS_BAD_OFFSETS = 4
@@ -46,6 +48,12 @@ SIGNATURES = {
     "dspark_markov_block_logits": (_i, [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _f, _p, _sz, _p, _p]),
     "dspark_l1_loss_workspace_bytes": (_sz, [_i, _i, _i]),
     "dspark_l1_loss": (_i, [_p, _p, _p, _f, _p, _p, _p, _p, _i, _i, _i, _i, _i, _p, _sz, _p]),
+    "dspark_markov_head_sample_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
+    "dspark_markov_head_sample": (_i, [_i, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _f, _u64,
+                                       _p, _sz, _p, _p]),
+    "dspark_markov_head_block_logits_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
+    "dspark_markov_head_block_logits": (_i, [_i, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _f,
+                                             _p, _sz, _p, _p]),
     "dspark_confidence_schedule": (_i, [_p, _i, _p, _f, _p, _i, _p, _p, _i, _i, _p, _p, _p, _p, _p,
                                         _i, _i, _i, _i, _p, _p]),
 }

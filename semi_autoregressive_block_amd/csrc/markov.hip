@@ -28,6 +28,7 @@
 
 #include "common.h"
 #include "philox.h"
+#include "markov_step.h"
 
 using namespace dspark;
 
@@ -35,31 +36,10 @@ namespace {
 
 constexpr int kThreads = 256;
 
-// Per-row argmax keys are folded with device-scope atomics, which MI355X
-// executes at the memory side; thousands of them on the same few cache
-// lines serialise.  Each row therefore has kKeyReplicas slots, each replica
-// in its own 4 KB-aligned region: workgroup w folds into replica w % 16 and
-// readers take the maximum over the replicas.
-constexpr int kKeyReplicas = 16;
-__host__ __device__ __forceinline__ int64_t replica_stride(int R) {  // in 64-bit keys
-  return ((int64_t)R * 8 + 4095) / 4096 * 512;
-}
-__host__ __device__ __forceinline__ int64_t keys_per_step(int R) { return kKeyReplicas * replica_stride(R); }
-
 __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
   const uint32_t lo = __shfl_xor((uint32_t)v, m, kWave);
   const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), m, kWave);
   return ((uint64_t)hi << 32) | lo;
-}
-
-__device__ __forceinline__ uint64_t read_key(const uint64_t* keys, int row, int R) {
-  uint64_t k = 0;
-#pragma unroll
-  for (int q = 0; q < kKeyReplicas; ++q) {
-    const uint64_t x = keys[q * replica_stride(R) + row];
-    k = x > k ? x : k;
-  }
-  return k;
 }
 
 __device__ __forceinline__ int decode_prev(const uint64_t* keys_prev, const int32_t* first_prev,
@@ -114,9 +94,12 @@ constexpr int kLdsRow = 144;  // bytes per staged W2 row of a tile (128 + 16: sp
 
 // SC: soft-capped logits c * tanh(l / c) (block logits only; sampling is then
 // greedy and the temperature argument carries 1 / c).
-template <int NW, int KS, int NS, bool FL, bool SC = false>
+// EB: the rank-r row of each row is read from `ebuf` ([R, gamma, r] float32,
+// rounded to bf16 here) instead of gathered from W1 by the previous token
+// (the gated and recurrent heads compute it beforehand).
+template <int NW, int KS, int NS, bool FL, bool SC = false, bool EB = false>
 __global__ __launch_bounds__(64 * NW) void markov_step_mfma(
-    const float* __restrict__ base, const uint16_t* __restrict__ w1,
+    const float* __restrict__ base, const uint16_t* __restrict__ w1, const float* __restrict__ ebuf,
     const uint16_t* __restrict__ w2, const int32_t* __restrict__ first_prev,
     const uint64_t* __restrict__ keys_prev, uint64_t* __restrict__ keys_out,
     float* __restrict__ step_logits, int R, int gamma, int V, int r, int step, float invT,
@@ -150,7 +133,15 @@ __global__ __launch_bounds__(64 * NW) void markov_step_mfma(
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
       const int k = kk * 32 + g * 8;
-      const u32x4 v = *(const u32x4*)(w1 + (int64_t)pv * r + min(k, r - 8));
+      u32x4 v;
+      if constexpr (EB) {
+        const f32x4* ep = (const f32x4*)(ebuf + ((int64_t)rowc * gamma + step) * r + min(k, r - 8));
+        const f32x4 x0 = ep[0], x1 = ep[1];
+        v = u32x4{pack_bf16x2(x0[0], x0[1]), pack_bf16x2(x0[2], x0[3]), pack_bf16x2(x1[0], x1[1]),
+                  pack_bf16x2(x1[2], x1[3])};
+      } else {
+        v = *(const u32x4*)(w1 + (int64_t)pv * r + min(k, r - 8));
+      }
       eb[kk] = (row < R && k < r) ? v : u32x4{0u, 0u, 0u, 0u};
     }
   };
@@ -275,9 +266,13 @@ __global__ __launch_bounds__(64 * NW) void markov_step_mfma(
   // chain runs and the chain's reads do not queue behind the bulk prefetch
   Set sets[NS];
   load_set(0, sets[0]);
-  const int pv = decode_prev(keys_prev, first_prev, rowc, R, V,
-                             blockIdx.x == 0 && g == 0 && row < R ? status : nullptr);
-  gather_e(pv);
+  if constexpr (EB) {
+    gather_e(0);
+  } else {
+    const int pv = decode_prev(keys_prev, first_prev, rowc, R, V,
+                               blockIdx.x == 0 && g == 0 && row < R ? status : nullptr);
+    gather_e(pv);
+  }
 #pragma unroll
   for (int q = 1; q < NS; ++q) load_set(q, sets[q]);
   store_w2(smem, sets[0]);
@@ -312,9 +307,10 @@ __global__ __launch_bounds__(64 * NW) void markov_step_mfma(
 // 16 rows per pass with E in LDS, fp32 FMAs.
 constexpr int kRowChunk = 16;
 
-template <bool kBf16W, bool SC = false>
+template <bool kBf16W, bool SC = false, bool EB = false>
 __global__ __launch_bounds__(kThreads) void markov_step_valu(
-    const float* __restrict__ base, const void* __restrict__ w1v, const void* __restrict__ w2v,
+    const float* __restrict__ base, const void* __restrict__ w1v, const float* __restrict__ ebuf,
+    const void* __restrict__ w2v,
     const int32_t* __restrict__ first_prev, const uint64_t* __restrict__ keys_prev,
     uint64_t* __restrict__ keys_out, float* __restrict__ step_logits, int R, int gamma, int V,
     int r, int step, float invT, int greedy, uint32_t seed_lo, uint32_t seed_hi,
@@ -332,11 +328,14 @@ __global__ __launch_bounds__(kThreads) void markov_step_valu(
   for (int c = threadIdx.x; c < kRowChunk * r; c += kThreads) {
     const int rr = c / r, k = c % r, row = row0 + rr;
     float v = 0.f;
-    if (row < R) v = w1((int64_t)decode_prev(keys_prev, first_prev, row, R, V, nullptr) * r + k);
+    if (row < R) {
+      if constexpr (EB) v = ebuf[((int64_t)row * gamma + step) * r + k];
+      else v = w1((int64_t)decode_prev(keys_prev, first_prev, row, R, V, nullptr) * r + k);
+    }
     E[c] = v;
   }
   if (threadIdx.x < kRowChunk) rowkey[threadIdx.x] = 0ull;
-  if (threadIdx.x < kRowChunk && row0 + threadIdx.x < R && blockIdx.x == 0)
+  if (!EB && threadIdx.x < kRowChunk && row0 + threadIdx.x < R && blockIdx.x == 0)
     decode_prev(keys_prev, first_prev, row0 + threadIdx.x, R, V, status);
   __syncthreads();
 
@@ -435,17 +434,17 @@ hipError_t allow_lds_once(K kern, size_t bytes) {
   return e;
 }
 
-template <int NW, int KS, int NS, bool FL, bool SC>
+template <int NW, int KS, int NS, bool FL, bool SC, bool EB>
 hipError_t launch_mfma(int grid_x, int grid_y, hipStream_t s, const float* base, const uint16_t* w1,
-                       const uint16_t* w2, const int32_t* first_prev, const uint64_t* kp,
+                       const float* ebuf, const uint16_t* w2, const int32_t* first_prev, const uint64_t* kp,
                        uint64_t* ko, float* step_logits, int R, int gamma, int V, int r, int step,
                        float invT, int greedy, uint32_t slo, uint32_t shi, int32_t* st) {
   (void)r;
   const size_t shm = (size_t)2 * 32 * KS * kLdsRow + (FL ? (size_t)NW * 4096 : 0);
-  auto kern = markov_step_mfma<NW, KS, NS, FL, SC>;
+  auto kern = markov_step_mfma<NW, KS, NS, FL, SC, EB>;
   hipError_t e = allow_lds_once(kern, shm);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(grid_x, grid_y), dim3(64 * NW), shm, s, base, w1, w2, first_prev,
+  hipLaunchKernelGGL(kern, dim3(grid_x, grid_y), dim3(64 * NW), shm, s, base, w1, ebuf, w2, first_prev,
                      kp, ko, step_logits, R, gamma, V, r, step, invT, greedy, slo, shi, st);
   return hipGetLastError();
 }
@@ -455,9 +454,9 @@ hipError_t launch_mfma(int grid_x, int grid_y, hipStream_t s, const float* base,
 // (up to 128 rows per workgroup, 8 waves, one compute unit each; up to 64
 // rows use 4 waves and two workgroups per compute unit), else the vector
 // kernel.
-template <bool SC>
+template <bool SC, bool EB = false>
 hipError_t launch_step(bool mfma_ok, bool bf, int cus, hipStream_t s, const float* base, const void* w1,
-                       const void* w2, const int32_t* first_prev, const uint64_t* kp, uint64_t* ko,
+                       const float* ebuf, const void* w2, const int32_t* first_prev, const uint64_t* kp, uint64_t* ko,
                        float* step_logits, int R, int gamma, int V, int r, int step, float invT,
                        int greedy, uint32_t slo, uint32_t shi, int32_t* st) {
   if (mfma_ok) {
@@ -470,10 +469,10 @@ hipError_t launch_step(bool mfma_ok, bool bf, int cus, hipStream_t s, const floa
     if (gx < 1) gx = 1;
     const uint16_t *a = (const uint16_t*)w1, *b = (const uint16_t*)w2;
     if (wide)
-      return r <= 256 ? launch_mfma<8, 8, 2, true, SC>(gx, gy, s, base, a, b, first_prev, kp, ko, step_logits, R, gamma, V, r, step, invT, greedy, slo, shi, st)
-                      : launch_mfma<8, 16, 2, false, SC>(gx, gy, s, base, a, b, first_prev, kp, ko, step_logits, R, gamma, V, r, step, invT, greedy, slo, shi, st);
-    return r <= 256 ? launch_mfma<4, 8, 2, false, SC>(gx, gy, s, base, a, b, first_prev, kp, ko, step_logits, R, gamma, V, r, step, invT, greedy, slo, shi, st)
-                    : launch_mfma<4, 16, 2, false, SC>(gx, gy, s, base, a, b, first_prev, kp, ko, step_logits, R, gamma, V, r, step, invT, greedy, slo, shi, st);
+      return r <= 256 ? launch_mfma<8, 8, 2, true, SC, EB>(gx, gy, s, base, a, ebuf, b, first_prev, kp, ko, step_logits, R, gamma, V, r, step, invT, greedy, slo, shi, st)
+                      : launch_mfma<8, 16, 2, false, SC, EB>(gx, gy, s, base, a, ebuf, b, first_prev, kp, ko, step_logits, R, gamma, V, r, step, invT, greedy, slo, shi, st);
+    return r <= 256 ? launch_mfma<4, 8, 2, false, SC, EB>(gx, gy, s, base, a, ebuf, b, first_prev, kp, ko, step_logits, R, gamma, V, r, step, invT, greedy, slo, shi, st)
+                    : launch_mfma<4, 16, 2, false, SC, EB>(gx, gy, s, base, a, ebuf, b, first_prev, kp, ko, step_logits, R, gamma, V, r, step, invT, greedy, slo, shi, st);
   }
   const int gy = (R + kRowChunk - 1) / kRowChunk;
   int gx = 2 * cus;
@@ -482,16 +481,54 @@ hipError_t launch_step(bool mfma_ok, bool bf, int cus, hipStream_t s, const floa
   if (gx < 1) gx = 1;
   const size_t shm = (size_t)kRowChunk * r * 4 + kRowChunk * 8;
   if (bf) {
-    (void)allow_lds_once(markov_step_valu<true, SC>, shm);
-    hipLaunchKernelGGL((markov_step_valu<true, SC>), dim3(gx, gy), dim3(kThreads), shm, s, base, w1, w2, first_prev, kp, ko, step_logits, R, gamma, V, r, step, invT, greedy, slo, shi, st);
+    (void)allow_lds_once(markov_step_valu<true, SC, EB>, shm);
+    hipLaunchKernelGGL((markov_step_valu<true, SC, EB>), dim3(gx, gy), dim3(kThreads), shm, s, base, w1, ebuf, w2, first_prev, kp, ko, step_logits, R, gamma, V, r, step, invT, greedy, slo, shi, st);
   } else {
-    (void)allow_lds_once(markov_step_valu<false, SC>, shm);
-    hipLaunchKernelGGL((markov_step_valu<false, SC>), dim3(gx, gy), dim3(kThreads), shm, s, base, w1, w2, first_prev, kp, ko, step_logits, R, gamma, V, r, step, invT, greedy, slo, shi, st);
+    (void)allow_lds_once(markov_step_valu<false, SC, EB>, shm);
+    hipLaunchKernelGGL((markov_step_valu<false, SC, EB>), dim3(gx, gy), dim3(kThreads), shm, s, base, w1, ebuf, w2, first_prev, kp, ko, step_logits, R, gamma, V, r, step, invT, greedy, slo, shi, st);
   }
   return hipGetLastError();
 }
 
 }  // namespace
+
+namespace dspark {
+
+hipError_t markov_step_embedded(const float* base, const float* ebuf, const void* w2, int wdtype,
+                                uint64_t* keys_out, float* step_logits, int R, int gamma, int V, int r, int step,
+                                float softcap, float temperature, uint64_t seed, hipStream_t s) {
+  const int cus = cu_count();
+  if (cus <= 0) return hipErrorInvalidDevice;
+  const bool bf = wdtype == DSPARK_BF16;
+  const bool mfma_ok = bf && V % 8 == 0 && r % 8 == 0 && r <= 512 && (uintptr_t)w2 % 16 == 0 &&
+                       (uintptr_t)ebuf % 16 == 0 && (uintptr_t)base % 16 == 0 &&
+                       (!step_logits || (uintptr_t)step_logits % 16 == 0);
+  const uint32_t slo = (uint32_t)seed, shi = (uint32_t)(seed >> 32);
+  if (softcap > 0.f)
+    return launch_step<true, true>(mfma_ok, bf, cus, s, base, nullptr, ebuf, w2, nullptr, nullptr, keys_out,
+                                   step_logits, R, gamma, V, r, step, 1.f / softcap, 1, 0u, 0u, nullptr);
+  const int greedy = temperature == 0.f;
+  return launch_step<false, true>(mfma_ok, bf, cus, s, base, nullptr, ebuf, w2, nullptr, nullptr, keys_out,
+                                  step_logits, R, gamma, V, r, step, greedy ? 1.f : 1.f / temperature, greedy,
+                                  slo, shi, nullptr);
+}
+
+hipError_t markov_zero_keys(uint64_t* keys, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(zero_u64_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, keys, n);
+  return hipGetLastError();
+}
+
+hipError_t markov_finalize_tokens(const uint64_t* keys, int32_t* tokens, int R, int gamma, int V,
+                                  int32_t* status, hipStream_t s) {
+  const int64_t n = (int64_t)R * gamma;
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(finalize_tokens_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, keys, tokens,
+                     R, gamma, V, status);
+  return hipGetLastError();
+}
+
+}  // namespace dspark
 
 extern "C" size_t dspark_markov_sample_workspace_bytes(int R, int gamma, int V, int r, int wdtype) {
   (void)V; (void)r; (void)wdtype;
@@ -537,7 +574,7 @@ extern "C" int dspark_markov_sample(const float* base_logits, const void* w1, co
   for (int step = 0; step < gamma; ++step) {
     const uint64_t* kp = step == 0 ? nullptr : keys + (int64_t)(step - 1) * keys_per_step(R);
     uint64_t* ko = keys + (int64_t)step * keys_per_step(R);
-    const hipError_t e = launch_step<false>(mfma_ok, bf, cus, s, base_logits, w1, w2, first_prev, kp, ko,
+    const hipError_t e = launch_step<false>(mfma_ok, bf, cus, s, base_logits, w1, nullptr, w2, first_prev, kp, ko,
                                             step_logits, R, gamma, V, r, step, invT, greedy, slo, shi,
                                             dev_status);
     if (e != hipSuccess) return fail(DSPARK_ERR_HIP, "markov_sample step %d: %s", step, hipGetErrorString(e));
@@ -591,9 +628,9 @@ extern "C" int dspark_markov_block_logits(const float* base_logits, const void* 
   // temperature slot carries 1 / c
   const hipError_t e =
       softcap > 0.f
-          ? launch_step<true>(mfma_ok, bf, cus, s, base_logits, w1, w2, prev, nullptr, keys, logits, N, 1, V, r,
+          ? launch_step<true>(mfma_ok, bf, cus, s, base_logits, w1, nullptr, w2, prev, nullptr, keys, logits, N, 1, V, r,
                               0, 1.f / softcap, 1, 0u, 0u, dev_status)
-          : launch_step<false>(mfma_ok, bf, cus, s, base_logits, w1, w2, prev, nullptr, keys, logits, N, 1, V,
+          : launch_step<false>(mfma_ok, bf, cus, s, base_logits, w1, nullptr, w2, prev, nullptr, keys, logits, N, 1, V,
                                r, 0, 1.f, 1, 0u, 0u, dev_status);
   if (e != hipSuccess) return fail(DSPARK_ERR_HIP, "markov_block_logits: %s", hipGetErrorString(e));
   if (argmax_tokens)

@@ -33,7 +33,7 @@ def lib():
 def test_every_declared_symbol_is_exported(lib):
     mod, L = lib
     names = _declared()
-    assert len(names) == 15, names
+    assert len(names) == 19, names
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(mod.SIGNATURES)
@@ -171,3 +171,39 @@ def test_confidence_schedule_rejects_bad_arguments(lib):
     assert call(args(bias=float("nan"))) == mod.ERR_INVALID_ARG
     assert call(args(vlen=NULL)) == mod.ERR_INVALID_ARG
     assert call(args(B=0)) == mod.OK
+
+
+def test_head_workspaces_and_bad_arguments(lib):
+    """Workspace sizes of the gated / recurrent heads and argument checks that
+    return before any device work."""
+    mod, L = lib
+    # keys | P [R*gamma, 3r] | E [R*gamma, r] | state [2, R, r], each 256-aligned
+    R, g, r = 128, 16, 256
+    keys = g * L.dspark_markov_sample_workspace_bytes(R, 1, 151936, r, 1)
+    assert L.dspark_markov_head_sample_workspace_bytes(mod.HEAD_RNN, R, g, 151936, r) == \
+        keys + R * g * 3 * r * 4 + R * g * r * 4 + 2 * R * r * 4
+    assert L.dspark_markov_head_sample_workspace_bytes(mod.HEAD_GATED, R, g, 151936, r) == \
+        keys + R * g * r * 4 + R * g * r * 4
+    assert L.dspark_markov_head_sample_workspace_bytes(7, R, g, 151936, r) == 0
+    assert L.dspark_markov_head_block_logits_workspace_bytes(mod.HEAD_GATED, 4, 16, 1000, 64) == \
+        L.dspark_markov_block_logits_workspace_bytes(64, 1000, 64, 1) + 64 * 64 * 4 * 2
+    null = None
+    args = dict(kind=mod.HEAD_RNN, R=2, gamma=4, V=100, r=16, d=32, wdtype=1)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return L.dspark_markov_head_sample(a["kind"], null, null, null, null, null, null, null, null, a["R"],
+                                           a["gamma"], a["V"], a["r"], a["d"], a["wdtype"], 0.0, 0, null, 0,
+                                           null, null)
+    assert call(kind=0) == mod.ERR_INVALID_ARG
+    assert call(r=12) == mod.ERR_INVALID_ARG          # rank not a multiple of 8
+    assert call(r=520) == mod.ERR_INVALID_ARG         # rank above 512
+    assert call(d=30) == mod.ERR_INVALID_ARG          # hidden size not a multiple of 8
+    assert call(wdtype=5) == mod.ERR_INVALID_ARG
+    assert call(gamma=1025) == mod.ERR_INVALID_ARG
+    assert call() == mod.ERR_INVALID_ARG              # null pointers
+    assert call(R=0) == mod.OK                        # empty batch: nothing to do
+    assert b"null" in L.dspark_last_error() or True
+    rc = L.dspark_markov_head_block_logits(mod.HEAD_GATED, null, null, null, null, null, null, null, null, 2, 4,
+                                           100, 16, 32, 1, -1.0, null, 0, null, null)
+    assert rc == mod.ERR_INVALID_ARG                  # negative soft cap
