@@ -261,7 +261,8 @@ int dspark_markov_block_logits(const float* base_logits, const void* w1, const v
  *
  *   base_logits  [R, gamma, V] float32
  *   hidden       [R, gamma, d] bf16, 16-byte aligned; d a multiple of 8
- *   w1 [V, r], w2 [r, V]   wdtype (bf16 or float32); r a multiple of 8, <= 512
+ *   w1 [V, r] (16-byte aligned), w2 [r, V]   wdtype (bf16 or float32); r a
+ *                multiple of 8, <= 512
  *   whead        as above, bf16, 16-byte aligned
  *
  * dspark_markov_head_sample: the gamma-step sampler with the state carried

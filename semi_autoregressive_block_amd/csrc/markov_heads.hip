@@ -21,7 +21,8 @@
 //   bf16 MFMA contraction over d: v_mfma_f32_16x16x32_bf16 with both
 //   operands read straight from row-major memory as 16-byte pieces (lane
 //   (n, g) of a fragment holds row n, entries 8g .. 8g+7 of the 32-wide
-//   slab), 64 x 64 output tiles per workgroup of four waves.
+//   slab), 64 x 64 output tiles per workgroup, its four waves splitting
+//   the contraction.
 // * Per position, a small kernel finishes the maps with the recurrent inputs
 //   ([s; W1[x]], or W1[x] alone) in float32 (the state is never rounded),
 //   applies the nonlinearities, writes E (float32) and the next state.
@@ -38,76 +39,78 @@ constexpr int kHeadGated = 1;
 constexpr int kHeadRnn = 2;
 constexpr int kProjTile = 64;   // output rows and columns per projection workgroup
 constexpr int kRowsPer = 16;    // rows per recurrent-step workgroup
-constexpr int kChanPer = 16;    // channels per recurrent-step workgroup
+constexpr int kChanPer = 8;     // channels per recurrent-step workgroup
 constexpr int kMaxRank = 512;
 
 // P[i][c] = sum_k A[i][k] B[c][k] for i < M, c < N (bf16 in, float32 out).
 // A rows are lda elements apart, B rows ldb; K, lda, ldb multiples of 8 and
-// both bases 16-byte aligned (checked by the host).  Wave w of the
-// workgroup owns rows 32(w & 1) .. +31 and columns 32(w >> 1) .. +31 of the
-// tile: two A and two B fragments per 32-wide slab, four products.
+// both bases 16-byte aligned (checked by the host).  A workgroup owns a
+// 64 x 64 output tile; each of its four waves computes the whole tile (4 x 4
+// products) over every fourth 32-wide slab of K, interleaved so that the
+// waves stream neighbouring pieces of the same rows, with the next slab's
+// eight 16-byte pieces loaded while the current slab's products run.  The
+// four partial tiles are summed through LDS at the end.
 __global__ __launch_bounds__(256) void head_proj_mfma(const uint16_t* __restrict__ A, int64_t lda,
                                                       const uint16_t* __restrict__ B, int64_t ldb,
                                                       float* __restrict__ P, int64_t ldp, int M, int N, int K) {
+  __shared__ f32x4 red[3][16][64];  // partial tiles of waves 1..3
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, g = lane >> 4;
-  const int i0 = blockIdx.x * kProjTile + (wave & 1) * 32;
-  const int c0 = blockIdx.y * kProjTile + (wave >> 1) * 32;
-  const uint16_t* ap[2];
-  const uint16_t* bp[2];
+  const int i0 = blockIdx.x * kProjTile, c0 = blockIdx.y * kProjTile;
+  const uint16_t* ap[4];
+  const uint16_t* bp[4];
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
+  for (int t = 0; t < 4; ++t) {
     ap[t] = A + (int64_t)min(i0 + 16 * t + n, M - 1) * lda;
     bp[t] = B + (int64_t)min(c0 + 16 * t + n, N - 1) * ldb;
   }
-  f32x4 acc[2][2];
+  f32x4 acc[4][4];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // two slabs per iteration, the next pair's pieces loaded before this
-  // pair's products
-  constexpr int U = 2;
-  u32x4 fa[U][2], fb[U][2];
-  auto load = [&](int k0) {
+    for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  u32x4 fa[4], fb[4];
+  auto load = [&](int slab) {
+    const int k = slab * 32 + 8 * g;
+    const bool ok = k < K;  // K is a multiple of 8: the whole piece is in the row
+    const int kc = ok ? k : 0;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int k = k0 + 32 * u;
-      const bool ok = k + 8 * g < K;  // K is a multiple of 8: the whole piece is in the row
-      const int kc = ok ? k + 8 * g : 0;
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const u32x4 x = *(const u32x4*)(ap[t] + kc), y = *(const u32x4*)(bp[t] + kc);
-        fa[u][t] = ok ? x : u32x4{0u, 0u, 0u, 0u};
-        fb[u][t] = ok ? y : u32x4{0u, 0u, 0u, 0u};
-      }
+    for (int t = 0; t < 4; ++t) {
+      const u32x4 x = *(const u32x4*)(ap[t] + kc), y = *(const u32x4*)(bp[t] + kc);
+      fa[t] = ok ? x : u32x4{0u, 0u, 0u, 0u};
+      fb[t] = ok ? y : u32x4{0u, 0u, 0u, 0u};
     }
   };
-  load(0);
-  for (int k0 = 0; k0 < K; k0 += 32 * U) {
-    u32x4 ca[U][2], cb[U][2];
+  const int nslab = (K + 31) / 32;
+  if (wave < nslab) load(wave);
+  for (int sl = wave; sl < nslab; sl += 4) {
+    u32x4 ca[4], cb[4];
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+    for (int t = 0; t < 4; ++t) { ca[t] = fa[t]; cb[t] = fb[t]; }
+    if (sl + 4 < nslab) load(sl + 4);
 #pragma unroll
-      for (int t = 0; t < 2; ++t) { ca[u][t] = fa[u][t]; cb[u][t] = fb[u][t]; }
-    if (k0 + 32 * U < K) load(k0 + 32 * U);
+    for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int b = 0; b < 2; ++b) acc[a][b] = mfma16x16x32(cb[u][b], ca[u][a], acc[a][b]);
+      for (int b = 0; b < 4; ++b) acc[a][b] = mfma16x16x32(cb[b], ca[a], acc[a][b]);
   }
+  if (wave > 0) {
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) red[wave - 1][4 * a + b][lane] = acc[a][b];
+  }
+  __syncthreads();
+  if (wave > 0) return;
   // lane (n, g) of product (a, b) holds row i0 + 16a + n, columns
   // c0 + 16b + 4g .. +3 (N is a multiple of 4)
 #pragma unroll
-  for (int a = 0; a < 2; ++a) {
+  for (int a = 0; a < 4; ++a) {
     const int i = i0 + 16 * a + n;
-    if (i >= M) continue;
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
+    for (int b = 0; b < 4; ++b) {
+      const f32x4 v = acc[a][b] + red[0][4 * a + b][lane] + red[1][4 * a + b][lane] + red[2][4 * a + b][lane];
       const int c = c0 + 16 * b + 4 * g;
-      if (c < N) *(f32x4*)(P + (int64_t)i * ldp + c) = acc[a][b];
+      if (i < M && c < N) *(f32x4*)(P + (int64_t)i * ldp + c) = v;
     }
   }
 }
@@ -119,14 +122,28 @@ __device__ __forceinline__ float ldw(const void* p, int64_t i) {
 
 __device__ __forceinline__ float sigm(float x) { return 1.f / (1.f + expf(-x)); }
 
-// One position of every row: rows row0 .. +15 and channels j0 .. +15 per
-// workgroup, one (row, channel) per thread.
-//   z = [s; W1[x]] (RNN, length 2r) or W1[x] (gated, length r), staged in LDS
+// One position of every row: rows row0 .. +15 and channels j0 .. +7 per
+// workgroup; thread t takes (row i, channel jj) = ((t mod 128) / 8,
+// t mod 8) and half kh = t / 128 of every chunk of the contraction, the two
+// halves summed through LDS at the end.
+//   z = [s; W1[x]] (RNN, length 2r) or W1[x] (gated, length r), in LDS
 //   acc_q = W_q,rec[j] . z  (q = gate, candidate, output; or the gate alone)
-// W_q,rec rows are ldw elements apart, matrix q at wrec + q * mstride; the
-// hidden-state part arrives in P[row, step, q * r + j].  The previous token
+// W_q,rec rows are ldwr elements apart, matrix q at wrec + q * mstride; the
+// hidden-state part arrives in P[row, step, q * r + j].  The workgroup's
+// weight rows are staged in LDS as float32 in 256-wide chunks of z, the next
+// chunk's 16-byte loads in flight while the current chunk is used.  Rows
+// are padded by 4 floats so that the rows a wave reads at one k fall in
+// distinct LDS banks.  The first chunk and the hidden-state terms, which do
+// not depend on the previous token, are loaded first.  The previous token
 // is the caller's (prev_tok[row * prev_stride]) or the argmax folded in the
 // previous step's keys.
+constexpr int kChunk = 256;          // z entries per staged weight chunk
+constexpr int kWPad = kChunk + 4;    // floats per staged weight row
+__host__ __device__ constexpr size_t head_step_lds(bool rnn, int r) {
+  return (size_t)(rnn ? 3 : 1) * kChanPer * kWPad * 4 + (size_t)kRowsPer * ((rnn ? 2 : 1) * r + 4) * 4 +
+         kRowsPer * 4 + (size_t)(rnn ? 3 : 1) * 128 * 4;
+}
+
 template <bool RNN, bool kBf16W1>
 __global__ __launch_bounds__(256) void head_step_kernel(
     const float* __restrict__ P, const void* __restrict__ w1, const uint16_t* __restrict__ wrec, int64_t ldwr,
@@ -134,15 +151,51 @@ __global__ __launch_bounds__(256) void head_step_kernel(
     const uint64_t* __restrict__ keys_prev, const float* __restrict__ s_in, float* __restrict__ s_out,
     float* __restrict__ ebuf, int R, int gamma, int V, int r, int step, int32_t* __restrict__ status) {
   extern __shared__ __align__(16) unsigned char smem[];
-  const int zlen = RNN ? 2 * r : r;
-  float* z = (float*)smem;                           // [kRowsPer][zlen]
-  int* pv = (int*)(smem + (size_t)kRowsPer * zlen * 4);  // [kRowsPer]
+  constexpr int NQ = RNN ? 3 : 1;
+  const int zlen = RNN ? 2 * r : r, zst = zlen + 4;
+  float* wl = (float*)smem;                          // [NQ][kChanPer][kWPad]
+  float* z = wl + NQ * kChanPer * kWPad;             // [kRowsPer][zst]
+  int* pv = (int*)(z + kRowsPer * zst);              // [kRowsPer]
+  float* red = (float*)(pv + kRowsPer);              // [NQ][128]
   const int row0 = blockIdx.x * kRowsPer, j0 = blockIdx.y * kChanPer;
+  const int t = threadIdx.x & 127, kh = threadIdx.x >> 7;
+  const int i = t / kChanPer, jj = t % kChanPer, j = j0 + jj, row = row0 + i;
+  // weight chunk c0: NQ x 8 rows of cw / 8 pieces, at most NQ per thread
+  constexpr int kPer = NQ * kChanPer * (kChunk / 8) / 256;
+  u32x4 wv[kPer];
+  auto load_chunk = [&](int c0) {
+    const int n8 = min(kChunk, zlen - c0) / 8, total = NQ * kChanPer * n8;
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int e = min((int)threadIdx.x + 256 * u, total - 1);
+      const int q = e / (kChanPer * n8), rem = e % (kChanPer * n8), jr = rem / n8, k8 = rem % n8;
+      wv[u] = *(const u32x4*)(wrec + q * mstride + (int64_t)min(j0 + jr, r - 1) * ldwr + c0 + 8 * k8);
+    }
+  };
+  auto store_chunk = [&](int c0) {
+    const int n8 = min(kChunk, zlen - c0) / 8, total = NQ * kChanPer * n8;
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int e = threadIdx.x + 256 * u;
+      if (e < total) {
+        const int q = e / (kChanPer * n8), rem = e % (kChanPer * n8), jr = rem / n8, k8 = rem % n8;
+        float* dst = wl + (q * kChanPer + jr) * kWPad + 8 * k8;
+        const u32x4 w = wv[u];
+        *(f32x4*)dst = f32x4{bf16lo(w[0]), bf16hi(w[0]), bf16lo(w[1]), bf16hi(w[1])};
+        *(f32x4*)(dst + 4) = f32x4{bf16lo(w[2]), bf16hi(w[2]), bf16lo(w[3]), bf16hi(w[3])};
+      }
+    }
+  };
+  load_chunk(0);
+  const int64_t pos = (int64_t)min(row, R - 1) * gamma + step;
+  float hp[NQ];
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) hp[q] = P[pos * (NQ * r) + q * r + min(j, r - 1)];
   if (threadIdx.x < kRowsPer) {
-    const int row = row0 + threadIdx.x;
+    const int rw = row0 + threadIdx.x;
     int p = 0;
-    if (row < R) {
-      p = keys_prev ? (int)argmax_key_index(read_key(keys_prev, row, R)) : prev_tok[(int64_t)row * prev_stride];
+    if (rw < R) {
+      p = keys_prev ? (int)argmax_key_index(read_key(keys_prev, rw, R)) : prev_tok[(int64_t)rw * prev_stride];
       if (p < 0 || p >= V) {
         if (blockIdx.y == 0) status_or(status, DSPARK_STATUS_BAD_TOKEN);
         p = 0;
@@ -151,46 +204,87 @@ __global__ __launch_bounds__(256) void head_step_kernel(
     pv[threadIdx.x] = p;
   }
   __syncthreads();
-  for (int c = threadIdx.x; c < kRowsPer * zlen; c += 256) {
-    const int rr = c / zlen, k = c % zlen, row = row0 + rr;
-    float v = 0.f;
-    if (row < R) {
-      if (RNN && k < r) v = s_in[(int64_t)row * r + k];
-      else v = ldw<kBf16W1>(w1, (int64_t)pv[rr] * r + (RNN ? k - r : k));
+  // z: 16-byte pieces from clamped, always-valid addresses (rows past R
+  // read row R - 1 or token 0 and are never stored), in batches of 4 loads
+  // per thread issued before any conversion or LDS store
+  if constexpr (RNN) {
+    const int n4 = r / 4, total = kRowsPer * n4;
+    for (int c0 = threadIdx.x; c0 < total; c0 += 256 * 4) {
+      f32x4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int cc = min(c0 + 256 * u, total - 1), rr = cc / n4, k4 = cc % n4;
+        v[u] = *(const f32x4*)(s_in + (int64_t)min(row0 + rr, R - 1) * r + 4 * k4);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int c = c0 + 256 * u;
+        if (c < total) *(f32x4*)(z + (c / n4) * zst + 4 * (c % n4)) = v[u];
+      }
     }
-    z[c] = v;
   }
-  __syncthreads();
-  const int i = threadIdx.x / kChanPer, j = j0 + threadIdx.x % kChanPer, row = row0 + i;
-  constexpr int NQ = RNN ? 3 : 1;
+  {
+    constexpr int per = kBf16W1 ? 8 : 4;  // W1 entries per 16-byte piece
+    const int ne = r / per, total = kRowsPer * ne, eoff = RNN ? r : 0;
+    for (int c0 = threadIdx.x; c0 < total; c0 += 256 * 4) {
+      u32x4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int cc = min(c0 + 256 * u, total - 1), rr = cc / ne, kp = cc % ne;
+        v[u] = *(const u32x4*)((const char*)w1 + ((int64_t)pv[rr] * r + (int64_t)kp * per) * (kBf16W1 ? 2 : 4));
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int c = c0 + 256 * u;
+        if (c >= total) continue;
+        float* dst = z + (c / ne) * zst + eoff + (c % ne) * per;
+        if constexpr (kBf16W1) {
+          *(f32x4*)dst = f32x4{bf16lo(v[u][0]), bf16hi(v[u][0]), bf16lo(v[u][1]), bf16hi(v[u][1])};
+          *(f32x4*)(dst + 4) = f32x4{bf16lo(v[u][2]), bf16hi(v[u][2]), bf16lo(v[u][3]), bf16hi(v[u][3])};
+        } else {
+          *(f32x4*)dst = __builtin_bit_cast(f32x4, v[u]);
+        }
+      }
+    }
+  }
   float acc[NQ];
 #pragma unroll
   for (int q = 0; q < NQ; ++q) acc[q] = 0.f;
-  const int jc = min(j, r - 1);
-  const float* zr = z + i * zlen;
-  for (int k = 0; k < zlen; k += 8) {
-    const f32x4 z0 = *(const f32x4*)(zr + k), z1 = *(const f32x4*)(zr + k + 4);
+  const float* zr = z + i * zst;
+  for (int c0 = 0; c0 < zlen; c0 += kChunk) {
+    const int cw = min(kChunk, zlen - c0);  // a multiple of 8: halves of multiples of 4
+    __syncthreads();                        // z staged / previous chunk consumed
+    store_chunk(c0);
+    if (c0 + kChunk < zlen) load_chunk(c0 + kChunk);
+    __syncthreads();
+    const int k0 = kh * (cw / 2), k1 = k0 + cw / 2;
+    for (int k = k0; k < k1; k += 4) {
+      const f32x4 zv = *(const f32x4*)(zr + c0 + k);
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-      const u32x4 w = *(const u32x4*)(wrec + q * mstride + (int64_t)jc * ldwr + k);
-      float a = acc[q];
-      a = fmaf(bf16lo(w[0]), z0[0], a); a = fmaf(bf16hi(w[0]), z0[1], a);
-      a = fmaf(bf16lo(w[1]), z0[2], a); a = fmaf(bf16hi(w[1]), z0[3], a);
-      a = fmaf(bf16lo(w[2]), z1[0], a); a = fmaf(bf16hi(w[2]), z1[1], a);
-      a = fmaf(bf16lo(w[3]), z1[2], a); a = fmaf(bf16hi(w[3]), z1[3], a);
-      acc[q] = a;
+      for (int q = 0; q < NQ; ++q) {
+        const f32x4 w = *(const f32x4*)(wl + (q * kChanPer + jj) * kWPad + k);
+        float a = acc[q];
+        a = fmaf(w[0], zv[0], a); a = fmaf(w[1], zv[1], a);
+        a = fmaf(w[2], zv[2], a); a = fmaf(w[3], zv[3], a);
+        acc[q] = a;
+      }
     }
   }
-  if (row >= R || j >= r) return;
-  const int64_t pos = (int64_t)row * gamma + step;
-  const float* p = P + pos * (NQ * r);
+  if (kh == 1) {
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) red[q * 128 + t] = acc[q];
+  }
+  __syncthreads();
+  if (kh == 1 || row >= R || j >= r) return;
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) acc[q] += red[q * 128 + t];
   if constexpr (RNN) {
-    const float gt = sigm(acc[0] + p[j]);
-    const float cand = tanhf(acc[1] + p[r + j]);
-    ebuf[pos * r + j] = tanhf(acc[2] + p[2 * r + j]);
+    const float gt = sigm(acc[0] + hp[0]);
+    const float cand = tanhf(acc[1] + hp[1]);
+    ebuf[pos * r + j] = tanhf(acc[2] + hp[2]);
     s_out[(int64_t)row * r + j] = gt * zr[j] + (1.f - gt) * cand;
   } else {
-    ebuf[pos * r + j] = sigm(acc[0] + p[j]) * zr[j];
+    ebuf[pos * r + j] = sigm(acc[0] + hp[0]) * zr[j];
   }
 }
 
@@ -266,7 +360,7 @@ hipError_t run_head(const HeadArgs& a, const int32_t* prev_tok, int64_t prev_str
   }
   const uint16_t* wrec = wh + (rnn ? 0 : a.d);
   const int64_t mstride = (int64_t)a.r * ldw;
-  const size_t shm = (size_t)kRowsPer * (rnn ? 2 : 1) * a.r * 4 + kRowsPer * 4;
+  const size_t shm = head_step_lds(rnn, a.r);
   const dim3 grid((a.R + kRowsPer - 1) / kRowsPer, (a.r + kChanPer - 1) / kChanPer);
   for (int k = 0; k < a.gamma; ++k) {
     const float* sin = S + (int64_t)(k & 1) * a.R * a.r;
@@ -295,8 +389,8 @@ hipError_t run_head(const HeadArgs& a, const int32_t* prev_tok, int64_t prev_str
 
 int check_alignment(const char* what, const HeadArgs& a) {
   using namespace dspark_host;
-  if ((uintptr_t)a.hidden % 16 || (uintptr_t)a.whead % 16)
-    return fail(DSPARK_ERR_INVALID_ARG, "%s: hidden and head weights must be 16-byte aligned", what);
+  if ((uintptr_t)a.hidden % 16 || (uintptr_t)a.whead % 16 || (uintptr_t)a.w1 % 16)
+    return fail(DSPARK_ERR_INVALID_ARG, "%s: hidden, w1 and head weights must be 16-byte aligned", what);
   return 0;
 }
 
