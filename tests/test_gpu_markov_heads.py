@@ -88,6 +88,8 @@ CASES = [
     ("rnn", 4, 6, 3000, 32, 64, "f32", 0.0),       # float32 W1/W2
     ("gated", 4, 4, 2048, 32, 64, "f32", 5.0),     # soft cap
     ("rnn", 2, 3, 1024, 512, 64, "bf16", 30.0),    # rank 512 (64 KB of staged state), soft cap
+    ("rnn", 3, 2, 512, 8, 8, "bf16", 0.0),         # smallest rank and hidden size: the contraction is all tail
+    ("gated", 1, 1, 64, 8, 24, "f32", 0.0),        # one position, d below one 32-wide slab
 ]
 
 
@@ -158,3 +160,29 @@ def test_wrong_head_shape_is_rejected(dsp):
     base, hidden, w1, w2, whead, prev = _inputs(4, "gated", 2, 3, 256, 16, 32, "bf16")
     with pytest.raises(ValueError):
         dsp.markov_head_block_logits("rnn", *_dev_args(base, hidden, w1, w2, whead, "bf16"), dev(prev))
+
+
+def test_empty_batch_is_a_no_op(dsp):
+    base, hidden, w1, w2, whead, _ = _inputs(8, "rnn", 1, 4, 256, 16, 32, "bf16")
+    args = _dev_args(base[:0], hidden[:0], w1, w2, whead, "bf16")
+    tok, _ = dsp.markov_head_sample("rnn", *args, dev(np.zeros(0, dtype=np.int32)))
+    assert tuple(tok.shape) == (0, 4)
+    logits, _ = dsp.markov_head_block_logits("rnn", *args, dev(np.zeros((0, 4), dtype=np.int32)))
+    assert tuple(logits.shape) == (0, 4, 256)
+
+
+def test_workspace_reused_by_a_smaller_call(dsp):
+    """One workspace, two calls in a row (the second on fewer rows and
+    steps): the state, the projection and the key slots are rebuilt each
+    call, so the second result matches the oracle too."""
+    R, G, V, r, d = 40, 6, 2048, 32, 64
+    ws = torch.empty(dsp.markov_head_sample_workspace_bytes("rnn", R, G, V, r), dtype=torch.uint8, device=DEV)
+    for seed, (rr, gg) in ((11, (R, G)), (12, (17, 3))):
+        base, hidden, w1, w2, whead, _ = _inputs(seed, "rnn", rr, gg, V, r, d, "bf16")
+        first = np.random.default_rng(seed).integers(0, V, size=rr).astype(np.int32)
+        tok, sl = dsp.markov_head_sample("rnn", *_dev_args(base, hidden, w1, w2, whead, "bf16"), dev(first),
+                                         want_step_logits=True, workspace=ws)
+        tok = tok.cpu().numpy().astype(np.int64)
+        _, z, l = OH.sample_block_tokens("rnn", base, *_ref_args(hidden, w1, w2, whead, "bf16"), first, teacher=tok)
+        _check_logits(sl.cpu().numpy(), l, "bf16", base)
+        _check_tokens(tok, z, 2 * _bar("bf16"))
