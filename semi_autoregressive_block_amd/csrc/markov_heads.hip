@@ -130,14 +130,14 @@ __device__ __forceinline__ float sigm(float x) { return 1.f / (1.f + expf(-x)); 
 //   acc_q = W_q,rec[j] . z  (q = gate, candidate, output; or the gate alone)
 // W_q,rec rows are ldwr elements apart, matrix q at wrec + q * mstride; the
 // hidden-state part arrives in P[row, step, q * r + j].  The workgroup's
-// weight rows are staged in LDS as float32 in 256-wide chunks of z, the next
+// weight rows are staged in LDS as float32 in 512-wide chunks of z, the next
 // chunk's 16-byte loads in flight while the current chunk is used.  Rows
 // are padded by 4 floats so that the rows a wave reads at one k fall in
 // distinct LDS banks.  The first chunk and the hidden-state terms, which do
 // not depend on the previous token, are loaded first.  The previous token
 // is the caller's (prev_tok[row * prev_stride]) or the argmax folded in the
 // previous step's keys.
-constexpr int kChunk = 256;          // z entries per staged weight chunk
+constexpr int kChunk = 512;          // z entries per staged weight chunk
 constexpr int kWPad = kChunk + 4;    // floats per staged weight row
 __host__ __device__ constexpr size_t head_step_lds(bool rnn, int r) {
   return (size_t)(rnn ? 3 : 1) * kChanPer * kWPad * 4 + (size_t)kRowsPer * ((rnn ? 2 : 1) * r + 4) * 4 +
