@@ -14,7 +14,8 @@ each definition states.  Sources, cited per function:
   sections 3.1–3.13;
 * page 2 — "从 DFlash 到 dLLM Self-Spec（三）" (r00kie-liu.github.io),
   sections 3.4, 3.5, 3.8;
-* page 4 — "DSpark 深度解读" (juejin.cn), sections 3.2–3.4, 4.1 and 5.1;
+* page 3 — "DSpark 论文精读", the speculative-decoding primer;
+* page 4 — "DSpark 深度解读" (juejin.cn), sections 1.2, 3.2–3.4, 4.1 and 5.1;
 * Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3"
   (SC'11) for the Philox counter-based generator.
 
@@ -34,6 +35,9 @@ Modules:
 * ``markov_heads``— gated and recurrent Markov heads: step embedding,
                     teacher-forced block logits and the stateful sampler
                     (page 1 §3.7; page 4 §3.3).
+* ``verify``      — the lossless verify step: rejection sampling of a drafted
+                    block against the target (page 3's primer, page 4 §1.2;
+                    the published speculative-sampling rule).
 * ``philox``      — Philox4x32-10 / 4x64-10 and the Gumbel noise built on it.
 
 Every function here is pinned by a ``-m "not gpu"`` test against something
@@ -41,4 +45,4 @@ other than itself (closed forms, brute force, library routines, published
 known-answer vectors); there is no "parity unpinned" function.
 """
 
-from . import accept_rate, attention, eval_mask, markov, markov_heads, philox, scheduler, tv_loss  # noqa: F401
+from . import accept_rate, attention, eval_mask, markov, markov_heads, philox, scheduler, tv_loss, verify  # noqa: F401

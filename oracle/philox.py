@@ -96,13 +96,16 @@ def philox4x64(counter, key, rounds=10):
     return tuple(int(x) for x in out)
 
 
-def gumbel_uniform_bits(seed, row, step, V):
-    """Raw 32-bit draws x[v], v in [0, V), for one (row, step)."""
+def gumbel_uniform_bits(seed, row, step, V, stream=0):
+    """Raw 32-bit draws x[v], v in [0, V), for one (row, step); `stream` is
+    the fourth counter word (0 for the draft sampler's noise; other values
+    give streams independent of it)."""
     nblk = (V + 3) // 4
     ctr = np.zeros((nblk, 4), dtype=np.uint64)
     ctr[:, 0] = np.arange(nblk, dtype=np.uint64)
     ctr[:, 1] = step
     ctr[:, 2] = row
+    ctr[:, 3] = stream
     key = (int(seed) & 0xFFFFFFFF, (int(seed) >> 32) & 0xFFFFFFFF)
     words = philox4x32(ctr, key)  # [nblk, 4]; word (v & 3) of block (v >> 2)
     return words.reshape(-1)[:V]
@@ -114,7 +117,7 @@ def uniform_from_bits(x):
     return ((x >> np.uint64(9)).astype(np.float64) + 0.5) * 2.0 ** -23
 
 
-def gumbel(seed, row, step, V):
+def gumbel(seed, row, step, V, stream=0):
     """Gumbel(0,1) noise G[v] = -ln(-ln u[v]) for one (row, step), float64."""
-    u = uniform_from_bits(gumbel_uniform_bits(seed, row, step, V))
+    u = uniform_from_bits(gumbel_uniform_bits(seed, row, step, V, stream))
     return -np.log(-np.log(u))
