@@ -18,14 +18,15 @@ on the same 4 x 512 x 8-row shape: the L1 (TV) loss with its float32
 gradient and tau_greedy ("l1_loss") and the teacher-forced Markov block
 logits ("block_logits"), and, at the serving shape, the confidence head with
 the verify-length scheduler ("confidence_schedule"), and the gated and
-recurrent Markov-head samplers ("markov_heads").
+recurrent Markov-head samplers ("markov_heads") and the lossless verify
+step ("verify").
 
 Prints ONE JSON line: metric, value (drafted tokens/s), ms_per_step, the
 per-operation breakdown, the roofline of the dominant kernel (achieved
 algorithmic GB/s from HIP events on the launch stream vs the 8 TB/s HBM
 peak) and the CPU oracle timed on a bounded sample of the same workload.
 
---only {round,attention,markov,accept,train_attention,copy,block_logits,l1_loss,schedule,heads} restricts the run to one part
+--only {round,attention,markov,accept,train_attention,copy,block_logits,l1_loss,schedule,heads,verify} restricts the run to one part
 (for profiler runs); --no-cpu skips the CPU baseline.
 """
 
@@ -51,7 +52,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--only", choices=["round", "attention", "markov", "accept", "train_attention", "copy",
-                                       "block_logits", "l1_loss", "schedule", "heads"],
+                                       "block_logits", "l1_loss", "schedule", "heads", "verify"],
                     default=None)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -345,6 +346,26 @@ def main():
         del base, hid, w1h, w2h, heads
         torch.cuda.empty_cache()
 
+    if args.only in (None, "verify"):
+        # lossless verify of 128 drafted blocks of 16 tokens, V = 151936, T = 1,
+        # draft logits near the target's (about half the drafts kept)
+        g = torch.Generator(device=dev).manual_seed(W.SEED_BASE + 70)
+        R, Kv, V = 128, 16, 151936
+        tl = torch.randn((R, Kv + 1, V), generator=g, device=dev).mul_(2)
+        dl = tl[:, :Kv] + torch.randn((R, Kv, V), generator=g, device=dev).mul_(0.3)
+        xt = torch.distributions.Categorical(logits=dl).sample().to(torch.int32)
+        ws = torch.empty(dsp.verify_workspace_bytes(R, Kv), dtype=torch.uint8, device=dev)
+        nv, tv = torch.empty(R, dtype=torch.int32, device=dev), torch.empty(R, dtype=torch.int32, device=dev)
+        f_v = lambda: dsp.verify(dl, tl, xt, temperature=1.0, seed=3, n_accepted=nv, next_token=tv, workspace=ws)
+        v_ms = timed(torch, f_v, K, Wm)
+        v_bytes = (2 * Kv + 1) * R * V * 4 + 2 * R * V * 4  # every position's logits once, the stop row twice
+        if args.only == "verify":
+            print(json.dumps({"verify_ms": v_ms, "GBps": v_bytes / v_ms / 1e6}))
+            return
+        result["verify"] = dict(ms=v_ms, bytes=v_bytes, mean_kept=float(nv.float().mean().item()))
+        del tl, dl, xt
+        torch.cuda.empty_cache()
+
     if args.only in (None, "schedule"):
         # confidence head + verify-length scheduler at the serving shape: 128
         # blocks of 16 positions, hidden size 4096 (32 heads x 128), Markov
@@ -409,6 +430,12 @@ def main():
         line["accept_rate"] = {"workload": "4 x 512 x 8 rows, V=151936 bf16, with tau",
                                "ms": a["ms"], "GBps": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
                                "rows_per_s": 16384 / (a["ms"] / 1e3)}
+    if "verify" in result:
+        a = result["verify"]
+        gbs = a["bytes"] / a["ms"] / 1e6
+        line["verify"] = {"workload": "128 drafted blocks of 16 tokens, V=151936, float32 draft and target logits, "
+                                      "T=1", "ms": a["ms"], "GBps": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
+                          "mean_kept": a["mean_kept"]}
     if "heads" in result:
         line["markov_heads"] = {"workload": "gamma = 16 sampling steps for 128 requests, V=151936, rank 256, "
                                             "hidden 4096 bf16, float32 base, greedy",

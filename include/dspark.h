@@ -16,6 +16,7 @@
  *                               the same for the gated and recurrent heads
  *   dspark_l1_loss              L1 (TV) alignment loss, its gradient, tau_greedy
  *   dspark_confidence_schedule  confidence head, prefix survival, verify length
+ *   dspark_verify               lossless verify (rejection sampling) of a drafted block
  *
  * Sources (cited per entry point): page 1 = "03 · DSpark 建模：Markov 与
  * Confidence" (devpress.csdn.net), page 2 = "从 DFlash 到 dLLM Self-Spec
@@ -293,6 +294,32 @@ int dspark_markov_head_block_logits(int kind, const float* base_logits, const vo
                                     int32_t* argmax_tokens, int B, int gamma, int V, int r, int d, int wdtype,
                                     float softcap, void* ws, size_t ws_bytes, int32_t* dev_status,
                                     void* stream);
+
+/* ------------------------------------------------------------------------
+ * Lossless verify step (page 3's speculative-decoding primer; page 4 §1.2):
+ * rejection sampling of R drafted blocks of K tokens against the target.
+ * The pages give the outline; the steps are the published speculative-
+ * sampling rule: q_k = softmax(draft[k] / T), p_k = softmax(target[k] / T);
+ * keep x_k while u_k < p_k(x_k) / q_k(x_k); at the first rejected k draw
+ * from max(0, p_k - q_k) normalised; if all K are kept draw one more token
+ * from p_K.  T = 0: keep x_k while it is the target's argmax (lowest index
+ * on ties); the extra token is that argmax at the stopping position.
+ * Random numbers: Philox4x32-10 keyed by seed; u_k = word 0 at counter
+ * (k, 0, row, 2) as ((x >> 9) + 1/2) 2^-23; draws are Gumbel-max with word
+ * v & 3 at counter (v >> 2, k, row, 1).  float32 arithmetic.
+ *
+ *   draft_logits  [R, K, V] float32 (the draft's step logits)
+ *   target_logits [R, K + 1, V] float32
+ *   draft_tokens  [R, K] int32 (outside [0, V): token 0 is used and
+ *                 DSPARK_STATUS_BAD_TOKEN set in *dev_status, nullable)
+ *   n_accepted    [R] int32 (out): kept drafts, 0 .. K
+ *   next_token    [R] int32 (out): the target's token after them
+ * Workspace from dspark_verify_workspace_bytes (256-byte aligned).
+ * ---------------------------------------------------------------------- */
+size_t dspark_verify_workspace_bytes(int R, int K);
+int dspark_verify(const float* draft_logits, const float* target_logits, const int32_t* draft_tokens,
+                  int32_t* n_accepted, int32_t* next_token, int R, int K, int V, float temperature,
+                  uint64_t seed, void* ws, size_t ws_bytes, int32_t* dev_status, void* stream);
 
 /* ------------------------------------------------------------------------
  * L1 (total-variation) alignment loss, its gradient and tau_greedy (page 1

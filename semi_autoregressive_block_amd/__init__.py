@@ -359,6 +359,40 @@ def markov_head_block_logits(kind, base, hidden, w1, w2, whead, prev, *, softcap
     return logits, tokens
 
 
+def verify_workspace_bytes(R, K) -> int:
+    return int(_LIB.dspark_verify_workspace_bytes(R, K))
+
+
+def verify(draft_logits, target_logits, draft_tokens, *, temperature=1.0, seed=0, n_accepted=None,
+           next_token=None, status=None, workspace=None):
+    """Lossless verify of R drafted blocks.  draft_logits [R, K, V] float32;
+    target_logits [R, K + 1, V] float32; draft_tokens [R, K] int32.  Returns
+    (n_accepted [R] int32, next_token [R] int32)."""
+    dev = target_logits.device
+    _check(target_logits, "target_logits", torch.float32, ndim=3)
+    R, K1, V = target_logits.shape
+    K = K1 - 1
+    _check(draft_logits, "draft_logits", torch.float32, dev, 3)
+    _check(draft_tokens, "draft_tokens", torch.int32, dev, 2)
+    if tuple(draft_logits.shape) != (R, K, V) or tuple(draft_tokens.shape) != (R, K):
+        raise ValueError("draft_logits must be [R, K, V] and draft_tokens [R, K] for target_logits [R, K + 1, V]")
+    if n_accepted is None:
+        n_accepted = torch.empty((R,), dtype=torch.int32, device=dev)
+    if next_token is None:
+        next_token = torch.empty((R,), dtype=torch.int32, device=dev)
+    _check(n_accepted, "n_accepted", torch.int32, dev, 1)
+    _check(next_token, "next_token", torch.int32, dev, 1)
+    if status is not None:
+        _check(status, "status", torch.int32, dev)
+    ws, wsb = _workspace(verify_workspace_bytes(R, K), dev, workspace)
+    rc = _LIB.dspark_verify(_ptr(draft_logits), _ptr(target_logits), _ptr(draft_tokens), _ptr(n_accepted),
+                            _ptr(next_token), R, K, V, float(temperature), int(seed) & (2**64 - 1), _ptr(ws), wsb,
+                            _ptr(status), _stream(dev))
+    if rc != 0:
+        raise DSparkError(rc, "verify")
+    return n_accepted, next_token
+
+
 def l1_loss_workspace_bytes(B, A, gamma) -> int:
     return int(_LIB.dspark_l1_loss_workspace_bytes(B, A, gamma))
 

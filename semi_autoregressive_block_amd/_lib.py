@@ -54,6 +54,8 @@ SIGNATURES = {
     "dspark_markov_head_block_logits_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
     "dspark_markov_head_block_logits": (_i, [_i, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _f,
                                              _p, _sz, _p, _p]),
+    "dspark_verify_workspace_bytes": (_sz, [_i, _i]),
+    "dspark_verify": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _f, _u64, _p, _sz, _p, _p]),
     "dspark_confidence_schedule": (_i, [_p, _i, _p, _f, _p, _i, _p, _p, _i, _i, _p, _p, _p, _p, _p,
                                         _i, _i, _i, _i, _p, _p]),
 }

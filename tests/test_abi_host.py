@@ -33,7 +33,7 @@ def lib():
 def test_every_declared_symbol_is_exported(lib):
     mod, L = lib
     names = _declared()
-    assert len(names) == 19, names
+    assert len(names) == 21, names
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(mod.SIGNATURES)
@@ -207,3 +207,14 @@ def test_head_workspaces_and_bad_arguments(lib):
     rc = L.dspark_markov_head_block_logits(mod.HEAD_GATED, null, null, null, null, null, null, null, null, 2, 4,
                                            100, 16, 32, 1, -1.0, null, 0, null, null)
     assert rc == mod.ERR_INVALID_ARG                  # negative soft cap
+
+
+def test_verify_workspace_and_bad_arguments(lib):
+    mod, L = lib
+    assert L.dspark_verify_workspace_bytes(128, 16) == 128 * 17 * 8 * 4 + 512 + 1024
+    assert L.dspark_verify_workspace_bytes(0, 16) == 0
+    n = None
+    assert L.dspark_verify(n, n, n, n, n, 4, 2, 0, 1.0, 0, n, 0, n, n) == mod.ERR_INVALID_ARG      # V = 0
+    assert L.dspark_verify(n, n, n, n, n, 4, 2, 10, -1.0, 0, n, 0, n, n) == mod.ERR_INVALID_ARG    # T < 0
+    assert L.dspark_verify(n, n, n, n, n, 4, 2, 10, 1.0, 0, n, 0, n, n) == mod.ERR_INVALID_ARG     # null pointers
+    assert L.dspark_verify(n, n, n, n, n, 0, 2, 10, 1.0, 0, n, 0, n, n) == mod.OK                  # nothing to do

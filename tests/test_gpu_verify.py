@@ -1,0 +1,125 @@
+"""Lossless verify step on the GPU vs the oracle.
+
+Bars: the number of kept drafts is exact except where the decisive
+acceptance test is a float32 near-tie (|u - p/q| within 1e-4 relative);
+the extra token equals the oracle's draw wherever the oracle's top-2 margin
+of the Gumbel-max values exceeds 1e-3 and otherwise lies within 1e-3 of the
+maximum; greedy verification is exact."""
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import DEV, dev
+from oracle import philox
+from oracle import verify as VF
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dsp():
+    import semi_autoregressive_block_amd as m
+    return m
+
+
+def _inputs(seed, R, K, V, spread=0.7):
+    rng = np.random.default_rng(seed)
+    t = (rng.standard_normal((R, K + 1, V)) * 2).astype(np.float32)
+    d = (t[:, :K] + rng.standard_normal((R, K, V)) * spread).astype(np.float32)
+    q = VF.softmax(d)
+    x = np.array([[rng.choice(V, p=q[i, k]) for k in range(K)] for i in range(R)], dtype=np.int32).reshape(R, K)
+    return d, t, x
+
+
+def _oracle_z(d, t, k, K, V, T, seed, row):
+    g = philox.gumbel(seed, row, k, V, stream=1)
+    if k == K:
+        return t[k].astype(np.float64) / T + g
+    p, q = VF.softmax(t[k] / T), VF.softmax(d[k] / T)
+    with np.errstate(divide="ignore"):
+        return np.log(np.maximum(p - q, 0.0)) + g
+
+
+def _check(dsp, d, t, x, T, seed, rows=None):
+    R, K = x.shape
+    V = t.shape[-1]
+    n, tok = dsp.verify(dev(d), dev(t), dev(x), temperature=T, seed=seed)
+    n, tok = n.cpu().numpy(), tok.cpu().numpy()
+    rows = range(R) if rows is None else rows
+    same = 0
+    for i in rows:
+        n_or, tok_or, ratios, us = VF.verify_row(d[i], t[i], x[i], T, seed, i)
+        if n[i] != n_or:
+            k = min(n[i], n_or)
+            assert abs(us[k] - ratios[k]) <= 1e-4 * max(1.0, ratios[k]), (i, n[i], n_or)
+            continue
+        same += 1
+        z = _oracle_z(d[i], t[i], n_or, K, V, T, seed, i)
+        assert z[tok[i]] >= z.max() - 1e-3, (i, tok[i], tok_or)
+        top2 = np.sort(z)[-2:]
+        if top2[1] - top2[0] > 1e-3:
+            assert tok[i] == tok_or, (i, tok[i], tok_or)
+    assert same >= 0.9 * len(rows)
+    return n
+
+
+@pytest.mark.parametrize("R,K,V,T", [(64, 4, 1000, 1.0), (48, 8, 4099, 0.7), (5, 1, 7, 1.3)])
+def test_random_blocks(dsp, R, K, V, T):
+    d, t, x = _inputs(R + K + V, R, K, V)
+    n = _check(dsp, d, t, x, T, seed=R * 7 + 1)
+    if R >= 48:
+        assert 0 < n.mean() < K  # both outcomes occur
+
+
+def test_bonus_only_block(dsp):
+    """K = 0: nothing to verify, one token drawn from the target."""
+    d, t, x = _inputs(3, 16, 0, 300)
+    n = _check(dsp, d, t, x, 1.0, seed=9)
+    assert np.all(n == 0)
+
+
+def test_greedy(dsp):
+    R, K, V = 6, 5, 500
+    rng = np.random.default_rng(4)
+    t = rng.standard_normal((R, K + 1, V)).astype(np.float32)
+    d = rng.standard_normal((R, K, V)).astype(np.float32)
+    x = np.argmax(t[:, :K], axis=-1).astype(np.int32)
+    for i in range(R):
+        if i < K:
+            x[i, i] = (x[i, i] + 1) % V  # row i rejects at position i; the last row keeps all
+    n, tok = dsp.verify(dev(d), dev(t), dev(x), temperature=0.0)
+    n_or, tok_or = VF.verify(d, t, x, temperature=0.0)
+    np.testing.assert_array_equal(n.cpu().numpy(), n_or)
+    np.testing.assert_array_equal(tok.cpu().numpy(), tok_or)
+    np.testing.assert_array_equal(n_or, [0, 1, 2, 3, 4, 5])
+
+
+def test_serving_shape_sampled_rows(dsp):
+    """128 requests, K = 16, V = 151936; rows 0, 64 and 127 replayed."""
+    R, K, V = 128, 16, 151936
+    g = torch.Generator(device=DEV).manual_seed(77)
+    t = torch.randn((R, K + 1, V), generator=g, device=DEV) * 2
+    d = t[:, :K] + torch.randn((R, K, V), generator=g, device=DEV) * 0.3
+    x = torch.distributions.Categorical(logits=d).sample().to(torch.int32)
+    rows = [0, 64, 127]
+    sel = torch.as_tensor(rows, device=DEV)
+    n, tok = dsp.verify(d, t, x, temperature=1.0, seed=31)
+    dn, tn, xn = d[sel].cpu().numpy(), t[sel].cpu().numpy(), x[sel].cpu().numpy()
+    for j, i in enumerate(rows):
+        n_or, tok_or, ratios, us = VF.verify_row(dn[j], tn[j], xn[j], 1.0, 31, i)
+        if int(n[i]) != n_or:
+            k = min(int(n[i]), n_or)
+            assert abs(us[k] - ratios[k]) <= 1e-4 * max(1.0, ratios[k])
+            continue
+        z = _oracle_z(dn[j], tn[j], n_or, K, V, 1.0, 31, i)
+        assert z[int(tok[i])] >= z.max() - 1e-3
+
+
+def test_bad_draft_token_is_flagged(dsp):
+    d, t, x = _inputs(5, 2, 3, 64)
+    x[1, 0] = 64
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    dsp.verify(dev(d), dev(t), dev(x), status=st)
+    from semi_autoregressive_block_amd import _lib
+    assert int(st.item()) & _lib.STATUS_BAD_TOKEN
