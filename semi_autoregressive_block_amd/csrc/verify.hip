@@ -35,20 +35,23 @@ constexpr int kStat = 8;  // floats per (row, position): m_t, s_t, m_d, s_d, arg
 struct Soft {
   float m, s;
 };
-__device__ __forceinline__ Soft soft_merge(Soft a, Soft b) {
-  const float m = fmaxf(a.m, b.m);
-  if (m == -INFINITY) return {m, 0.f};
-  return {m, a.s * expf(a.m - m) + b.s * expf(b.m - m)};
-}
 
-// Running (max, sum of exp(y - max)) with one exponential per element.
-__device__ __forceinline__ void soft_add(Soft& a, float y) {
+// Running (max, sum of 2^(y - max)) with one exponential per element; the
+// statistics pass works on y = logits * log2(e) / T (base 2: one v_exp_f32
+// per element) and converts the maximum back to natural-log scale at the
+// end (the sum is the same in both bases).
+__device__ __forceinline__ void soft_add2(Soft& a, float y) {
   if (y > a.m) {
-    a.s = a.s * expf(a.m - y) + 1.f;
+    a.s = a.s * exp2f(a.m - y) + 1.f;
     a.m = y;
   } else {
-    a.s += expf(y - a.m);
+    a.s += exp2f(y - a.m);
   }
+}
+__device__ __forceinline__ Soft soft_merge2(Soft a, Soft b) {
+  const float m = fmaxf(a.m, b.m);
+  if (m == -INFINITY) return {m, 0.f};
+  return {m, a.s * exp2f(a.m - m) + b.s * exp2f(b.m - m)};
 }
 
 template <typename T, typename F>
@@ -83,8 +86,11 @@ __global__ __launch_bounds__(kThreads) void verify_stats_kernel(const float* __r
   __shared__ Soft ldss[kThreads / 64];
   const int k = blockIdx.x, row = blockIdx.y;
   const float* t = target + ((int64_t)row * (K + 1) + k) * V;
+  constexpr float kLog2e = 1.4426950408889634f, kLn2 = 0.69314718055994531f;
+  const float sc = invT * kLog2e;
   Soft st{-INFINITY, 0.f};
-  uint64_t best = 0;
+  float bv = -INFINITY;  // this thread's first maximum (indices rise along its scan)
+  uint32_t bi = 0xffffffffu;
   // 16-byte loads when every row starts 16-byte aligned (vec: V % 4 == 0
   // and both bases aligned, decided by the host)
   const int nv = vec ? V / 4 : 0;
@@ -92,31 +98,32 @@ __global__ __launch_bounds__(kThreads) void verify_stats_kernel(const float* __r
     const f32x4 y = *(const f32x4*)(t + 4 * c);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const uint64_t key = argmax_key(y[e], (uint32_t)(4 * c + e));
-      best = key > best ? key : best;
-      if (!greedy) soft_add(st, y[e] * invT);
+      if (y[e] > bv) { bv = y[e]; bi = (uint32_t)(4 * c + e); }
+      if (!greedy) soft_add2(st, y[e] * sc);
     }
   }
   for (int v = 4 * nv + threadIdx.x; v < V; v += kThreads) {
     const float y = t[v];
-    const uint64_t key = argmax_key(y, (uint32_t)v);
-    best = key > best ? key : best;
-    if (!greedy) soft_add(st, y * invT);
+    if (y > bv) { bv = y; bi = (uint32_t)v; }
+    if (!greedy) soft_add2(st, y * sc);
   }
+  uint64_t best = bi == 0xffffffffu ? 0ull : argmax_key(bv, bi);
   best = block_reduce(best, [](uint64_t a, uint64_t b) { return a > b ? a : b; }, lds64);
   float* out = stats + ((int64_t)row * (K + 1) + k) * kStat;
-  if (!greedy) st = block_reduce(st, soft_merge, ldss);
+  if (!greedy) st = block_reduce(st, soft_merge2, ldss);
   Soft sd{-INFINITY, 0.f};
   if (!greedy && k < K) {
     const float* d = draft + ((int64_t)row * K + k) * V;
     for (int c = threadIdx.x; c < nv; c += kThreads) {
       const f32x4 y = *(const f32x4*)(d + 4 * c);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) soft_add(sd, y[e] * invT);
+      for (int e = 0; e < 4; ++e) soft_add2(sd, y[e] * sc);
     }
-    for (int v = 4 * nv + threadIdx.x; v < V; v += kThreads) soft_add(sd, d[v] * invT);
-    sd = block_reduce(sd, soft_merge, ldss);
+    for (int v = 4 * nv + threadIdx.x; v < V; v += kThreads) soft_add2(sd, d[v] * sc);
+    sd = block_reduce(sd, soft_merge2, ldss);
   }
+  st.m *= kLn2;
+  sd.m *= kLn2;
   if (threadIdx.x == 0) {
     out[0] = st.m; out[1] = st.s; out[2] = sd.m; out[3] = sd.s;
     out[4] = __uint_as_float(argmax_key_index(best));
