@@ -121,13 +121,17 @@ def round_inputs(torch, dsp, W, dev):
                             dtype=torch.uint8, device=dev),
         ws_mk=torch.empty(dsp.markov_sample_workspace_bytes(B, G, V, r), dtype=torch.uint8, device=dev),
     )
-    ctx_total = int(st["ctx_offsets"][-1])
-    # algorithmic bytes: every input byte the definition reads once, every output written once
-    attn_bytes = (ctx_total * Hkv * D * 2 * 2          # context K and V
-                  + B * G * Hq * D * 2 * 2            # Q in, out
-                  + B * G * Hkv * D * 2 * 2           # own-block K and V
+    kept = st["keep"][:, 0] != 0
+    ctx_kept = int(st["ctx_lens"][kept].sum())
+    nk = int(kept.sum())
+    # algorithmic bytes: every input byte the definition reads once (a
+    # finished request's block, keep = 0, reads nothing), every output
+    # written once
+    attn_bytes = (ctx_kept * Hkv * D * 2 * 2           # context K and V of kept blocks
+                  + nk * G * Hq * D * 2 + B * G * Hq * D * 2  # Q of kept blocks in, every out row
+                  + nk * G * Hkv * D * 2 * 2          # own-block K and V of kept blocks
                   + (B + 1) * 4 + B * 5)              # offsets, anchors, keep
-    attn_flops = 4.0 * D * G * Hq * float(sum(int(s) + G for s in st["ctx_lens"]))
+    attn_flops = 4.0 * D * G * Hq * float(sum(int(s) + G for s in st["ctx_lens"][kept]))
     step_bytes = r * V * 2 + B * V * 4 + B * r * 2 + B * 8  # W2, base slice, W1 rows, keys
     return inp, bufs, dict(attn_bytes=attn_bytes, attn_flops=attn_flops,
                            markov_step_bytes=step_bytes, markov_steps=G, tokens=B * G)

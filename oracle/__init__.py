@@ -14,7 +14,8 @@ each definition states.  Sources, cited per function:
   sections 3.1–3.13;
 * page 2 — "从 DFlash 到 dLLM Self-Spec（三）" (r00kie-liu.github.io),
   sections 3.4, 3.5, 3.8;
-* page 3 — "DSpark 论文精读", the speculative-decoding primer;
+* page 3 — "如何评价 DeepSeek 发布 DSpark？哪些亮点值得关注？" (foosynaptic.github.io
+  reading notes), the speculative-decoding primer;
 * page 4 — "DSpark 深度解读" (juejin.cn), sections 1.2, 3.2–3.4, 4.1 and 5.1;
 * Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3"
   (SC'11) for the Philox counter-based generator.

@@ -3,7 +3,8 @@ target model — oracle.
 
 Test infrastructure only (see ``oracle/__init__``).
 
-What is computed (page 3, "DSpark 论文精读", the speculative-decoding
+What is computed (page 3, "如何评价 DeepSeek 发布 DSpark？哪些亮点值得关注？",
+the speculative-decoding
 primer: the target checks the K drafted positions in one pass, accepts from
 left to right the prefix that agrees with its distribution P by rejection
 sampling, cuts at the first failure and draws that position again from the

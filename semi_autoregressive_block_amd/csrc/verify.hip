@@ -1,5 +1,6 @@
 // Lossless verify step: rejection sampling of a drafted block against the
-// target model (page 3, "DSpark 论文精读", the speculative-decoding primer;
+// target model (page 3, "如何评价 DeepSeek 发布 DSpark？哪些亮点值得关注？", the
+// speculative-decoding primer;
 // page 4, "DSpark 深度解读", §1.2).  The pages give the outline (accept the
 // prefix consistent with P from left to right, cut at the first failure
 // and draw that position again from the target, output distribution
@@ -39,7 +40,10 @@ struct Soft {
 // Running (max, sum of 2^(y - max)) with one exponential per element; the
 // statistics pass works on y = logits * log2(e) / T (base 2: one v_exp_f32
 // per element) and converts the maximum back to natural-log scale at the
-// end (the sum is the same in both bases).
+// end (the sum is the same in both bases).  The running maximum starts at
+// -FLT_MAX, not -inf, so a masked logit (-inf) adds 2^-inf = 0 even before
+// the first finite one (-inf - -inf would be NaN), at no extra instruction.
+constexpr float kSoftInit = -3.402823466e38f;
 __device__ __forceinline__ void soft_add2(Soft& a, float y) {
   if (y > a.m) {
     a.s = a.s * exp2f(a.m - y) + 1.f;
@@ -88,7 +92,7 @@ __global__ __launch_bounds__(kThreads) void verify_stats_kernel(const float* __r
   const float* t = target + ((int64_t)row * (K + 1) + k) * V;
   constexpr float kLog2e = 1.4426950408889634f, kLn2 = 0.69314718055994531f;
   const float sc = invT * kLog2e;
-  Soft st{-INFINITY, 0.f};
+  Soft st{kSoftInit, 0.f};
   float bv = -INFINITY;  // this thread's first maximum (indices rise along its scan)
   uint32_t bi = 0xffffffffu;
   // 16-byte loads when every row starts 16-byte aligned (vec: V % 4 == 0
@@ -111,7 +115,7 @@ __global__ __launch_bounds__(kThreads) void verify_stats_kernel(const float* __r
   best = block_reduce(best, [](uint64_t a, uint64_t b) { return a > b ? a : b; }, lds64);
   float* out = stats + ((int64_t)row * (K + 1) + k) * kStat;
   if (!greedy) st = block_reduce(st, soft_merge2, ldss);
-  Soft sd{-INFINITY, 0.f};
+  Soft sd{kSoftInit, 0.f};
   if (!greedy && k < K) {
     const float* d = draft + ((int64_t)row * K + k) * V;
     for (int c = threadIdx.x; c < nv; c += kThreads) {

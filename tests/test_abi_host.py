@@ -202,8 +202,9 @@ def test_head_workspaces_and_bad_arguments(lib):
     assert call(wdtype=5) == mod.ERR_INVALID_ARG
     assert call(gamma=1025) == mod.ERR_INVALID_ARG
     assert call() == mod.ERR_INVALID_ARG              # null pointers
+    assert b"null required pointer" in L.dspark_last_error()
     assert call(R=0) == mod.OK                        # empty batch: nothing to do
-    assert b"null" in L.dspark_last_error() or True
+    assert L.dspark_last_error() == b""
     rc = L.dspark_markov_head_block_logits(mod.HEAD_GATED, null, null, null, null, null, null, null, null, 2, 4,
                                            100, 16, 32, 1, -1.0, null, 0, null, null)
     assert rc == mod.ERR_INVALID_ARG                  # negative soft cap

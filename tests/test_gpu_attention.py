@@ -139,6 +139,35 @@ def test_bad_anchor_and_offsets_are_clamped_and_flagged(dsp):
     assert int(st.item()) & 4
 
 
+def _offset_view(a, dtype, shift):
+    """The same values in a contiguous view whose data pointer sits `shift`
+    elements past an allocation boundary (bf16: 2 bytes per element), so it
+    is not 16-byte aligned."""
+    t = as_dtype(a, dtype)
+    buf = torch.empty(t.numel() + shift, dtype=t.dtype, device=DEV)
+    v = buf[shift:].view(t.shape)
+    v.copy_(t)
+    return v
+
+
+@pytest.mark.parametrize("which", ["all", "out", "k_ctx"])
+def test_bf16_unaligned_views(dsp, which):
+    """bf16 tensors that are not 16-byte aligned (e.g. views that start one
+    element into an allocation) take the vector-ALU kernel; it must agree
+    with the oracle like the matrix-core kernel."""
+    c = W.attention_case(71, [700, 130], 3, 8, 8, 2, 128, "bf16")
+    c.keep[1, 2] = 0
+    names = ["q", "k_ctx", "v_ctx", "k_blk", "v_blk"]
+    shift = {n: (1 if which in ("all", n) else 0) for n in names + ["out"]}
+    ts = {n: _offset_view(getattr(c, n), "bf16", shift[n]) for n in names}
+    assert which != "all" or all(ts[n].data_ptr() % 16 for n in names)
+    out = _offset_view(np.zeros(c.q.shape, np.uint16), "bf16", shift["out"])
+    o, lse = dsp.block_attention(ts["q"], ts["k_ctx"], ts["v_ctx"], dev(c.ctx_offsets), ts["k_blk"],
+                                 ts["v_blk"], dev(c.anchor), dev(c.keep), max_ctx=700, out=out, want_lse=True)
+    assert o.data_ptr() == out.data_ptr()
+    _compare((o.float().cpu().numpy(), lse.cpu().numpy()), _ref(c), TOL["bf16"])
+
+
 def test_deterministic(dsp):
     c = W.attention_case(61, [3000, 5000], 2, 16, 32, 8, 128, "bf16")
     args = (as_dtype(c.q, "bf16"), as_dtype(c.k_ctx, "bf16"), as_dtype(c.v_ctx, "bf16"),
@@ -189,7 +218,13 @@ def test_config2_full_size_sampled(dsp):
 
 
 def test_config5_full_size_sampled(dsp):
+    """384 of the 4096 (request, head) outputs: every query head of the 8
+    requests with the longest contexts (all their workgroups) and one random
+    head of every request, in the launch configuration the bench times."""
     inp = W.config5_device(torch, DEV)
+    lens = np.diff(inp["ctx_offsets"].cpu().numpy())
+    longest = np.argsort(lens, kind="stable")[-8:]
     rng = np.random.default_rng(8)
-    picks = [(int(b), 0, int(h)) for b, h in zip(rng.integers(0, 128, 16), rng.integers(0, 32, 16))]
+    picks = [(int(b), 0, h) for b in longest for h in range(32)]
+    picks += [(b, 0, int(h)) for b, h in zip(range(128), rng.integers(0, 32, 128))]
     _sampled(dsp, inp, picks, 16)

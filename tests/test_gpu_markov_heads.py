@@ -120,7 +120,8 @@ def test_sampler_against_teacher_forced_oracle(dsp, kind, temperature):
 
 def test_sampler_serving_shape_sampled_rows(dsp):
     """R = 128 requests, gamma = 16, V = 151936, r = 256, d = 4096 with the
-    recurrent head; rows 0, 77 and 127 replayed by the oracle."""
+    recurrent head; 17 rows (every eighth and the last) replayed by the
+    oracle, tokens and step logits."""
     R, G, V, r, d = 128, 16, 151936, 256, 4096
     rng = np.random.default_rng(21)
     base = torch.randn((R, G, V), generator=torch.Generator().manual_seed(5)).mul_(3).to(DEV)
@@ -130,14 +131,18 @@ def test_sampler_serving_shape_sampled_rows(dsp):
     fan = 2 * r + d
     whead = W.to_bf16_bits((rng.standard_normal((3, r, fan)) * 1.5 / np.sqrt(fan)).astype(np.float32))
     first = rng.integers(0, V, size=R).astype(np.int32)
-    tok, _ = dsp.markov_head_sample("rnn", base, as_dtype(hid, "bf16"), as_dtype(w1, "bf16"), as_dtype(w2, "bf16"),
-                                    as_dtype(whead, "bf16"), dev(first))
+    tok, sl = dsp.markov_head_sample("rnn", base, as_dtype(hid, "bf16"), as_dtype(w1, "bf16"), as_dtype(w2, "bf16"),
+                                     as_dtype(whead, "bf16"), dev(first), want_step_logits=True)
     tok = tok.cpu().numpy().astype(np.int64)
-    rows = np.array([0, 77, 127])
-    b = base[torch.as_tensor(rows, device=DEV)].cpu().numpy()
-    _, z, _ = OH.sample_block_tokens("rnn", b, W.values(hid[rows], "bf16"), W.values(w1, "bf16"),
-                                     W.values(w2, "bf16"), W.values(whead, "bf16"), first[rows], teacher=tok[rows],
-                                     rows=rows)
+    rows = np.array(list(range(0, R, 8)) + [R - 1])
+    sel = torch.as_tensor(rows, device=DEV)
+    b = base[sel].cpu().numpy()
+    got = sl[sel].cpu().numpy()
+    del sl
+    _, z, l = OH.sample_block_tokens("rnn", b, W.values(hid[rows], "bf16"), W.values(w1, "bf16"),
+                                     W.values(w2, "bf16").astype(np.float64), W.values(whead, "bf16"), first[rows],
+                                     teacher=tok[rows], rows=rows)
+    _check_logits(got, l, "bf16", b)
     _check_tokens(tok[rows], z, 2 * _bar("bf16"))
 
 

@@ -42,6 +42,11 @@ def _markov_inputs(seed, N, V, r, wdtype, wscale=0.05):
 
 
 def _check_tokens(tok, ref_logits):
+    """Rows with a clear winner (top-2 margin above 1e-3) must pick it; the
+    others must pick a logit within 1e-3 of the row's maximum."""
+    best = ref_logits.max(axis=-1)
+    chosen = ref_logits[np.arange(len(tok)), tok]
+    assert np.all(chosen >= best - 1e-3), np.max(best - chosen)
     top2 = np.sort(ref_logits, axis=-1)[:, -2:]
     sure = top2[:, 1] - top2[:, 0] > 1e-3
     np.testing.assert_array_equal(tok[sure], np.argmax(ref_logits, axis=-1)[sure])

@@ -95,25 +95,111 @@ def test_greedy(dsp):
     np.testing.assert_array_equal(n_or, [0, 1, 2, 3, 4, 5])
 
 
-def test_serving_shape_sampled_rows(dsp):
-    """128 requests, K = 16, V = 151936; rows 0, 64 and 127 replayed."""
+def test_serving_shape_all_rows(dsp):
+    """128 requests, K = 16, V = 151936: the kept count of every row, the
+    extra token of 32 rows (the first, the last and every fourth)."""
     R, K, V = 128, 16, 151936
     g = torch.Generator(device=DEV).manual_seed(77)
     t = torch.randn((R, K + 1, V), generator=g, device=DEV) * 2
     d = t[:, :K] + torch.randn((R, K, V), generator=g, device=DEV) * 0.3
     x = torch.distributions.Categorical(logits=d).sample().to(torch.int32)
-    rows = [0, 64, 127]
-    sel = torch.as_tensor(rows, device=DEV)
     n, tok = dsp.verify(d, t, x, temperature=1.0, seed=31)
-    dn, tn, xn = d[sel].cpu().numpy(), t[sel].cpu().numpy(), x[sel].cpu().numpy()
-    for j, i in enumerate(rows):
-        n_or, tok_or, ratios, us = VF.verify_row(dn[j], tn[j], xn[j], 1.0, 31, i)
+    n, tok = n.cpu().numpy(), tok.cpu().numpy()
+    dn, tn, xn = d.cpu().numpy(), t.cpu().numpy(), x.cpu().numpy()
+    token_rows = set(range(0, R, 4)) | {R - 1}
+    same = checked = 0
+    for i in range(R):
+        n_or, tok_or, ratios, us = VF.verify_row(dn[i], tn[i], xn[i], 1.0, 31, i)
         if int(n[i]) != n_or:
             k = min(int(n[i]), n_or)
-            assert abs(us[k] - ratios[k]) <= 1e-4 * max(1.0, ratios[k])
+            assert abs(us[k] - ratios[k]) <= 1e-4 * max(1.0, ratios[k]), (i, int(n[i]), n_or)
             continue
-        z = _oracle_z(dn[j], tn[j], n_or, K, V, 1.0, 31, i)
-        assert z[int(tok[i])] >= z.max() - 1e-3
+        same += 1
+        if i in token_rows:
+            checked += 1
+            z = _oracle_z(dn[i], tn[i], n_or, K, V, 1.0, 31, i)
+            assert z[int(tok[i])] >= z.max() - 1e-3, (i, int(tok[i]), tok_or)
+            top2 = np.sort(z)[-2:]
+            if top2[1] - top2[0] > 1e-3:
+                assert int(tok[i]) == tok_or, (i, int(tok[i]), tok_or)
+    assert same >= R - 2 and checked >= 30
+    assert 0 < n.mean() < K
+
+
+def _masked_inputs(seed, R, K, V, strip_threads=(0, 5), frac=0.3):
+    """Target and draft logits with -inf entries: index 0 of every row, the
+    whole strip of vocabulary entries that thread c of a 256-thread
+    workgroup reads with 16-byte loads (4 (c + 256 j) + e), and a random
+    fraction; the drafted tokens are drawn from the draft's own softmax, so
+    they never sit on a -inf draft logit but do sit on -inf target logits."""
+    rng = np.random.default_rng(seed)
+    t = (rng.standard_normal((R, K + 1, V)) * 2).astype(np.float32)
+    d = (t[:, :K] + rng.standard_normal((R, K, V)) * 0.7).astype(np.float32)
+    strip = np.zeros(V, dtype=bool)
+    for c in strip_threads:
+        for j in range(0, V // 4, 256):
+            q = j + c
+            if 4 * q < V:
+                strip[4 * q:4 * q + 4] = True
+    strip[0] = True
+    mt = (rng.random((R, K + 1, V)) < frac) | strip
+    md = (rng.random((R, K, V)) < frac) | strip
+    t[mt] = -np.inf
+    d[md] = -np.inf
+    q = VF.softmax(d)
+    x = np.array([[rng.choice(V, p=q[i, k]) for k in range(K)] for i in range(R)], dtype=np.int32).reshape(R, K)
+    return d, t, x
+
+
+@pytest.mark.parametrize("V", [4096, 4099])
+def test_masked_logits_sampled(dsp, V):
+    """-inf target and draft logits (masked vocabulary entries) at T = 1 and
+    T = 0.8: kept counts and extra tokens match the oracle, no row comes
+    out as the all-rejected token 0."""
+    R, K = 40, 6
+    d, t, x = _masked_inputs(V, R, K, V)
+    for T, seed in ((1.0, 3), (0.8, 4)):
+        n = _check(dsp, d, t, x, T, seed=seed)
+        assert 0 < n.mean() < K
+        _, tok = dsp.verify(dev(d), dev(t), dev(x), temperature=T, seed=seed)
+        tok = tok.cpu().numpy()
+        for i in range(R):  # the extra token never lands on a masked target entry
+            assert np.isfinite(t[i, n[i], tok[i]]), (i, n[i], tok[i])
+
+
+def test_masked_logits_greedy(dsp):
+    """Greedy verification with -inf target logits: exact."""
+    R, K, V = 12, 5, 4096
+    d, t, x = _masked_inputs(11, R, K, V)
+    am = np.argmax(t[:, :K], axis=-1).astype(np.int32)
+    x = am.copy()
+    for i in range(min(R, K)):
+        x[i, i] = (x[i, i] + 1) % V
+    n, tok = dsp.verify(dev(d), dev(t), dev(x), temperature=0.0)
+    n_or, tok_or = VF.verify(d, t, x, temperature=0.0)
+    np.testing.assert_array_equal(n.cpu().numpy(), n_or)
+    np.testing.assert_array_equal(tok.cpu().numpy(), tok_or)
+
+
+def test_greedy_ties(dsp):
+    """Greedy with tied target maxima: the lowest tied index is the target's
+    choice, so a draft on the higher tied index is rejected and the extra
+    token is the lower one."""
+    R, K, V = 6, 3, 1000
+    rng = np.random.default_rng(12)
+    t = rng.standard_normal((R, K + 1, V)).astype(np.float32)
+    d = rng.standard_normal((R, K, V)).astype(np.float32)
+    lo, hi = 17, 801
+    t[:, :, lo] = t[:, :, hi] = 9.0
+    x = np.full((R, K), lo, dtype=np.int32)
+    x[1, 0] = hi
+    x[2, 2] = hi
+    n, tok = dsp.verify(dev(d), dev(t), dev(x), temperature=0.0)
+    n_or, tok_or = VF.verify(d, t, x, temperature=0.0)
+    np.testing.assert_array_equal(n.cpu().numpy(), n_or)
+    np.testing.assert_array_equal(tok.cpu().numpy(), tok_or)
+    np.testing.assert_array_equal(n_or, [K, 0, 2, K, K, K])
+    assert np.all(tok_or == lo)
 
 
 def test_bad_draft_token_is_flagged(dsp):

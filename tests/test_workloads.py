@@ -34,6 +34,7 @@ def test_structures_have_the_stated_shapes():
     assert np.array_equal(s["anchor"][:, 0], s["ctx_lens"])
     trunc = (s["mask"].seq_lens - s["ctx_lens"] - 1) < 16
     assert 0.1 < trunc.mean() < 0.45
+    assert (s["keep"] == 0).sum() == 6 and s["keep"].shape == (128, 1)  # about 5 % finished requests
 
 
 def test_config1_shapes():

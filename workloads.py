@@ -223,7 +223,7 @@ CONFIG2 = dict(B=1, S=4096, A=512, n_real=472, gamma=8, Hq=32, Hkv=8, D=128)
 CONFIG3 = dict(R=64, gamma=16, V=151936, r=256, temperature=1.0)
 CONFIG4 = dict(B=4, A=512, n_real=472, gamma=8, V=151936, S=4096)
 CONFIG5 = dict(B=128, S_lo=1024, S_hi=8192, gamma=16, Hq=32, Hkv=8, D=128,
-               V=151936, r=256, n_hi=63)
+               V=151936, r=256, n_hi=63, n_finished=6)
 
 
 def config2_structure():
@@ -261,10 +261,12 @@ def config4_structure():
 def config5_structure():
     """Serving round structure: 128 requests with context lengths
     S_b ~ U{1024..8192}; one block per request anchored at the end of its
-    context (anchor = S_b: the block sees the whole context); every block
-    kept; remaining generation budget n_b ~ U{0..63} so seq_lens_b =
-    S_b + 1 + n_b and about a quarter of the blocks are truncated by the
-    eval mask; first previous tokens uniform in [0, V)."""
+    context (anchor = S_b: the block sees the whole context); 6 of the 128
+    requests (about 5 %, drawn without replacement from their own seeded
+    stream) are finished and get keep = 0, the rest are kept; remaining
+    generation budget n_b ~ U{0..63} so seq_lens_b = S_b + 1 + n_b and
+    about a quarter of the blocks are truncated by the eval mask; first
+    previous tokens uniform in [0, V)."""
     c = CONFIG5
     rng = np.random.default_rng(SEED_BASE + 5)
     B = c["B"]
@@ -273,6 +275,8 @@ def config5_structure():
     offsets[1:] = np.cumsum(S)
     anchor = S.astype(np.int32)[:, None]
     keep = np.ones((B, 1), dtype=np.uint8)
+    fin = np.random.default_rng(SEED_BASE + 55).choice(B, size=c["n_finished"], replace=False)
+    keep[fin, 0] = 0
     n = rng.integers(0, c["n_hi"] + 1, size=B)
     seq_lens = (S + 1 + n).astype(np.int32)
     first_prev = rng.integers(0, c["V"], size=B, dtype=np.int32)
