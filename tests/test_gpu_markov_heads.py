@@ -121,7 +121,15 @@ def test_sampler_against_teacher_forced_oracle(dsp, kind, temperature):
 def test_sampler_serving_shape_sampled_rows(dsp):
     """R = 128 requests, gamma = 16, V = 151936, r = 256, d = 4096 with the
     recurrent head; 17 rows (every eighth and the last) replayed by the
-    oracle, tokens and step logits."""
+    oracle, tokens and step logits.
+
+    At this size the bias is large (RMS about 3), so the fixed 2e-2 bar is
+    replaced by the bound the arithmetic gives: E is rounded to bf16 (each
+    entry moves by at most 2^-9 of itself) before the float32 product, so
+    |l - l_oracle| <= 2^-9 sum_j |E_j W2[j, v]| plus float32 slack (1e-3
+    covers the 256-term sums and the base add).  A token differs from the
+    oracle's argmax only where the two logits are within the sum of their
+    bounds."""
     R, G, V, r, d = 128, 16, 151936, 256, 4096
     rng = np.random.default_rng(21)
     base = torch.randn((R, G, V), generator=torch.Generator().manual_seed(5)).mul_(3).to(DEV)
@@ -139,11 +147,29 @@ def test_sampler_serving_shape_sampled_rows(dsp):
     b = base[sel].cpu().numpy()
     got = sl[sel].cpu().numpy()
     del sl
-    _, z, l = OH.sample_block_tokens("rnn", b, W.values(hid[rows], "bf16"), W.values(w1, "bf16"),
-                                     W.values(w2, "bf16").astype(np.float64), W.values(whead, "bf16"), first[rows],
-                                     teacher=tok[rows], rows=rows)
-    _check_logits(got, l, "bf16", b)
-    _check_tokens(tok[rows], z, 2 * _bar("bf16"))
+    w1v, w2v, hv, whv = (W.values(w1, "bf16"), W.values(w2, "bf16").astype(np.float64),
+                         W.values(hid[rows], "bf16"), W.values(whead, "bf16"))
+    _, z, l = OH.sample_block_tokens("rnn", b, hv, w1v, w2v, whv, first[rows], teacher=tok[rows], rows=rows)
+    # the oracle's E along the device's token path, for the rounding bound
+    s_ = np.zeros((len(rows), r))
+    prev = first[rows].astype(np.int64)
+    aw2 = np.abs(w2v)
+    mism = 0
+    for k in range(G):
+        s_, e = OH.rnn_cell(s_, w1v[prev], hv[:, k], whv)
+        bound = 2.0 ** -9 * (np.abs(e) @ aw2) + 1e-3
+        err = np.abs(got[:, k] - l[:, k])
+        assert np.all(err <= bound), (k, float(err.max()), float((err - bound).max()))
+        for j in range(len(rows)):
+            a, t = int(np.argmax(z[j, k])), int(tok[rows[j], k])
+            if a != t:
+                mism += 1
+                assert z[j, k, a] - z[j, k, t] <= bound[j, a] + bound[j, t], (rows[j], k, a, t)
+        prev = tok[rows, k]
+    res = got - l
+    bias = l - b
+    assert np.sqrt(np.mean(res ** 2)) < 2.0 ** -8 * np.sqrt(np.mean(bias ** 2))
+    assert mism <= 0.05 * len(rows) * G, mism
 
 
 def test_bad_previous_token_is_clamped_and_flagged(dsp):
