@@ -160,6 +160,31 @@ int dspark_markov_sample(const float* base_logits, const void* w1, const void* w
                          void* ws, size_t ws_bytes, int32_t* dev_status, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Allocation-free Markov sampler, for callers that cannot allocate device
+ * memory or pass a workspace (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  Same arguments, semantics and
+ * results as dspark_markov_sample, without (ws, ws_bytes): its per-step
+ * argmax keys live in a fixed device array of DSPARK_NOALLOC_SCRATCH_BYTES
+ * inside the library (one per GPU the library runs on, held until the
+ * process ends, cleared at the start of every call).  It calls no
+ * allocator.
+ *   - Sizes whose dspark_markov_sample_workspace_bytes(R, gamma, V, r,
+ *     wdtype) exceeds DSPARK_NOALLOC_SCRATCH_BYTES return
+ *     DSPARK_ERR_WORKSPACE (e.g. R = 128 rows allow gamma <= 64).
+ *   - All calls on one GPU share that array: two calls whose executions
+ *     overlap on one GPU (different streams, or host threads without
+ *     ordering) race and give undefined tokens.  Serialise them.
+ *   - DSPARK_ERR_HIP if the array's device address cannot be looked up on
+ *     the current device (done once per device, on its first call).
+ * ---------------------------------------------------------------------- */
+#define DSPARK_NOALLOC_SCRATCH_BYTES ((size_t)4 << 20)
+int dspark_markov_sample_noalloc(const float* base_logits, const void* w1, const void* w2,
+                                 const int32_t* first_prev, int32_t* tokens, float* step_logits,
+                                 int R, int gamma, int V, int r, int wdtype,
+                                 float temperature, uint64_t seed,
+                                 int32_t* dev_status, void* stream);
+
+/* ------------------------------------------------------------------------
  * TV-distance accept rate (page 1 §3.9, the paper's Eq. 8; page 2 §3.5 and
  * §3.8.3) and the tau statistic (page 1 §3.10).  Per row of V logits:
  *

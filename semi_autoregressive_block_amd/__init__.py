@@ -10,6 +10,7 @@ Functions (same names and argument meaning as the C entry points):
 
 * ``block_attention``  — block-masked dual-source attention
 * ``markov_sample``    — Markov-head gamma-step sampler
+* ``markov_sample_noalloc`` — the same through the allocation-free entry point
 * ``accept_rate``      — TV accept rate (+ tau)
 * ``eval_mask``        — cumulative-product eval mask
 * ``markov_block_logits`` — teacher-forced Markov logits of a whole block
@@ -27,7 +28,7 @@ from . import _lib
 
 _LIB = _lib.load()
 
-__all__ = ["block_attention", "markov_sample", "accept_rate", "eval_mask",
+__all__ = ["block_attention", "markov_sample", "markov_sample_noalloc", "accept_rate", "eval_mask",
            "block_attention_workspace_bytes", "markov_sample_workspace_bytes",
            "accept_rate_workspace_bytes", "markov_block_logits", "markov_block_logits_workspace_bytes",
            "l1_loss", "l1_loss_workspace_bytes", "confidence_schedule", "set_wait_limit", "last_error", "version",
@@ -147,11 +148,7 @@ def markov_sample_workspace_bytes(R, gamma, V, r, wdtype=_lib.BF16) -> int:
     return int(_LIB.dspark_markov_sample_workspace_bytes(R, gamma, V, r, wdtype))
 
 
-def markov_sample(base, w1, w2, first_prev, *, temperature=0.0, seed=0, tokens=None,
-                  step_logits=None, want_step_logits=False, status=None, workspace=None):
-    """base [R, gamma, V] float32; w1 [V, r]; w2 [r, V] (same dtype, bf16 or
-    float32); first_prev [R] int32.  Returns (tokens [R, gamma] int32,
-    step_logits [R, gamma, V] float32 or None)."""
+def _markov_sample_args(base, w1, w2, first_prev, tokens, step_logits, want_step_logits, status):
     dev = base.device
     _check(base, "base", torch.float32, ndim=3)
     R, gamma, V = base.shape
@@ -172,7 +169,16 @@ def markov_sample(base, w1, w2, first_prev, *, temperature=0.0, seed=0, tokens=N
         _check(step_logits, "step_logits", torch.float32, dev, 3)
     if status is not None:
         _check(status, "status", torch.int32, dev)
-    wdt = _dt(w1)
+    return dev, R, gamma, V, r, _dt(w1), tokens, step_logits
+
+
+def markov_sample(base, w1, w2, first_prev, *, temperature=0.0, seed=0, tokens=None,
+                  step_logits=None, want_step_logits=False, status=None, workspace=None):
+    """base [R, gamma, V] float32; w1 [V, r]; w2 [r, V] (same dtype, bf16 or
+    float32); first_prev [R] int32.  Returns (tokens [R, gamma] int32,
+    step_logits [R, gamma, V] float32 or None)."""
+    dev, R, gamma, V, r, wdt, tokens, step_logits = _markov_sample_args(
+        base, w1, w2, first_prev, tokens, step_logits, want_step_logits, status)
     nbytes = markov_sample_workspace_bytes(R, gamma, V, r, wdt)
     ws, wsb = _workspace(nbytes, dev, workspace)
     rc = _LIB.dspark_markov_sample(
@@ -181,6 +187,22 @@ def markov_sample(base, w1, w2, first_prev, *, temperature=0.0, seed=0, tokens=N
         _ptr(status), _stream(dev))
     if rc != 0:
         raise DSparkError(rc, "markov_sample")
+    return tokens, step_logits
+
+
+def markov_sample_noalloc(base, w1, w2, first_prev, *, temperature=0.0, seed=0, tokens=None,
+                          step_logits=None, want_step_logits=False, status=None):
+    """markov_sample through the library's allocation-free entry point: no
+    workspace (the per-step keys live in the library's fixed device array,
+    shared by every call on the GPU: calls must not overlap).  Pass `tokens`
+    (and `step_logits`) to keep this wrapper from allocating them."""
+    dev, R, gamma, V, r, wdt, tokens, step_logits = _markov_sample_args(
+        base, w1, w2, first_prev, tokens, step_logits, want_step_logits, status)
+    rc = _LIB.dspark_markov_sample_noalloc(
+        _ptr(base), _ptr(w1), _ptr(w2), _ptr(first_prev), _ptr(tokens), _ptr(step_logits),
+        R, gamma, V, r, wdt, float(temperature), int(seed) & (2**64 - 1), _ptr(status), _stream(dev))
+    if rc != 0:
+        raise DSparkError(rc, "markov_sample_noalloc")
     return tokens, step_logits
 
 

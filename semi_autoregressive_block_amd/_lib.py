@@ -23,6 +23,7 @@ STATUS_BAD_TOKEN = 2
 STATUS_BAD_OFFSETS = 4
 STATUS_BAD_LABEL = 8
 STATUS_WAIT_TIMEOUT = 16
+NOALLOC_SCRATCH_BYTES = 4 << 20  # DSPARK_NOALLOC_SCRATCH_BYTES
 
 _p = ctypes.c_void_p
 _i = ctypes.c_int
@@ -40,6 +41,7 @@ SIGNATURES = {
     "dspark_markov_sample_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
     "dspark_markov_sample": (_i, [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _u64,
                                   _p, _sz, _p, _p]),
+    "dspark_markov_sample_noalloc": (_i, [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _u64, _p, _p]),
     "dspark_accept_rate_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
     "dspark_accept_rate": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _p, _sz, _p, _p]),
     "dspark_set_wait_limit": (None, [ctypes.c_uint32]),

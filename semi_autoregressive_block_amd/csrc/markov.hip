@@ -536,29 +536,36 @@ extern "C" size_t dspark_markov_sample_workspace_bytes(int R, int gamma, int V, 
   return (size_t)gamma * keys_per_step(R) * sizeof(uint64_t);
 }
 
-extern "C" int dspark_markov_sample(const float* base_logits, const void* w1, const void* w2,
-                                   const int32_t* first_prev, int32_t* tokens, float* step_logits,
-                                   int R, int gamma, int V, int r, int wdtype, float temperature,
-                                   uint64_t seed, void* ws, size_t ws_bytes, int32_t* dev_status,
-                                   void* stream) {
+namespace {
+
+// Host-side checks shared by both sampler entry points; 0 = go on, 1 = done
+// (nothing to do), else the status to return.
+int markov_sample_check(const char* who, const float* base_logits, const void* w1, const void* w2,
+                        const int32_t* first_prev, const int32_t* tokens, int R, int gamma, int V, int r,
+                        int wdtype, float temperature) {
   using namespace dspark_host;
-  if (R < 0 || gamma < 0) return fail(DSPARK_ERR_INVALID_ARG, "markov_sample: negative dimension");
+  if (R < 0 || gamma < 0) return fail(DSPARK_ERR_INVALID_ARG, "%s: negative dimension", who);
   if (V < 1 || r < 1 || r > 1024)
-    return fail(DSPARK_ERR_INVALID_ARG, "markov_sample: need V >= 1 and 1 <= r <= 1024 (V=%d r=%d)", V, r);
-  if (gamma > 1024) return fail(DSPARK_ERR_INVALID_ARG, "markov_sample: gamma > 1024");
+    return fail(DSPARK_ERR_INVALID_ARG, "%s: need V >= 1 and 1 <= r <= 1024 (V=%d r=%d)", who, V, r);
+  if (gamma > 1024) return fail(DSPARK_ERR_INVALID_ARG, "%s: gamma > 1024", who);
   if (wdtype != DSPARK_BF16 && wdtype != DSPARK_F32)
-    return fail(DSPARK_ERR_INVALID_ARG, "markov_sample: unknown wdtype %d", wdtype);
+    return fail(DSPARK_ERR_INVALID_ARG, "%s: unknown wdtype %d", who, wdtype);
   if (!(temperature >= 0.f) || temperature == INFINITY)
-    return fail(DSPARK_ERR_INVALID_ARG, "markov_sample: temperature must be finite and >= 0");
-  if ((int64_t)R * gamma == 0) return ok();
+    return fail(DSPARK_ERR_INVALID_ARG, "%s: temperature must be finite and >= 0", who);
+  if ((int64_t)R * gamma == 0) {
+    ok();
+    return 1;
+  }
   if (!base_logits || !w1 || !w2 || !first_prev || !tokens)
-    return fail(DSPARK_ERR_INVALID_ARG, "markov_sample: null required pointer");
-  const size_t need = dspark_markov_sample_workspace_bytes(R, gamma, V, r, wdtype);
-  if (ws_bytes < need || !ws)
-    return fail(DSPARK_ERR_WORKSPACE, "markov_sample: workspace %zu bytes < %zu", ws_bytes, need);
-  if ((uintptr_t)ws % 8) return fail(DSPARK_ERR_INVALID_ARG, "markov_sample: workspace not 8-byte aligned");
-  hipStream_t s = (hipStream_t)stream;
-  uint64_t* keys = (uint64_t*)ws;  // [gamma][kKeyReplicas][replica_stride(R)]
+    return fail(DSPARK_ERR_INVALID_ARG, "%s: null required pointer", who);
+  return 0;
+}
+
+// The sampler proper over a key buffer of dspark_markov_sample_workspace_bytes.
+int markov_sample_run(const float* base_logits, const void* w1, const void* w2, const int32_t* first_prev,
+                      int32_t* tokens, float* step_logits, int R, int gamma, int V, int r, int wdtype,
+                      float temperature, uint64_t seed, uint64_t* keys, int32_t* dev_status, hipStream_t s) {
+  using namespace dspark_host;
   const int64_t nk = (int64_t)gamma * keys_per_step(R);
   hipLaunchKernelGGL(zero_u64_kernel, dim3((unsigned)((nk + 255) / 256)), dim3(256), 0, s, keys, nk);
   const int greedy = temperature == 0.f;
@@ -583,6 +590,73 @@ extern "C" int dspark_markov_sample(const float* base_logits, const void* w1, co
   hipLaunchKernelGGL(finalize_tokens_kernel, dim3((unsigned)((ntok + 255) / 256)), dim3(256), 0, s, keys,
                      tokens, R, gamma, V, dev_status);
   return check_launch("markov_sample");
+}
+
+}  // namespace
+
+extern "C" int dspark_markov_sample(const float* base_logits, const void* w1, const void* w2,
+                                   const int32_t* first_prev, int32_t* tokens, float* step_logits,
+                                   int R, int gamma, int V, int r, int wdtype, float temperature,
+                                   uint64_t seed, void* ws, size_t ws_bytes, int32_t* dev_status,
+                                   void* stream) {
+  using namespace dspark_host;
+  const int c = markov_sample_check("markov_sample", base_logits, w1, w2, first_prev, tokens, R, gamma, V, r,
+                                    wdtype, temperature);
+  if (c != 0) return c == 1 ? DSPARK_OK : c;
+  const size_t need = dspark_markov_sample_workspace_bytes(R, gamma, V, r, wdtype);
+  if (ws_bytes < need || !ws)
+    return fail(DSPARK_ERR_WORKSPACE, "markov_sample: workspace %zu bytes < %zu", ws_bytes, need);
+  if ((uintptr_t)ws % 8) return fail(DSPARK_ERR_INVALID_ARG, "markov_sample: workspace not 8-byte aligned");
+  return markov_sample_run(base_logits, w1, w2, first_prev, tokens, step_logits, R, gamma, V, r, wdtype,
+                           temperature, seed, (uint64_t*)ws, dev_status, (hipStream_t)stream);
+}
+
+// Allocation-free variant: the key buffer is a fixed array in device memory
+// (one copy per device, alive until the process ends).  In host code the
+// array's name only stands in for it; its device address is looked up once
+// per device and only that address is passed to kernels.
+static __device__ __align__(256) uint64_t scratch[DSPARK_NOALLOC_SCRATCH_BYTES / sizeof(uint64_t)];
+
+namespace {
+
+uint64_t* noalloc_scratch(int* err_dev) {
+  static std::atomic<void*> addr[64];  // per device, null = not looked up yet
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    *err_dev = dev;
+    return nullptr;
+  }
+  void* p = addr[dev].load(std::memory_order_acquire);
+  if (p) return (uint64_t*)p;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+    *err_dev = dev;
+    return nullptr;
+  }
+  addr[dev].store(p, std::memory_order_release);
+  return (uint64_t*)p;
+}
+
+}  // namespace
+
+extern "C" int dspark_markov_sample_noalloc(const float* base_logits, const void* w1, const void* w2,
+                                           const int32_t* first_prev, int32_t* tokens, float* step_logits,
+                                           int R, int gamma, int V, int r, int wdtype, float temperature,
+                                           uint64_t seed, int32_t* dev_status, void* stream) {
+  using namespace dspark_host;
+  const int c = markov_sample_check("markov_sample_noalloc", base_logits, w1, w2, first_prev, tokens, R, gamma,
+                                    V, r, wdtype, temperature);
+  if (c != 0) return c == 1 ? DSPARK_OK : c;
+  const size_t need = dspark_markov_sample_workspace_bytes(R, gamma, V, r, wdtype);
+  if (need > DSPARK_NOALLOC_SCRATCH_BYTES)
+    return fail(DSPARK_ERR_WORKSPACE,
+                "markov_sample_noalloc: R=%d, gamma=%d need %zu bytes of scratch, above the fixed %zu "
+                "(use dspark_markov_sample with a workspace)",
+                R, gamma, need, (size_t)DSPARK_NOALLOC_SCRATCH_BYTES);
+  int dev = -1;
+  uint64_t* keys = noalloc_scratch(&dev);
+  if (!keys) return fail(DSPARK_ERR_HIP, "markov_sample_noalloc: no scratch address on device %d", dev);
+  return markov_sample_run(base_logits, w1, w2, first_prev, tokens, step_logits, R, gamma, V, r, wdtype,
+                           temperature, seed, keys, dev_status, (hipStream_t)stream);
 }
 
 // Teacher-forced block logits (page 1 §3.7, apply_block_logits in training;

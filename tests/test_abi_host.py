@@ -33,7 +33,7 @@ def lib():
 def test_every_declared_symbol_is_exported(lib):
     mod, L = lib
     names = _declared()
-    assert len(names) == 21, names
+    assert len(names) == 22, names
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(mod.SIGNATURES)
@@ -219,3 +219,25 @@ def test_verify_workspace_and_bad_arguments(lib):
     assert L.dspark_verify(n, n, n, n, n, 4, 2, 10, -1.0, 0, n, 0, n, n) == mod.ERR_INVALID_ARG    # T < 0
     assert L.dspark_verify(n, n, n, n, n, 4, 2, 10, 1.0, 0, n, 0, n, n) == mod.ERR_INVALID_ARG     # null pointers
     assert L.dspark_verify(n, n, n, n, n, 0, 2, 10, 1.0, 0, n, 0, n, n) == mod.OK                  # nothing to do
+
+
+def test_markov_noalloc_rejects_sizes_beyond_its_array(lib):
+    mod, L = lib
+    p = ctypes.c_void_p(1)
+    # 128 rows x 65 steps of keys exceed the fixed array; refused on the host
+    assert L.dspark_markov_sample_workspace_bytes(128, 65, 151936, 256, mod.BF16) > mod.NOALLOC_SCRATCH_BYTES
+    rc = L.dspark_markov_sample_noalloc(p, p, p, p, p, None, 128, 65, 151936, 256, mod.BF16, 0.0, 0, None, None)
+    assert rc == mod.ERR_WORKSPACE and b"above the fixed" in L.dspark_last_error()
+    assert L.dspark_markov_sample_noalloc(None, p, p, p, p, None, 4, 2, 64, 32, mod.BF16, 0.0, 0, None,
+                                          None) == mod.ERR_INVALID_ARG
+    assert L.dspark_markov_sample_noalloc(p, p, p, p, p, None, 4, 2, 64, 32, mod.BF16, -1.0, 0, None,
+                                          None) == mod.ERR_INVALID_ARG
+    assert L.dspark_markov_sample_noalloc(p, p, p, p, p, None, 0, 2, 64, 32, mod.BF16, 0.0, 0, None,
+                                          None) == mod.OK
+
+
+def test_noalloc_limit_matches_header(lib):
+    mod, _ = lib
+    src = open(HEADER).read()
+    m = re.search(r"#define DSPARK_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", src)
+    assert m and (int(m.group(1)) << int(m.group(2))) == mod.NOALLOC_SCRATCH_BYTES
