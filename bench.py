@@ -26,7 +26,8 @@ per-operation breakdown, the roofline of the dominant kernel (achieved
 algorithmic GB/s from HIP events on the launch stream vs the 8 TB/s HBM
 peak) and the CPU oracle timed on a bounded sample of the same workload.
 
---only {round,attention,markov,accept,train_attention,copy,block_logits,l1_loss,schedule,heads,verify} restricts the run to one part
+--only {round,attention,markov,accept,train_attention,copy,block_logits,l1_loss,schedule,heads,verify,config1,config3}
+restricts the run to one part
 (for profiler runs); --no-cpu skips the CPU baseline.
 """
 
@@ -52,7 +53,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--only", choices=["round", "attention", "markov", "accept", "train_attention", "copy",
-                                       "block_logits", "l1_loss", "schedule", "heads", "verify"],
+                                       "block_logits", "l1_loss", "schedule", "heads", "verify", "config1",
+                                       "config3"],
                     default=None)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -186,6 +188,113 @@ def cpu_baseline(W, inp, budget_s):
                        "float64 numpy, BLAS threads = cores")
 
 
+def _oracle_threads(n):
+    """Context manager limiting the oracle's BLAS threads to n (None: as is)."""
+    import contextlib
+    if n is None:
+        return contextlib.nullcontext()
+    from threadpoolctl import threadpool_limits
+    return threadpool_limits(n)
+
+
+def _cores():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        return 1
+
+
+def config1_part(torch, dsp, W, dev, K, Wm, cpu):
+    """Tiny float32 draft round: eval mask + attention (2 rows x 8 blocks of
+    8, 4/2 heads, D = 64, context 128) + Markov sampling (16 rows, V = 4096,
+    r = 32, float32 weights, greedy).  Latency per round and 128 drafted
+    positions / t; the oracle on the same inputs, single-threaded and with
+    every BLAS thread."""
+    import numpy as np
+    attn, mk, mask = W.config1()
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    q, kc, vc, kb, vb = (t(getattr(attn, n)) for n in ("q", "k_ctx", "v_ctx", "k_blk", "v_blk"))
+    offs, anc, keep = t(attn.ctx_offsets), t(attn.anchor), t(attn.keep)
+    seq = t(mask.seq_lens)
+    lm = t(mask.loss_mask)
+    base, w1, w2, fp = t(mk.base), t(mk.w1), t(mk.w2), t(mk.first_prev)
+    out = torch.empty_like(q)
+    em = torch.empty((2, 8, 8), dtype=torch.uint8, device=dev)
+    tok = torch.empty((16, 8), dtype=torch.int32, device=dev)
+    wsa = torch.empty(max(1, dsp.block_attention_workspace_bytes(2, 8, 8, 4, 2, 64, 128)), dtype=torch.uint8,
+                      device=dev)
+    wsm = torch.empty(dsp.markov_sample_workspace_bytes(16, 8, 4096, 32, 0), dtype=torch.uint8, device=dev)
+
+    def rnd():
+        dsp.eval_mask(anc, keep, seq, lm, gamma=8, out=em)
+        dsp.block_attention(q, kc, vc, offs, kb, vb, anc, keep, max_ctx=128, scale=attn.scale, out=out,
+                            workspace=wsa)
+        dsp.markov_sample(base, w1, w2, fp, tokens=tok, workspace=wsm)
+
+    ms = timed(torch, rnd, K, Wm) if K > 0 else None
+    res = dict(ms=ms, tokens=128)
+    if cpu:
+        from oracle import attention as OA
+        from oracle import eval_mask as OE
+        from oracle import markov as OM
+
+        def oracle_round():
+            OE.eval_mask(mask.anchor, mask.keep, mask.seq_lens, mask.loss_mask, 8)
+            OA.block_attention(attn.q, attn.k_ctx, attn.v_ctx, attn.ctx_offsets, attn.k_blk, attn.v_blk,
+                               attn.anchor, attn.keep, 8, attn.scale)
+            OM.sample_block_tokens(mk.base, mk.w1, mk.w2, mk.first_prev, 0.0, 0)
+
+        for label, n in (("cpu_1thread", 1), ("cpu", None)):
+            with _oracle_threads(n):
+                oracle_round()
+                reps, t0 = 0, time.perf_counter()
+                while reps < 3 or time.perf_counter() - t0 < 2.0:
+                    oracle_round()
+                    reps += 1
+                el = (time.perf_counter() - t0) / reps
+                res[label] = dict(value=128 / el, unit="drafted tokens/s", ms=el * 1e3,
+                                  cores=1 if n == 1 else _cores(), kind="oracle",
+                                  sample=f"the whole round, {reps} repetitions")
+    return res
+
+
+def config3_part(torch, dsp, W, dev, K, Wm, cpu, budget_s):
+    """Markov sampling at the full configuration: 64 rows, gamma = 16,
+    V = 151936, rank 256, bf16 weights, temperature 1 Gumbel-max.  Time per
+    round, 1024 drafted tokens / t, algorithmic bytes per round vs the HBM
+    peak; the oracle on the first rows of the same inputs for about
+    budget_s."""
+    import numpy as np
+    c = W.CONFIG3
+    inp = W.config3_device(torch, dev)
+    R, G, V, r = c["R"], c["gamma"], c["V"], c["r"]
+    tok = torch.empty((R, G), dtype=torch.int32, device=dev)
+    ws = torch.empty(dsp.markov_sample_workspace_bytes(R, G, V, r), dtype=torch.uint8, device=dev)
+    f = lambda: dsp.markov_sample(inp["base"], inp["w1"], inp["w2"], inp["first_prev"],
+                                  temperature=inp["temperature"], seed=inp["seed"], tokens=tok, workspace=ws)
+    ms = timed(torch, f, K, Wm)
+    step_bytes = r * V * 2 + R * V * 4 + R * r * 2 + R * 4  # W2, base slice, W1 rows, prev
+    res = dict(ms=ms, tokens=R * G, bytes=G * step_bytes)
+    if cpu:
+        from oracle import markov as OM
+        fb = lambda x: W.bf16_to_f32(x.contiguous().view(torch.int16).cpu().numpy().view(np.uint16))
+        w1 = fb(inp["w1"]).astype(np.float64)
+        w2 = fb(inp["w2"]).astype(np.float64)
+        fp = inp["first_prev"].cpu().numpy()
+        n, t0 = 0, time.perf_counter()
+        while n < 1 or (time.perf_counter() - t0 < budget_s and n < R):
+            OM.sample_block_tokens(inp["base"][n:n + 1].cpu().numpy(), w1, w2, fp[n:n + 1],
+                                   inp["temperature"], inp["seed"], rows=np.array([n]))
+            n += 1
+        el = time.perf_counter() - t0
+        res["cpu"] = dict(value=n * G / el, unit="drafted tokens/s", cores=_cores(), kind="oracle",
+                          sample=f"first {n} of {R} rows, all 16 steps; {el:.1f} s; float64 numpy")
+    del inp, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -241,6 +350,18 @@ def main():
         round_inp = inp  # the CPU baseline runs last: seconds of host work would idle the GPU in between
         del bufs
         torch.cuda.empty_cache()
+
+    if args.only in (None, "config1"):
+        result["config1"] = config1_part(torch, dsp, W, dev, K, Wm, cpu=args.only == "config1" and not args.no_cpu)
+        if args.only == "config1":
+            print(json.dumps(result["config1"]))
+            return
+
+    if args.only in (None, "config3"):
+        result["config3"] = config3_part(torch, dsp, W, dev, K, Wm, cpu=False)
+        if args.only == "config3":
+            print(json.dumps(result["config3"]))
+            return
 
     if args.only in (None, "train_attention"):
         # training-shaped all-anchor attention: 472 kept blocks of 8 rows
@@ -392,6 +513,14 @@ def main():
 
     if not args.no_cpu:
         result["cpu"] = cpu_baseline(W, round_inp, args.cpu_seconds)
+        if "config1" in result:
+            # the oracles beside workloads 1 and 3, after every GPU part (idle GPU time between parts
+            # lowers the clocks of the next one)
+            c1 = config1_part(torch, dsp, W, dev, 0, 0, cpu=True)
+            result["config1"].update({k: c1[k] for k in ("cpu", "cpu_1thread")})
+        if "config3" in result:
+            result["config3"]["cpu"] = config3_part(torch, dsp, W, dev, 1, 0, cpu=True,
+                                                    budget_s=args.cpu_seconds / 2)["cpu"]
 
     r = result["round"]
     attn_gbs = r["attn_bytes"] / r["attn_ms"] / 1e6
@@ -466,6 +595,22 @@ def main():
                                                   "Hq=32/Hkv=8, D=128, bf16",
                                       "ms": a["ms"], "TFLOPs": tf, "mfma_frac": tf / MFMA_BF16_PEAK_TFLOPS,
                                       "algorithmic_flops": a["flops"]}
+    if "config1" in result:
+        a = result["config1"]
+        line["config1"] = {"workload": "tiny float32 round: 2 x 8 blocks of 8 over context 128, Hq=4/Hkv=2, D=64; "
+                                       "Markov 16 rows, V=4096, rank 32, greedy; eval mask",
+                           "ms": a["ms"], "tokens_per_s": a["tokens"] / (a["ms"] / 1e3)}
+        for k in ("cpu", "cpu_1thread"):
+            if k in a:
+                line["config1"][k] = a[k]
+    if "config3" in result:
+        a = result["config3"]
+        gbs = a["bytes"] / a["ms"] / 1e6
+        line["config3"] = {"workload": "Markov sampling: 64 rows, gamma=16, V=151936, rank 256, bf16 weights, "
+                                       "T=1 Gumbel-max", "ms": a["ms"], "tokens_per_s": a["tokens"] / (a["ms"] / 1e3),
+                           "GBps": gbs, "hbm_frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes": a["bytes"]}
+        if "cpu" in a:
+            line["config3"]["cpu"] = a["cpu"]
     if "cpu" in result:
         line["cpu_baseline"] = result["cpu"]
     print(json.dumps(line))

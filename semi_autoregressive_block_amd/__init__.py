@@ -6,16 +6,20 @@ outputs and workspace it needs through torch's allocator.  All arithmetic
 runs in the library's HIP kernels; if the library is missing the import
 fails.
 
-Functions (same names and argument meaning as the C entry points):
+Functions (same names and argument meaning as the C entry points; each
+``*_workspace_bytes`` mirrors the C size query):
 
 * ``block_attention``  — block-masked dual-source attention
 * ``markov_sample``    — Markov-head gamma-step sampler
 * ``markov_sample_noalloc`` — the same through the allocation-free entry point
-* ``accept_rate``      — TV accept rate (+ tau)
+* ``accept_rate``      — TV accept rate (+ tau); ``set_wait_limit``
 * ``eval_mask``        — cumulative-product eval mask
 * ``markov_block_logits`` — teacher-forced Markov logits of a whole block
+* ``markov_head_sample`` / ``markov_head_block_logits`` — the same for the
+  gated and recurrent heads
 * ``l1_loss``          — L1 (TV) alignment loss, its gradient, tau_greedy
 * ``confidence_schedule`` — confidence head, prefix survival, verify length
+* ``verify``           — lossless verify (rejection sampling) of drafted blocks
 """
 
 from __future__ import annotations
@@ -28,11 +32,17 @@ from . import _lib
 
 _LIB = _lib.load()
 
-__all__ = ["block_attention", "markov_sample", "markov_sample_noalloc", "accept_rate", "eval_mask",
-           "block_attention_workspace_bytes", "markov_sample_workspace_bytes",
-           "accept_rate_workspace_bytes", "markov_block_logits", "markov_block_logits_workspace_bytes",
-           "l1_loss", "l1_loss_workspace_bytes", "confidence_schedule", "set_wait_limit", "last_error", "version",
-           "DSparkError"]
+__all__ = ["block_attention", "block_attention_workspace_bytes",
+           "markov_sample", "markov_sample_noalloc", "markov_sample_workspace_bytes",
+           "accept_rate", "accept_rate_workspace_bytes", "set_wait_limit",
+           "eval_mask",
+           "markov_block_logits", "markov_block_logits_workspace_bytes",
+           "markov_head_sample", "markov_head_sample_workspace_bytes",
+           "markov_head_block_logits", "markov_head_block_logits_workspace_bytes",
+           "l1_loss", "l1_loss_workspace_bytes",
+           "confidence_schedule",
+           "verify", "verify_workspace_bytes",
+           "last_error", "version", "DSparkError"]
 
 
 class DSparkError(RuntimeError):

@@ -9,7 +9,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "dspark.h")
-LIB = os.path.join(ROOT, "semi_autoregressive_block_amd", "libdspark.so")
+LIB = os.environ.get("DSPARK_LIB_PATH") or os.path.join(ROOT, "semi_autoregressive_block_amd", "libdspark.so")
 
 
 def _declared():
