@@ -259,7 +259,7 @@ def config1_part(torch, dsp, W, dev, K, Wm, cpu):
     return res
 
 
-def config3_part(torch, dsp, W, dev, K, Wm, cpu, budget_s):
+def config3_part(torch, dsp, W, dev, K, Wm, cpu, budget_s=10.0):
     """Markov sampling at the full configuration: 64 rows, gamma = 16,
     V = 151936, rank 256, bf16 weights, temperature 1 Gumbel-max.  Time per
     round, 1024 drafted tokens / t, algorithmic bytes per round vs the HBM

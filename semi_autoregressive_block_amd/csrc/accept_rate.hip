@@ -586,6 +586,13 @@ extern "C" void dspark_set_wait_limit(uint32_t polls) {
   g_wait_limit.store(polls, std::memory_order_relaxed);
 }
 
+namespace dspark {
+uint32_t wait_limit() {
+  const uint32_t lim = g_wait_limit.load(std::memory_order_relaxed);
+  return lim ? lim : kSpinLimit;
+}
+}  // namespace dspark
+
 extern "C" int dspark_accept_rate(const void* draft_logits, const void* target_logits,
                                   float* accept, const uint8_t* eval_mask, float* tau, int B,
                                   int A, int gamma, int V, int dtype, void* ws, size_t ws_bytes,

@@ -575,6 +575,16 @@ int markov_sample_run(const float* base_logits, const void* w1, const void* w2, 
   if (cus <= 0) return fail(DSPARK_ERR_HIP, "markov_sample: device query failed");
 
   const bool bf = wdtype == DSPARK_BF16;
+  // up to 128 rows with bf16 weights: every step in one persistent launch with W2 held in
+  // registers (markov_round.hip); otherwise one launch per step
+  if (bf && markov_round_eligible(R, gamma, V, r, base_logits, w1, w2, step_logits)) {
+    const hipError_t e = markov_round_launch(base_logits, (const uint16_t*)w1, (const uint16_t*)w2, first_prev,
+                                             tokens, step_logits, R, gamma, V, r, invT, greedy, slo, shi, keys,
+                                             wait_limit(), dev_status, s);
+    if (e == hipSuccess) return check_launch("markov_sample");
+    if (e != hipErrorNotSupported)
+      return fail(DSPARK_ERR_HIP, "markov_sample (one launch): %s", hipGetErrorString(e));
+  }
   const bool mfma_ok = bf && V % 8 == 0 && r % 8 == 0 && r <= 512 && (uintptr_t)w1 % 16 == 0 &&
                        (uintptr_t)w2 % 16 == 0 && (uintptr_t)base_logits % 16 == 0 &&
                        (!step_logits || (uintptr_t)step_logits % 16 == 0);

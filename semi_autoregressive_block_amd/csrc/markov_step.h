@@ -43,6 +43,20 @@ hipError_t markov_step_embedded(const float* base, const float* ebuf, const void
                                 float softcap, float temperature, uint64_t seed, hipStream_t s);
 // Zero n key slots (a fill kernel: safe under stream capture).
 hipError_t markov_zero_keys(uint64_t* keys, int64_t n, hipStream_t s);
+// The whole gamma-step sampler in one persistent cooperative launch, with W2
+// held in registers across the steps (bf16 weights, R <= 128 rows, r a
+// multiple of 32 up to 256, V a multiple of 8, 16-byte aligned buffers).
+// keys: gamma * keys_per_step(R) zeroed slots; tokens [R, gamma] are written
+// directly.  hipErrorNotSupported (nothing enqueued) when the shape or the
+// device does not allow it.
+bool markov_round_eligible(int R, int gamma, int V, int r, const void* base, const void* w1, const void* w2,
+                           const void* step_logits);
+hipError_t markov_round_launch(const float* base, const uint16_t* w1, const uint16_t* w2, const int32_t* first_prev,
+                               int32_t* tokens, float* step_logits, int R, int gamma, int V, int r, float invT,
+                               int greedy, uint32_t slo, uint32_t shi, uint64_t* keys, uint32_t spin_limit,
+                               int32_t* status, hipStream_t s);
+// Poll limit of the bounded waits inside cooperative grids (dspark_set_wait_limit).
+uint32_t wait_limit();
 // tokens[row, step] = the argmax index folded in step's keys, for R x gamma.
 hipError_t markov_finalize_tokens(const uint64_t* keys, int32_t* tokens, int R, int gamma, int V,
                                   int32_t* status, hipStream_t s);
