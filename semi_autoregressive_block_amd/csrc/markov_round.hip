@@ -184,28 +184,53 @@ __global__ __launch_bounds__(kRT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int ninst = (npieces + 63) / 64;           // 1 KB copies per base block
   const int my_inst = (ninst - wave + kRW - 1) / kRW;  // this wave's share: copies wave, wave + 8, ...
 
+  // ---- copies.  `issued` counts this wave's direct-to-LDS copies; a copy group is waited for with
+  //      vmcnt(issued - count after the group) (vector memory operations complete in order)
+  uint32_t issued = 0;
+
   // ---- W2 operands: A[u][kk], lane (n, g) holds W2[32kk + 8g + e][16(ua + u) + n], e = 0..7,
-  //      built through LDS one rank step at a time (the base ring stages 32 rank rows of the
-  //      workgroup's columns; the transposing read gives the operand layout).  Units past nu
-  //      and rank steps past r are zero.
+  //      built through LDS one rank step at a time: the 32 rank rows of the workgroup's columns
+  //      come in by direct-to-LDS copies (two rank steps in flight, in the base ring's space;
+  //      rows padded by one 16-byte piece), and the transposing read gives the operand layout.
+  //      Units past nu and rank steps past r are zero; columns past V hold copies of column
+  //      V - 8 .. V - 1, whose products are never used.
   u32x4 A[kKU][kKS];
   {
-    unsigned char* stg = bring;
-    const int spitch = nuw * 32 + 16;  // bytes per staged rank row (+16: spreads banks)
-    const int npc = 32 * nuw * 2;      // 16-byte pieces per rank step
+    const int spc = 2 * nuw + 1;          // 16-byte pieces per staged rank row (last: padding)
+    const int spitch = spc * 16;
+    const int nwi = (32 * spc + 63) / 64;  // 1 KB copies per rank step
+    const int my_w = nuw > 0 ? (nwi - wave + kRW - 1) / kRW : 0;
+    auto stage = [&](int kk) -> unsigned char* { return bring + (kk & 1) * (kNS * kBSlot / 2); };
+    auto issue_w2 = [&](int kk) {
+      unsigned char* dst = stage(kk);
+      for (int jj = 0; jj < my_w; ++jj) {
+        const int i = wave + jj * kRW;
+        const int p = i * 64 + lane;
+        if (p < 32 * spc) {
+          const int row = p / spc;
+          int q = p - row * spc;
+          q = q < 2 * nuw ? q : 2 * nuw - 1;
+          const int col = min(U0 * 16 + q * 8, V - 8);
+          __builtin_amdgcn_global_load_lds((const void*)(a.w2 + (int64_t)(32 * kk + row) * V + col),
+                                           (lds_void*)(dst + i * 1024), 16, 0, 0);
+        }
+      }
+      issued += my_w;
+    };
+    uint32_t done_at[2] = {0, 0};
+    issue_w2(0);
+    done_at[0] = issued;
+    if (ks > 1) {
+      issue_w2(1);
+      done_at[1] = issued;
+    }
+    const int ul = ua - U0;
 #pragma unroll
     for (int kk = 0; kk < kKS; ++kk) {
       if (kk < ks) {
-        for (int pc = threadIdx.x; pc < npc; pc += kRT) {
-          const int row = pc / (2 * nuw), q = pc % (2 * nuw);
-          const int k = 32 * kk + row;
-          const int64_t col = (int64_t)U0 * 16 + q * 8;
-          u32x4 v = u32x4{0u, 0u, 0u, 0u};
-          if (k < r && col < V) v = *(const u32x4*)(a.w2 + (int64_t)k * V + col);
-          *(u32x4*)(stg + row * spitch + q * 16) = v;
-        }
-        __syncthreads();
-        const int ul = ua - U0;
+        wait_vmcnt_upto((int)(issued - done_at[kk & 1]));
+        block_barrier();  // every wave's copies of rank step kk have landed
+        const unsigned char* stg = stage(kk);
 #pragma unroll
         for (int u = 0; u < kKU; ++u) {
           u32x4 v = u32x4{0u, 0u, 0u, 0u};
@@ -218,7 +243,11 @@ __global__ __launch_bounds__(kRT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           }
           A[u][kk] = v;
         }
-        __syncthreads();
+        __syncthreads();  // every wave is done with this stage buffer
+        if (kk + 2 < ks) {
+          issue_w2(kk + 2);
+          done_at[kk & 1] = issued;
+        }
       } else {
 #pragma unroll
         for (int u = 0; u < kKU; ++u) A[u][kk] = u32x4{0u, 0u, 0u, 0u};
@@ -226,9 +255,8 @@ __global__ __launch_bounds__(kRT) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
   }
 
-  // ---- copies.  `issued` counts this wave's copies; last_b / last_e hold the count after each
-  //      ring slot's latest copies, so a block is waited for with vmcnt(issued - last)
-  uint32_t issued = 0, last_b[kNS] = {0, 0, 0}, last_e[kNS] = {0, 0, 0};
+  // last_b / last_e: the copy count after each ring slot's latest copies
+  uint32_t last_b[kNS] = {0, 0, 0}, last_e[kNS] = {0, 0, 0};
   // base block rb of step st into slot: piece p = q * pitch + c (row q of the block, column piece c;
   // c == 4 nuw is padding, filled with a duplicate of the row's last piece)
   // (q = p / pitch through a float reciprocal: exact here, since p < 2^12 and (p + 1/2) / pitch
