@@ -664,11 +664,19 @@ __global__ __launch_bounds__(64 * NPAR * RG) __attribute__((amdgpu_waves_per_eu(
 
 // ------------------------------------------------------ vector-ALU kernel
 // float32 inputs (and any input the MFMA path does not take): one wave per
-// (b, a, query head), rows of the block one after another, keys across lanes.
+// (b, a, query head).  The block's rows go in groups of eight; for each
+// group the visible keys go in chunks of 64: the chunk's K and V rows are
+// copied into LDS with coalesced loads (lanes along the head dim), then
+// lane j takes key j's scores against the eight query rows, each row takes
+// an online-softmax step (wave reductions), and P.V runs with lanes along
+// the head dim.
+constexpr int kValuRows = 8;
 template <bool kBf16>
 __global__ __launch_bounds__(64) void block_attn_valu(Params p, int D) {
-  __shared__ float qs[128];
-  __shared__ float ps[64];
+  __shared__ __align__(16) float qs[kValuRows][128];
+  __shared__ float ks[64][129];  // +1: lane j's reads of row j hit distinct banks
+  __shared__ float vs[64][128];
+  __shared__ __align__(16) float ps[kValuRows][64];
   auto ld = [&](const void* base, int64_t i) -> float {
     return kBf16 ? __uint_as_float((uint32_t)((const uint16_t*)base)[i] << 16) : ((const float*)base)[i];
   };
@@ -684,64 +692,103 @@ __global__ __launch_bounds__(64) void block_attn_valu(Params p, int D) {
   const bool kept = lim >= 0;
   if (!kept) lim = 0;
   const float c = p.scale * kLog2e;
-  for (int k = 0; k < p.gamma; ++k) {
-    const int64_t qrow = ((int64_t)b * p.A * p.gamma + (int64_t)a * p.gamma + k) * p.Hq + h;
+  const int nkeys = kept ? lim + p.gamma : 0;
+  const int64_t own0 = (int64_t)b * p.A * p.gamma + (int64_t)a * p.gamma;
+  // head-dim offset of key j's row (context keys first, then the block's own)
+  auto key_off = [&](int j) -> int64_t {
+    const int64_t row = j < lim ? (int64_t)c0 + j : own0 + (j - lim);
+    return (row * p.Hkv + kvh) * D;
+  };
+  for (int k0 = 0; k0 < p.gamma; k0 += kValuRows) {
+    const int nr = min(kValuRows, p.gamma - k0);
     __syncthreads();
-    for (int d = lane; d < D; d += 64) qs[d] = ld(p.q, qrow * D + d);
-    __syncthreads();
-    float m = -INFINITY, l = 0.f, o0 = 0.f, o1 = 0.f;
-    const int nkeys = kept ? lim + p.gamma : 0;
+    for (int kr = 0; kr < kValuRows; ++kr) {
+      const int64_t qrow = (own0 + k0 + min(kr, nr - 1)) * p.Hq + h;
+      for (int d = lane; d < D; d += 64) qs[kr][d] = ld(p.q, qrow * D + d);
+    }
+    float m[kValuRows], l[kValuRows], o0[kValuRows], o1[kValuRows];
+#pragma unroll
+    for (int kr = 0; kr < kValuRows; ++kr) { m[kr] = -INFINITY; l[kr] = 0.f; o0[kr] = 0.f; o1[kr] = 0.f; }
     for (int j0 = 0; j0 < nkeys; j0 += 64) {
-      const int j = j0 + lane;
-      float s = -INFINITY;
-      int64_t row = 0;
-      const void *kbp = nullptr, *vbp = nullptr;
-      if (j < nkeys) {
-        if (j < lim) { row = (int64_t)c0 + j; kbp = p.kc; vbp = p.vc; }
-        else { row = (int64_t)b * p.A * p.gamma + (int64_t)a * p.gamma + (j - lim); kbp = p.kb; vbp = p.vb; }
-        float acc = 0.f;
-        for (int d = 0; d < D; ++d) acc = fmaf(qs[d], ld(kbp, (row * p.Hkv + kvh) * D + d), acc);
-        s = acc;
-      }
-      float smax = s;
-      for (int off = 32; off > 0; off >>= 1) smax = fmaxf(smax, __shfl_xor(smax, off, 64));
-      const float mn = fmaxf(m, smax);
-      const float mu = mn == -INFINITY ? 0.f : mn;
-      const float alpha = __builtin_amdgcn_exp2f((m - mu) * c);
-      const float pj = j < nkeys ? __builtin_amdgcn_exp2f((s - mu) * c) : 0.f;
-      float psum = pj;
-      for (int off = 32; off > 0; off >>= 1) psum += __shfl_xor(psum, off, 64);
-      l = l * alpha + psum;
-      m = mn;
-      o0 *= alpha; o1 *= alpha;
-      __syncthreads();
-      ps[lane] = pj;
-      __syncthreads();
       const int nj = min(64, nkeys - j0);
+      __syncthreads();  // the previous chunk's reads are done
       for (int jj = 0; jj < nj; ++jj) {
-        const int jg = j0 + jj;
-        int64_t vr;
-        const void* vp;
-        if (jg < lim) { vr = (int64_t)c0 + jg; vp = p.vc; }
-        else { vr = (int64_t)b * p.A * p.gamma + (int64_t)a * p.gamma + (jg - lim); vp = p.vb; }
-        const float w = ps[jj];
-        if (lane < D) o0 = fmaf(w, ld(vp, (vr * p.Hkv + kvh) * D + lane), o0);
-        if (lane + 64 < D) o1 = fmaf(w, ld(vp, (vr * p.Hkv + kvh) * D + lane + 64), o1);
+        const int64_t off = key_off(j0 + jj);
+        const void* kp = j0 + jj < lim ? (const void*)p.kc : (const void*)p.kb;
+        const void* vp = j0 + jj < lim ? (const void*)p.vc : (const void*)p.vb;
+        for (int d = lane; d < D; d += 64) {
+          ks[jj][d] = ld(kp, off + d);
+          vs[jj][d] = ld(vp, off + d);
+        }
+      }
+      __syncthreads();
+      // scores of key j0 + lane against the group's rows
+      float sc[kValuRows];
+#pragma unroll
+      for (int kr = 0; kr < kValuRows; ++kr) sc[kr] = 0.f;
+      if (lane < nj) {
+        for (int d = 0; d < D; d += 4) {
+          const float k0v = ks[lane][d], k1v = ks[lane][d + 1], k2v = ks[lane][d + 2], k3v = ks[lane][d + 3];
+#pragma unroll
+          for (int kr = 0; kr < kValuRows; ++kr) {
+            const float4 q4 = *(const float4*)&qs[kr][d];
+            sc[kr] = fmaf(q4.x, k0v, fmaf(q4.y, k1v, fmaf(q4.z, k2v, fmaf(q4.w, k3v, sc[kr]))));
+          }
+        }
+      }
+#pragma unroll
+      for (int kr = 0; kr < kValuRows; ++kr) {
+        const float s = lane < nj ? sc[kr] : -INFINITY;
+        float smax = s;
+        for (int off = 32; off > 0; off >>= 1) smax = fmaxf(smax, __shfl_xor(smax, off, 64));
+        const float mn = fmaxf(m[kr], smax);
+        const float mu = mn == -INFINITY ? 0.f : mn;
+        const float alpha = __builtin_amdgcn_exp2f((m[kr] - mu) * c);
+        const float pj = lane < nj ? __builtin_amdgcn_exp2f((s - mu) * c) : 0.f;
+        float psum = pj;
+        for (int off = 32; off > 0; off >>= 1) psum += __shfl_xor(psum, off, 64);
+        l[kr] = l[kr] * alpha + psum;
+        m[kr] = mn;
+        o0[kr] *= alpha;
+        o1[kr] *= alpha;
+        ps[kr][lane] = pj;
+      }
+      __syncthreads();
+      // P.V with lanes along the head dim
+      for (int jj = 0; jj < nj; jj += 4) {
+        float v0[4], v1[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          v0[t] = (jj + t < nj && lane < D) ? vs[jj + t][lane] : 0.f;
+          v1[t] = (jj + t < nj && lane + 64 < D) ? vs[jj + t][lane + 64] : 0.f;
+        }
+#pragma unroll
+        for (int kr = 0; kr < kValuRows; ++kr) {
+          const float4 w = *(const float4*)&ps[kr][jj];  // entries past nj are zero
+          o0[kr] = fmaf(w.x, v0[0], fmaf(w.y, v0[1], fmaf(w.z, v0[2], fmaf(w.w, v0[3], o0[kr]))));
+          o1[kr] = fmaf(w.x, v1[0], fmaf(w.y, v1[1], fmaf(w.z, v1[2], fmaf(w.w, v1[3], o1[kr]))));
+        }
       }
     }
-    const float inv = (kept && l > 0.f) ? 1.f / l : 0.f;
-    if (kBf16) {
-      uint16_t* o = (uint16_t*)p.out + qrow * D;
-      if (lane < D) o[lane] = (uint16_t)f32_to_bf16(o0 * inv);
-      if (lane + 64 < D) o[lane + 64] = (uint16_t)f32_to_bf16(o1 * inv);
-    } else {
-      float* o = (float*)p.out + qrow * D;
-      if (lane < D) o[lane] = o0 * inv;
-      if (lane + 64 < D) o[lane + 64] = o1 * inv;
-    }
-    if (p.lse && lane == 0) {
-      const int64_t li = ((int64_t)b * p.Hq + h) * ((int64_t)p.A * p.gamma) + (int64_t)a * p.gamma + k;
-      p.lse[li] = (kept && l > 0.f) ? m * p.scale + kLn2 * __builtin_amdgcn_logf(l) : -INFINITY;
+#pragma unroll
+    for (int kr = 0; kr < kValuRows; ++kr) {
+      if (kr >= nr) break;
+      const int k = k0 + kr;
+      const int64_t qrow = (own0 + k) * p.Hq + h;
+      const float inv = (kept && l[kr] > 0.f) ? 1.f / l[kr] : 0.f;
+      if (kBf16) {
+        uint16_t* o = (uint16_t*)p.out + qrow * D;
+        if (lane < D) o[lane] = (uint16_t)f32_to_bf16(o0[kr] * inv);
+        if (lane + 64 < D) o[lane + 64] = (uint16_t)f32_to_bf16(o1[kr] * inv);
+      } else {
+        float* o = (float*)p.out + qrow * D;
+        if (lane < D) o[lane] = o0[kr] * inv;
+        if (lane + 64 < D) o[lane + 64] = o1[kr] * inv;
+      }
+      if (p.lse && lane == 0) {
+        const int64_t li = ((int64_t)b * p.Hq + h) * ((int64_t)p.A * p.gamma) + (int64_t)a * p.gamma + k;
+        p.lse[li] = (kept && l[kr] > 0.f) ? m[kr] * p.scale + kLn2 * __builtin_amdgcn_logf(l[kr]) : -INFINITY;
+      }
     }
   }
 }

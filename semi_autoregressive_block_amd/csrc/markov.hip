@@ -306,9 +306,14 @@ __global__ __launch_bounds__(64 * NW) void markov_step_mfma(
 // float32 (or unaligned bf16) weights: one thread per quad of columns,
 // 16 rows per pass with E in LDS, fp32 FMAs.
 constexpr int kRowChunk = 16;
+constexpr int kVThreads = 64;  // one wave per workgroup
 
+// One wave per (16-row chunk, run of column quads): E = the chunk's rank-r
+// rows, transposed into LDS ([k][16 rows]) so that each rank step reads the
+// 16 values with four broadcast reads; every lane owns one quad of columns
+// at a time and accumulates its 16 x 4 products in registers.
 template <bool kBf16W, bool SC = false, bool EB = false>
-__global__ __launch_bounds__(kThreads) void markov_step_valu(
+__global__ __launch_bounds__(kVThreads) void markov_step_valu(
     const float* __restrict__ base, const void* __restrict__ w1v, const float* __restrict__ ebuf,
     const void* __restrict__ w2v,
     const int32_t* __restrict__ first_prev, const uint64_t* __restrict__ keys_prev,
@@ -316,8 +321,8 @@ __global__ __launch_bounds__(kThreads) void markov_step_valu(
     int r, int step, float invT, int greedy, uint32_t seed_lo, uint32_t seed_hi,
     int32_t* __restrict__ status) {
   extern __shared__ __align__(16) unsigned char smem[];
-  float* E = (float*)smem;                                        // [kRowChunk][r]
-  uint64_t* rowkey = (uint64_t*)(smem + (size_t)kRowChunk * r * 4);  // [kRowChunk]
+  float* Et = (float*)smem;  // [r][kRowChunk]
+  __shared__ int prev_tok[kRowChunk];
   auto w1 = [&](int64_t i) -> float {
     return kBf16W ? __uint_as_float((uint32_t)((const uint16_t*)w1v)[i] << 16) : ((const float*)w1v)[i];
   };
@@ -325,53 +330,81 @@ __global__ __launch_bounds__(kThreads) void markov_step_valu(
     return kBf16W ? __uint_as_float((uint32_t)((const uint16_t*)w2v)[i] << 16) : ((const float*)w2v)[i];
   };
   const int row0 = blockIdx.y * kRowChunk;
-  for (int c = threadIdx.x; c < kRowChunk * r; c += kThreads) {
+  if (!EB && threadIdx.x < kRowChunk) {  // the chunk's previous tokens, decoded once
+    const int row = row0 + threadIdx.x;
+    prev_tok[threadIdx.x] =
+        row < R ? decode_prev(keys_prev, first_prev, row, R, V, blockIdx.x == 0 ? status : nullptr) : 0;
+  }
+  __syncthreads();
+  for (int c = threadIdx.x; c < kRowChunk * r; c += kVThreads) {
     const int rr = c / r, k = c % r, row = row0 + rr;
     float v = 0.f;
     if (row < R) {
       if constexpr (EB) v = ebuf[((int64_t)row * gamma + step) * r + k];
-      else v = w1((int64_t)decode_prev(keys_prev, first_prev, row, R, V, nullptr) * r + k);
+      else v = w1((int64_t)prev_tok[rr] * r + k);
     }
-    E[c] = v;
+    Et[k * kRowChunk + rr] = v;
   }
-  if (threadIdx.x < kRowChunk) rowkey[threadIdx.x] = 0ull;
-  if (!EB && threadIdx.x < kRowChunk && row0 + threadIdx.x < R && blockIdx.x == 0)
-    decode_prev(keys_prev, first_prev, row0 + threadIdx.x, R, V, status);
   __syncthreads();
 
   const int64_t nq = (V + 3) / 4;
-  const int64_t q0 = (int64_t)blockIdx.x * nq / gridDim.x, q1 = (int64_t)(blockIdx.x + 1) * nq / gridDim.x;
   float best_z[kRowChunk];
   uint32_t best_v[kRowChunk];
 #pragma unroll
   for (int i = 0; i < kRowChunk; ++i) { best_z[i] = -INFINITY; best_v[i] = 0xffffffffu; }
-  for (int64_t q = q0 + threadIdx.x; q < q1; q += kThreads) {
-    for (int j = 0; j < 4; ++j) {
-      const int64_t v = q * 4 + j;
-      if (v >= V) break;
-      float acc[kRowChunk];
+  for (int64_t q = (int64_t)blockIdx.x * kVThreads + threadIdx.x; q < nq; q += (int64_t)gridDim.x * kVThreads) {
+    const int64_t v0 = q * 4;
+    float acc[kRowChunk][4];
 #pragma unroll
-      for (int i = 0; i < kRowChunk; ++i) acc[i] = 0.f;
-      for (int k = 0; k < r; ++k) {
-        const float w = w2((int64_t)k * V + v);
+    for (int i = 0; i < kRowChunk; ++i)
 #pragma unroll
-        for (int i = 0; i < kRowChunk; ++i) acc[i] = fmaf(E[i * r + k], w, acc[i]);
+      for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
+    constexpr int kKB = 8;  // rank steps whose W2 loads go out together
+    for (int k0 = 0; k0 < r; k0 += kKB) {
+      float w[kKB][4];
+#pragma unroll
+      for (int kb = 0; kb < kKB; ++kb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          w[kb][j] = (k0 + kb < r && v0 + j < V) ? w2((int64_t)(k0 + kb) * V + v0 + j) : 0.f;
+#pragma unroll
+      for (int kb = 0; kb < kKB; ++kb) {
+        if (k0 + kb >= r) break;
+        const f32x4* e4 = (const f32x4*)(Et + (k0 + kb) * kRowChunk);
+#pragma unroll
+        for (int i4 = 0; i4 < kRowChunk / 4; ++i4) {
+          const f32x4 e = e4[i4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            acc[4 * i4 + 0][j] = fmaf(e[0], w[kb][j], acc[4 * i4 + 0][j]);
+            acc[4 * i4 + 1][j] = fmaf(e[1], w[kb][j], acc[4 * i4 + 1][j]);
+            acc[4 * i4 + 2][j] = fmaf(e[2], w[kb][j], acc[4 * i4 + 2][j]);
+            acc[4 * i4 + 3][j] = fmaf(e[3], w[kb][j], acc[4 * i4 + 3][j]);
+          }
+        }
       }
-      uint32_t x = 0;
+    }
+    float bl[kRowChunk][4];  // the chunk's base logits, all loads in flight together
 #pragma unroll
-      for (int i = 0; i < kRowChunk; ++i) {
-        const int row = row0 + i;
-        if (row >= R) break;
+    for (int i = 0; i < kRowChunk; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        bl[i][j] = (row0 + i < R && v0 + j < V) ? base[((int64_t)(row0 + i) * gamma + step) * V + v0 + j] : 0.f;
+#pragma unroll
+    for (int i = 0; i < kRowChunk; ++i) {
+      const int row = row0 + i;
+      if (row >= R) break;
+      u32x4 xs = u32x4{0u, 0u, 0u, 0u};
+      if (!greedy) xs = philox4x32_10(u32x4{(uint32_t)q, (uint32_t)step, (uint32_t)row, 0u}, seed_lo, seed_hi);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t v = v0 + j;
+        if (v >= V) break;
         const int64_t off = ((int64_t)row * gamma + step) * V + v;
-        float l = base[off] + acc[i];
+        float l = bl[i][j] + acc[i][j];
         if constexpr (SC) l = tanhf(l * invT) / invT;
         if (step_logits) step_logits[off] = l;
-        float z = l;
-        if (!greedy) {
-          const u32x4 xs = philox4x32_10(u32x4{(uint32_t)q, (uint32_t)step, (uint32_t)row, 0u}, seed_lo, seed_hi);
-          x = xs[j];
-          z = fmaf(l, invT, gumbel_from_bits(x));
-        }
+        const float z = greedy ? l : fmaf(l, invT, gumbel_from_bits(xs[j]));
         if (z > best_z[i]) { best_z[i] = z; best_v[i] = (uint32_t)v; }
       }
     }
@@ -384,13 +417,8 @@ __global__ __launch_bounds__(kThreads) void markov_step_valu(
       const uint64_t o = shfl_xor_u64(key, m);
       key = o > key ? o : key;
     }
-    if ((threadIdx.x & 63) == 0 && key) atomicMax((unsigned long long*)&rowkey[i], (unsigned long long)key);
-  }
-  __syncthreads();
-  if (threadIdx.x < kRowChunk) {
-    const int row = row0 + threadIdx.x;
-    const uint64_t key = rowkey[threadIdx.x];
-    if (row < R && key) fold_key_global(keys_out, row, R, key);
+    const int row = row0 + i;
+    if (threadIdx.x == 0 && row < R && key) fold_key_global(keys_out, row, R, key);
   }
 }
 
@@ -475,17 +503,17 @@ hipError_t launch_step(bool mfma_ok, bool bf, int cus, hipStream_t s, const floa
                     : launch_mfma<4, 16, 2, false, SC, EB>(gx, gy, s, base, a, ebuf, b, first_prev, kp, ko, step_logits, R, gamma, V, r, step, invT, greedy, slo, shi, st);
   }
   const int gy = (R + kRowChunk - 1) / kRowChunk;
-  int gx = 2 * cus;
+  int gx = 4 * cus;
   const int64_t quads = (V + 3) / 4;
-  if ((int64_t)gx * kThreads > quads) gx = (int)((quads + kThreads - 1) / kThreads);
+  if ((int64_t)gx * kVThreads > quads) gx = (int)((quads + kVThreads - 1) / kVThreads);
   if (gx < 1) gx = 1;
-  const size_t shm = (size_t)kRowChunk * r * 4 + kRowChunk * 8;
+  const size_t shm = (size_t)kRowChunk * r * 4;
   if (bf) {
     (void)allow_lds_once(markov_step_valu<true, SC, EB>, shm);
-    hipLaunchKernelGGL((markov_step_valu<true, SC, EB>), dim3(gx, gy), dim3(kThreads), shm, s, base, w1, ebuf, w2, first_prev, kp, ko, step_logits, R, gamma, V, r, step, invT, greedy, slo, shi, st);
+    hipLaunchKernelGGL((markov_step_valu<true, SC, EB>), dim3(gx, gy), dim3(kVThreads), shm, s, base, w1, ebuf, w2, first_prev, kp, ko, step_logits, R, gamma, V, r, step, invT, greedy, slo, shi, st);
   } else {
     (void)allow_lds_once(markov_step_valu<false, SC, EB>, shm);
-    hipLaunchKernelGGL((markov_step_valu<false, SC, EB>), dim3(gx, gy), dim3(kThreads), shm, s, base, w1, ebuf, w2, first_prev, kp, ko, step_logits, R, gamma, V, r, step, invT, greedy, slo, shi, st);
+    hipLaunchKernelGGL((markov_step_valu<false, SC, EB>), dim3(gx, gy), dim3(kVThreads), shm, s, base, w1, ebuf, w2, first_prev, kp, ko, step_logits, R, gamma, V, r, step, invT, greedy, slo, shi, st);
   }
   return hipGetLastError();
 }
