@@ -302,7 +302,7 @@ def config3_part(torch, dsp, W, dev, K, Wm, cpu, budget_s=10.0):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "the bench runs on one GPU: --gpus must be 1 (the path has no multi-GPU mode)",
                           "n_gpus": args.gpus}))
         sys.exit(2)
     import torch

@@ -30,11 +30,9 @@
 
 #include <algorithm>
 #include <atomic>
-#include <map>
-#include <mutex>
-#include <utility>
 
 #include "common.h"
+#include "host_cache.h"
 
 using namespace dspark;
 
@@ -523,13 +521,10 @@ int device_cus() {
 // 512 VGPRs per SIMD lane, allocated in blocks of 8), so a cluster never
 // waits on a member that the hardware could not place.
 int device_wg_capacity(const void* kernel) {
-  static std::mutex mu;
-  static std::map<std::pair<int, const void*>, int> cache;
-  int dev = 0;
+  static KeyedCache<int> cache;
+  int dev = 0, have = 0;
   if (hipGetDevice(&dev) != hipSuccess) return -1;
-  std::lock_guard<std::mutex> lock(mu);
-  auto it = cache.find({dev, kernel});
-  if (it != cache.end()) return it->second;
+  if (cache.find(dev, kernel, have)) return have;
   int cus = 0, per = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, kThreads, 0) != hipSuccess) return -1;
@@ -543,7 +538,7 @@ int device_wg_capacity(const void* kernel) {
   if (getenv("DSPARK_VERBOSE"))
     fprintf(stderr, "[dspark] accept_rate: %d VGPRs, %zu B LDS -> %d workgroups per CU\n",
             attr.numRegs, (size_t)attr.sharedSizeBytes, per);
-  cache[{dev, kernel}] = cus * per;
+  cache.put(dev, kernel, cus * per);
   return cus * per;
 }
 

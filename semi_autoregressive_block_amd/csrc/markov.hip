@@ -23,10 +23,9 @@
 //   replicas on the device; there is no host round trip inside the gamma
 //   loop.
 #include <atomic>
-#include <map>
-#include <mutex>
 
 #include "common.h"
+#include "host_cache.h"
 #include "philox.h"
 #include "markov_step.h"
 
@@ -451,14 +450,12 @@ int cu_count() {
 // of microseconds of host time, far more than a step's launch).
 template <typename K>
 hipError_t allow_lds_once(K kern, size_t bytes) {
-  static std::mutex mu;
-  static std::map<const void*, size_t> done;
-  std::lock_guard<std::mutex> lock(mu);
-  size_t& have = done[(const void*)kern];
-  if (have >= bytes) return hipSuccess;
+  static KeyedCache<size_t> done;
+  size_t have = 0;
+  if (done.find(0, (const void*)kern, have) && have >= bytes) return hipSuccess;
   const hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                                            (int)bytes);
-  if (e == hipSuccess) have = bytes;
+  if (e == hipSuccess) done.put(0, (const void*)kern, bytes);
   return e;
 }
 

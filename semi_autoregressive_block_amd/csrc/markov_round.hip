@@ -41,10 +41,9 @@
 // co-resident).  The arrival counter of step i lives in the last key of
 // replica 0 of step i's slots (unused: R <= 128 rows of 512 per replica).
 #include <atomic>
-#include <map>
-#include <mutex>
 
 #include "common.h"
+#include "host_cache.h"
 #include "markov_step.h"
 #include "philox.h"
 
@@ -454,19 +453,16 @@ struct Capacity {
 // Compute units and co-resident workgroups of the round kernel per device
 // (cached: the queries cost far more than a launch).
 Capacity round_capacity(const void* kern) {
-  static std::mutex mu;
-  static std::map<std::pair<int, const void*>, Capacity> cache;
+  static KeyedCache<Capacity> cache;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return {};
-  std::lock_guard<std::mutex> lock(mu);
-  auto it = cache.find({dev, kern});
-  if (it != cache.end()) return it->second;
   Capacity c;
+  if (cache.find(dev, kern, c)) return c;
   if (hipDeviceGetAttribute(&c.cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return {};
   int coop = 0;
   if (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess || !coop) c.cus = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&c.per_cu, kern, kRT, 0) != hipSuccess) c.per_cu = 0;
-  cache[{dev, kern}] = c;
+  cache.put(dev, kern, c);
   return c;
 }
 
