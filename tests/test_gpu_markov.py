@@ -65,6 +65,10 @@ def test_config1_fp32(dsp):
     (64, 4, 65536, 72, 0.5),      # rank zero-padded to 256, 64-row workgroups
     (128, 1, 60000, 256, 0.0),    # a single step
     (100, 6, 52000, 128, 1.0),    # rank 128, ragged last tile
+    (81, 4, 40000, 256, 0.0),     # six row blocks, the last with one row: block-pipelined round kernel
+    (96, 5, 40000, 256, 0.8),     # six full row blocks, Gumbel noise
+    (120, 3, 30000, 64, 0.0),     # eight row blocks, rank 64
+    (128, 6, 20000, 256, 1.0),    # eight full row blocks, Gumbel noise
 ])
 def test_bf16_variants(dsp, R, G, V, r, T):
     mk = W.markov_case(R * 1000 + V, R, G, V, r, "bf16", base_std=2.0, w1_std=1.0,
@@ -101,6 +105,30 @@ def test_permutation_chain(dsp):
     for i in range(G):
         cur = pi[cur]
         assert np.array_equal(tok[:, i], cur)
+
+
+@pytest.mark.parametrize("R", [81, 100, 128])
+def test_permutation_chain_row_blocks(dsp, R):
+    """Tokens confined to the first 256 of V = 4096: W1[x] = c e_x and
+    W2[k] = c e_pi(k) (bf16-exact, c = 8), so token_i = pi^(i+1)(first) for
+    every row; with six to eight 16-row blocks every step's tokens come from
+    the previous step's decoded keys of the same rows."""
+    rng = np.random.default_rng(R)
+    V, r, G, c = 4096, 256, 12, 8.0
+    pi = rng.permutation(r)
+    w1 = np.zeros((V, r), np.float32)
+    w1[np.arange(r), np.arange(r)] = c
+    w2 = np.zeros((r, V), np.float32)
+    w2[np.arange(r), pi] = c
+    base = rng.standard_normal((R, G, V)).astype(np.float32)
+    first = rng.integers(0, r, size=R).astype(np.int32)
+    tok, _ = dsp.markov_sample(dev(base), as_dtype(W.to_bf16_bits(w1), "bf16"),
+                               as_dtype(W.to_bf16_bits(w2), "bf16"), dev(first))
+    tok = tok.cpu().numpy()
+    cur = first.astype(np.int64)
+    for i in range(G):
+        cur = pi[cur]
+        assert np.array_equal(tok[:, i], cur), i
 
 
 def test_gumbel_frequencies_on_device(dsp):
