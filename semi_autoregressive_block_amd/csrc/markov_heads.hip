@@ -18,11 +18,10 @@
 // Work split:
 // * The hidden-state part of every map, h @ W_h^T for all R x gamma
 //   positions at once (it does not depend on the sampled tokens), is one
-//   bf16 MFMA contraction over d: v_mfma_f32_16x16x32_bf16 with both
-//   operands read straight from row-major memory as 16-byte pieces (lane
-//   (n, g) of a fragment holds row n, entries 8g .. 8g+7 of the 32-wide
-//   slab), 64 x 64 output tiles per workgroup, its four waves splitting
-//   the contraction.
+//   bf16 MFMA contraction over d: 128 x 128 output tiles, operands staged
+//   in LDS by direct-to-LDS copies, v_mfma_f32_32x32x16_bf16, and the
+//   contraction split over workgroups (partial tiles summed by the reader)
+//   so that a few hundred workgroups fill the chip.
 // * Per position, a small kernel finishes the maps with the recurrent inputs
 //   ([s; W1[x]], or W1[x] alone) in float32 (the state is never rounded),
 //   applies the nonlinearities, writes E (float32) and the next state.
@@ -37,82 +36,172 @@ namespace {
 
 constexpr int kHeadGated = 1;
 constexpr int kHeadRnn = 2;
-constexpr int kProjTile = 64;   // output rows and columns per projection workgroup
 constexpr int kRowsPer = 16;    // rows per recurrent-step workgroup
 constexpr int kChanPer = 8;     // channels per recurrent-step workgroup
 constexpr int kMaxRank = 512;
 
-// P[i][c] = sum_k A[i][k] B[c][k] for i < M, c < N (bf16 in, float32 out).
-// A rows are lda elements apart, B rows ldb; K, lda, ldb multiples of 8 and
-// both bases 16-byte aligned (checked by the host).  A workgroup owns a
-// 64 x 64 output tile; each of its four waves computes the whole tile (4 x 4
-// products) over every fourth 32-wide slab of K, interleaved so that the
-// waves stream neighbouring pieces of the same rows, with the next slab's
-// eight 16-byte pieces loaded while the current slab's products run.  The
-// four partial tiles are summed through LDS at the end.
-__global__ __launch_bounds__(256) void head_proj_mfma(const uint16_t* __restrict__ A, int64_t lda,
-                                                      const uint16_t* __restrict__ B, int64_t ldb,
-                                                      float* __restrict__ P, int64_t ldp, int M, int N, int K) {
-  __shared__ f32x4 red[3][16][64];  // partial tiles of waves 1..3
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int n = lane & 15, g = lane >> 4;
-  const int i0 = blockIdx.x * kProjTile, c0 = blockIdx.y * kProjTile;
-  const uint16_t* ap[4];
-  const uint16_t* bp[4];
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    ap[t] = A + (int64_t)min(i0 + 16 * t + n, M - 1) * lda;
-    bp[t] = B + (int64_t)min(c0 + 16 * t + n, N - 1) * ldb;
+// P_z[i][c] = sum_{k in split z} A[i][k] B[c][k] for i < M, c < N (bf16 in, float32 out): the
+// hidden-state part of the heads' maps.  A rows are lda elements apart, B rows ldb; K, lda, ldb
+// multiples of 8 and both bases 16-byte aligned (checked by the host).
+//
+// A workgroup of four waves owns a 128 x 128 output tile and one contiguous split of the
+// contraction (blockIdx.z; a second kernel sums the splits' partial tiles in fixed order, so
+// results do not depend on scheduling).  The contraction goes in 32-wide slabs through a
+// six-stage LDS ring filled by direct-to-LDS copies (five slabs, 80 KB, in flight: one workgroup
+// per compute unit, whose load rate is set by the bytes it keeps in flight): a stage holds the
+// tile's 128 A rows and 128 B rows, 64 bytes each, with the four 16-byte pieces of row x stored
+// at piece p ^ ((x >> 2) & 3), so that the 16 rows one read instruction touches per cycle fall
+// in distinct banks.  Wave (wm, wn) computes the 64 x 64 quarter at rows 64 wm, columns 64 wn as
+// 2 x 2 products v_mfma_f32_32x32x16_bf16 with B as the first operand, so lane l ends up holding
+// row l mod 32 of a product and columns 8q + 4(l / 32) .. +3: 16-byte stores.  The LDS reads are
+// inline assembly that waits for its own results, because the compiler would otherwise wait for
+// every copy in flight before each of them.
+constexpr int kGemmTile = 128;
+constexpr int kGemmSlab = 32;
+constexpr int kGemmStages = 6;
+constexpr int kGemmStageBytes = 2 * kGemmTile * kGemmSlab * 2;  // A and B pieces of one slab
+
+__device__ __forceinline__ void lds_read4_b128(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3, u32x4& x0,
+                                               u32x4& x1, u32x4& x2, u32x4& x3) {
+  asm volatile(
+      "ds_read_b128 %0, %4\n\tds_read_b128 %1, %5\n\tds_read_b128 %2, %6\n\tds_read_b128 %3, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(x0), "=&v"(x1), "=&v"(x2), "=&v"(x3)
+      : "v"(a0), "v"(a1), "v"(a2), "v"(a3)
+      : "memory");
+}
+
+__device__ __forceinline__ void wait_vmcnt_copies(int n) {  // n = copies allowed in flight (a multiple of 4)
+  switch (n) {
+    case 0: wait_vmcnt<0>(); break;
+    case 4: wait_vmcnt<4>(); break;
+    case 8: wait_vmcnt<8>(); break;
+    case 12: wait_vmcnt<12>(); break;
+    default: wait_vmcnt<16>(); break;
   }
-  f32x4 acc[4][4];
+}
+static_assert(4 * (kGemmStages - 2) <= 16, "copies in flight beyond the waits above");
+
+__global__ __launch_bounds__(256) void head_proj_gemm(const uint16_t* __restrict__ A, int64_t lda,
+                                                      const uint16_t* __restrict__ B, int64_t ldb,
+                                                      float* __restrict__ P, int64_t split_stride, int M, int N,
+                                                      int K, int kchunk) {
+  __shared__ __align__(16) unsigned char ring[kGemmStages * kGemmStageBytes];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave & 1, wn = wave >> 1;
+  const int i0 = blockIdx.x * kGemmTile, c0 = blockIdx.y * kGemmTile;
+  const int kb = blockIdx.z * kchunk, ke = min(K, kb + kchunk);
+  const int nst = (ke - kb + kGemmSlab - 1) / kGemmSlab;  // >= 1: the host launches no empty split
+
+  // copies: per stage 16 of 1 KB (A then B), 4 per wave; copy c, lane l -> LDS chunk 64 c + l of the
+  // stage = row (64 c + l) / 4 of A (c < 8) or B, stored piece (l & 3), which holds the row's piece
+  // (l & 3) ^ ((row >> 2) & 3)
+  const uint16_t* src[4];
+  int kpiece[4];
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int j = 0; j < 4; ++j) {
+    const int c = wave * 4 + j;  // 0 .. 15
+    const int x = ((c & 7) * 64 + lane) >> 2;
+    const int piece = (lane & 3) ^ ((x >> 2) & 3);
+    src[j] = c < 8 ? A + (int64_t)min(i0 + x, M - 1) * lda : B + (int64_t)min(c0 + x, N - 1) * ldb;
+    kpiece[j] = piece * 8;
+  }
+  auto issue = [&](int st) {
+    unsigned char* dst = ring + (st % kGemmStages) * kGemmStageBytes;
+    const int k = kb + st * kGemmSlab;
 #pragma unroll
-    for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-  u32x4 fa[4], fb[4];
-  auto load = [&](int slab) {
-    const int k = slab * 32 + 8 * g;
-    const bool ok = k < K;  // K is a multiple of 8: the whole piece is in the row
-    const int kc = ok ? k : 0;
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const u32x4 x = *(const u32x4*)(ap[t] + kc), y = *(const u32x4*)(bp[t] + kc);
-      fa[t] = ok ? x : u32x4{0u, 0u, 0u, 0u};
-      fb[t] = ok ? y : u32x4{0u, 0u, 0u, 0u};
+    for (int j = 0; j < 4; ++j) {
+      // a piece past the contraction end reads the row's first piece (valid memory); its products
+      // are dropped below by zeroing the operands
+      const int kk = k + kpiece[j] < ke ? k + kpiece[j] : 0;
+      __builtin_amdgcn_global_load_lds((const void*)(src[j] + kk),
+                                       (__attribute__((address_space(3))) void*)(dst + (wave * 4 + j) * 1024), 16,
+                                       0, 0);
     }
   };
-  const int nslab = (K + 31) / 32;
-  if (wave < nslab) load(wave);
-  for (int sl = wave; sl < nslab; sl += 4) {
-    u32x4 ca[4], cb[4];
+
+  f32x16 acc[2][2];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) { ca[t] = fa[t]; cb[t] = fb[t]; }
-    if (sl + 4 < nslab) load(sl + 4);
+  for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int b = 0; b < 2; ++b)
 #pragma unroll
-      for (int b = 0; b < 4; ++b) acc[a][b] = mfma16x16x32(cb[b], ca[a], acc[a][b]);
+      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+
+  // this lane's operand rows: A rows 64 wm + 32 a + (l & 31), B rows 64 wn + 32 b + (l & 31); the
+  // piece of k16 step t is 2 t + (l >> 5)
+  const uint32_t ring_lds = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)ring;
+  uint32_t roff[4];  // byte offsets of the four operand rows inside a stage
+  int rsw[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int x = (q < 2 ? 64 * wm + 32 * q : 64 * wn + 32 * (q - 2)) + (lane & 31);
+    roff[q] = (uint32_t)((q < 2 ? 0 : kGemmTile * 64) + x * 64);
+    rsw[q] = (x >> 2) & 3;
   }
-  if (wave > 0) {
+  const int h = lane >> 5;
+
+  const int pre = nst < kGemmStages - 1 ? nst : kGemmStages - 1;
+  for (int st = 0; st < pre; ++st) issue(st);
+  for (int st = 0; st < nst; ++st) {
+    const int ahead = min(nst - 1 - st, kGemmStages - 2);  // stages issued after this one
+    wait_vmcnt_copies(4 * ahead);
+    __builtin_amdgcn_s_barrier();  // every wave's copies of stage st are in; stage st - 1 is consumed
+    if (st + kGemmStages - 1 < nst) issue(st + kGemmStages - 1);
+    const uint32_t sbase = ring_lds + (st % kGemmStages) * kGemmStageBytes;
+    const int k = kb + st * kGemmSlab;
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-      for (int b = 0; b < 4; ++b) red[wave - 1][4 * a + b][lane] = acc[a][b];
-  }
-  __syncthreads();
-  if (wave > 0) return;
-  // lane (n, g) of product (a, b) holds row i0 + 16a + n, columns
-  // c0 + 16b + 4g .. +3 (N is a multiple of 4)
-#pragma unroll
-  for (int a = 0; a < 4; ++a) {
-    const int i = i0 + 16 * a + n;
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const f32x4 v = acc[a][b] + red[0][4 * a + b][lane] + red[1][4 * a + b][lane] + red[2][4 * a + b][lane];
-      const int c = c0 + 16 * b + 4 * g;
-      if (i < M && c < N) *(f32x4*)(P + (int64_t)i * ldp + c) = v;
+    for (int t = 0; t < 2; ++t) {
+      const int pc = 2 * t + h;  // this lane's piece in the slab
+      u32x4 fa0, fa1, fb0, fb1;
+      lds_read4_b128(sbase + roff[0] + ((pc ^ rsw[0]) << 4), sbase + roff[1] + ((pc ^ rsw[1]) << 4),
+                     sbase + roff[2] + ((pc ^ rsw[2]) << 4), sbase + roff[3] + ((pc ^ rsw[3]) << 4), fa0, fa1, fb0,
+                     fb1);
+      if (k + 8 * pc >= ke) fa0 = fa1 = fb0 = fb1 = u32x4{0u, 0u, 0u, 0u};
+      acc[0][0] = mfma32x32x16(fb0, fa0, acc[0][0]);
+      acc[0][1] = mfma32x32x16(fb1, fa0, acc[0][1]);
+      acc[1][0] = mfma32x32x16(fb0, fa1, acc[1][0]);
+      acc[1][1] = mfma32x32x16(fb1, fa1, acc[1][1]);
     }
   }
+
+  // lane l: row i0 + 64 wm + 32 a + (l & 31), columns c0 + 64 wn + 32 b + 8 q + 4 h .. +3 (N is a
+  // multiple of 8, so a group that starts inside the row ends inside it)
+  float* Pz = P + (int64_t)blockIdx.z * split_stride;
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    const int i = i0 + 64 * wm + 32 * a + (lane & 31);
+    if (i >= M) continue;
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int c = c0 + 64 * wn + 32 * b + 8 * q + 4 * h;
+        if (c < N)
+          *(f32x4*)(Pz + (int64_t)i * N + c) =
+              f32x4{acc[a][b][4 * q], acc[a][b][4 * q + 1], acc[a][b][4 * q + 2], acc[a][b][4 * q + 3]};
+      }
+  }
+}
+
+// P[i] = sum_z P_z[i] in split order, for the n = M x N entries (16-byte vectors; n is a
+// multiple of 8).
+__global__ __launch_bounds__(256) void proj_sum_splits(float* __restrict__ P, int nsplit, int64_t n) {
+  const int64_t v = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (v >= n) return;
+  f32x4 acc = *(const f32x4*)(P + v);
+  for (int z = 1; z < nsplit; ++z) acc += *(const f32x4*)(P + z * n + v);
+  *(f32x4*)(P + v) = acc;
+}
+
+// Splits of the contraction for an M x N projection: at most one workgroup per compute unit of
+// a 256-unit chip (the workgroup's LDS ring takes most of a unit), at most 8 splits.  Depends on
+// M and N only, so the workspace can be sized without the contraction length.
+int proj_splits(int M, int N) {
+  const int64_t tiles = (int64_t)((M + kGemmTile - 1) / kGemmTile) * ((N + kGemmTile - 1) / kGemmTile);
+  const int64_t sk = 256 / (tiles > 0 ? tiles : 1);
+  return (int)(sk < 1 ? 1 : (sk > 8 ? 8 : sk));
 }
 
 template <bool kBf16>
@@ -295,7 +384,7 @@ __global__ void fill_zero_f32(float* p, int64_t n) {
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
-// Workspace layout: keys | P [R*gamma, NQ*r] | E [R*gamma, r] | s ping-pong [2, R, r]
+// Workspace layout: keys | P [splits][R*gamma, NQ*r] | E [R*gamma, r] | s ping-pong [2, R, r]
 struct Layout {
   size_t keys, proj, emb, state, total;
 };
@@ -304,7 +393,7 @@ Layout layout(int kind, int R, int gamma, int r, int64_t nkeys) {
   Layout L;
   L.keys = 0;
   L.proj = align256((size_t)nkeys * 8);
-  L.emb = L.proj + align256((size_t)R * gamma * nq * r * 4);
+  L.emb = L.proj + align256((size_t)proj_splits(R * gamma, nq * r) * R * gamma * nq * r * 4);
   L.state = L.emb + align256((size_t)R * gamma * r * 4);
   L.total = L.state + (kind == kHeadRnn ? align256((size_t)2 * R * r * 4) : 0);
   return L;
@@ -350,8 +439,17 @@ hipError_t run_head(const HeadArgs& a, const int32_t* prev_tok, int64_t prev_str
   // h-part columns: gated [h; e] -> column 0; recurrent [s; e; h] -> column 2r.
   // The stacked recurrent maps are one [3r, 2r + d] matrix.
   const uint16_t* Bh = wh + (rnn ? 2 * a.r : 0);
-  hipLaunchKernelGGL(head_proj_mfma, dim3((M + kProjTile - 1) / kProjTile, (N + kProjTile - 1) / kProjTile),
-                     dim3(256), 0, s, (const uint16_t*)a.hidden, (int64_t)a.d, Bh, ldw, P, (int64_t)N, M, N, a.d);
+  // contraction splits: partial tiles split_stride apart, then summed into the first
+  const int sk_max = proj_splits(M, N);
+  const int kchunk = ((a.d + sk_max - 1) / sk_max + kGemmSlab - 1) / kGemmSlab * kGemmSlab;
+  const int nsplit = (a.d + kchunk - 1) / kchunk;  // <= sk_max, none empty
+  const int64_t split_stride = (int64_t)M * N;
+  hipLaunchKernelGGL(head_proj_gemm,
+                     dim3((M + kGemmTile - 1) / kGemmTile, (N + kGemmTile - 1) / kGemmTile, nsplit), dim3(256), 0,
+                     s, (const uint16_t*)a.hidden, (int64_t)a.d, Bh, ldw, P, split_stride, M, N, a.d, kchunk);
+  if (nsplit > 1)
+    hipLaunchKernelGGL(proj_sum_splits, dim3((unsigned)((split_stride / 4 + 255) / 256)), dim3(256), 0, s, P, nsplit,
+                       split_stride);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (rnn) {
