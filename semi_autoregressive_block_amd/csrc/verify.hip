@@ -58,7 +58,7 @@ __device__ __forceinline__ Soft soft_merge2(Soft a, Soft b) {
   return {m, a.s * exp2f(a.m - m) + b.s * exp2f(b.m - m)};
 }
 
-template <typename T, typename F>
+template <int NT = kThreads, typename T, typename F>
 __device__ __forceinline__ T block_reduce(T v, F op, T* lds) {
   for (int off = 32; off > 0; off >>= 1) {
     T o;
@@ -76,12 +76,35 @@ __device__ __forceinline__ T block_reduce(T v, F op, T* lds) {
   if (lane == 0) lds[w] = v;
   __syncthreads();
   v = lds[0];
-  for (int i = 1; i < kThreads / 64; ++i) v = op(v, lds[i]);
+  for (int i = 1; i < NT / 64; ++i) v = op(v, lds[i]);
   return v;
 }
 
 // Statistics of position k (blockIdx.x) of row blockIdx.y over the scaled
-// logits y = logits / T (T = 0: only the target's argmax).
+// logits y = logits / T (T = 0: only the target's argmax).  With 16-byte
+// rows (vec) each thread takes kBatch vectors of the target row and as many
+// of the draft row per step, all loads issued before any is used (a single
+// load in flight per thread left the stream latency-bound), then folds each
+// row's batch into its running (max, sum) with one rescale per batch and
+// one exponential per element.
+constexpr int kBatch = 8;
+__device__ __forceinline__ void soft_add_batch(Soft& a, const f32x4* y, float sc) {
+  float m = a.m;
+#pragma unroll
+  for (int b = 0; b < kBatch; ++b)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) m = fmaxf(m, y[b][e] * sc);
+  a.s *= exp2f(a.m - m);  // m >= a.m > -inf
+  a.m = m;
+  float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+  for (int b = 0; b < kBatch; ++b) {
+    s0 += exp2f(fmaf(y[b][0], sc, -m)) + exp2f(fmaf(y[b][1], sc, -m));
+    s1 += exp2f(fmaf(y[b][2], sc, -m)) + exp2f(fmaf(y[b][3], sc, -m));
+  }
+  a.s += s0 + s1;
+}
+
 __global__ __launch_bounds__(kThreads) void verify_stats_kernel(const float* __restrict__ draft,
                                                                 const float* __restrict__ target, int K, int V,
                                                                 float invT, int greedy, int vec,
@@ -90,42 +113,42 @@ __global__ __launch_bounds__(kThreads) void verify_stats_kernel(const float* __r
   __shared__ Soft ldss[kThreads / 64];
   const int k = blockIdx.x, row = blockIdx.y;
   const float* t = target + ((int64_t)row * (K + 1) + k) * V;
+  const bool with_d = !greedy && k < K;
+  const float* d = draft + ((int64_t)row * K + (k < K ? k : 0)) * V;
   constexpr float kLog2e = 1.4426950408889634f, kLn2 = 0.69314718055994531f;
   const float sc = invT * kLog2e;
-  Soft st{kSoftInit, 0.f};
+  Soft st{kSoftInit, 0.f}, sd{kSoftInit, 0.f};
   float bv = -INFINITY;  // this thread's first maximum (indices rise along its scan)
   uint32_t bi = 0xffffffffu;
-  // 16-byte loads when every row starts 16-byte aligned (vec: V % 4 == 0
-  // and both bases aligned, decided by the host)
   const int nv = vec ? V / 4 : 0;
-  for (int c = threadIdx.x; c < nv; c += kThreads) {
-    const f32x4 y = *(const f32x4*)(t + 4 * c);
+  const f32x4 none = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+  for (int c0 = threadIdx.x; c0 < nv; c0 += kThreads * kBatch) {
+    f32x4 yt[kBatch], yd[kBatch];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if (y[e] > bv) { bv = y[e]; bi = (uint32_t)(4 * c + e); }
-      if (!greedy) soft_add2(st, y[e] * sc);
+    for (int b = 0; b < kBatch; ++b) {
+      const int c = c0 + b * kThreads;
+      yt[b] = c < nv ? *(const f32x4*)(t + 4 * c) : none;
+      yd[b] = with_d && c < nv ? *(const f32x4*)(d + 4 * c) : none;
     }
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (yt[b][e] > bv) { bv = yt[b][e]; bi = (uint32_t)(4 * (c0 + b * kThreads) + e); }
+    if (!greedy) soft_add_batch(st, yt, sc);
+    if (with_d) soft_add_batch(sd, yd, sc);
   }
   for (int v = 4 * nv + threadIdx.x; v < V; v += kThreads) {
     const float y = t[v];
     if (y > bv) { bv = y; bi = (uint32_t)v; }
     if (!greedy) soft_add2(st, y * sc);
+    if (with_d) soft_add2(sd, d[v] * sc);
   }
   uint64_t best = bi == 0xffffffffu ? 0ull : argmax_key(bv, bi);
   best = block_reduce(best, [](uint64_t a, uint64_t b) { return a > b ? a : b; }, lds64);
   float* out = stats + ((int64_t)row * (K + 1) + k) * kStat;
   if (!greedy) st = block_reduce(st, soft_merge2, ldss);
-  Soft sd{kSoftInit, 0.f};
-  if (!greedy && k < K) {
-    const float* d = draft + ((int64_t)row * K + k) * V;
-    for (int c = threadIdx.x; c < nv; c += kThreads) {
-      const f32x4 y = *(const f32x4*)(d + 4 * c);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) soft_add2(sd, y[e] * sc);
-    }
-    for (int v = 4 * nv + threadIdx.x; v < V; v += kThreads) soft_add2(sd, d[v] * sc);
-    sd = block_reduce(sd, soft_merge2, ldss);
-  }
+  if (with_d) sd = block_reduce(sd, soft_merge2, ldss);
   st.m *= kLn2;
   sd.m *= kLn2;
   if (threadIdx.x == 0) {
@@ -170,7 +193,7 @@ __global__ void verify_decide_kernel(const float* __restrict__ draft, const floa
 // a draft was rejected there, from p at the position after the block.
 __global__ __launch_bounds__(kThreads) void verify_resample_kernel(
     const float* __restrict__ draft, const float* __restrict__ target, const float* __restrict__ stats,
-    const int32_t* __restrict__ pos_in, int K, int V, float invT, uint32_t slo, uint32_t shi,
+    const int32_t* __restrict__ pos_in, int K, int V, float invT, uint32_t slo, uint32_t shi, int vec,
     uint64_t* __restrict__ keys) {
   __shared__ uint64_t lds64[kThreads / 64];
   const int row = blockIdx.y, k = pos_in[row];
@@ -182,6 +205,19 @@ __global__ __launch_bounds__(kThreads) void verify_resample_kernel(
   const int64_t q0 = (int64_t)blockIdx.x * nq / gridDim.x, q1 = (int64_t)(blockIdx.x + 1) * nq / gridDim.x;
   uint64_t best = 0;
   for (int64_t q = q0 + threadIdx.x; q < q1; q += kThreads) {
+    // the quad's logits first (16-byte loads when rows are 16-byte aligned), then its noise
+    f32x4 tv, dv = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (vec) {
+      tv = *(const f32x4*)(t + 4 * q);
+      if (k < K) dv = *(const f32x4*)(d + 4 * q);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t v = min(4 * q + e, (int64_t)V - 1);
+        tv[e] = t[v];
+        if (k < K) dv[e] = d[v];
+      }
+    }
     const u32x4 w = philox4x32_10(u32x4{(uint32_t)q, (uint32_t)k, (uint32_t)row, 1u}, slo, shi);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -189,11 +225,11 @@ __global__ __launch_bounds__(kThreads) void verify_resample_kernel(
       if (v >= V) break;
       float z;
       if (k < K) {
-        const float p = expf(t[v] * invT - mt - ls_t), qd = expf(d[v] * invT - md - ls_d);
+        const float p = expf(tv[e] * invT - mt - ls_t), qd = expf(dv[e] * invT - md - ls_d);
         if (!(p > qd)) continue;
         z = logf(p - qd) + gumbel_from_bits(w[e]);
       } else {
-        z = t[v] * invT + gumbel_from_bits(w[e]);
+        z = tv[e] * invT + gumbel_from_bits(w[e]);
       }
       const uint64_t key = argmax_key(z, (uint32_t)v);
       best = key > best ? key : best;
@@ -261,7 +297,7 @@ extern "C" int dspark_verify(const float* draft_logits, const float* target_logi
     const int64_t nq = (V + 3) / 4;
     const int splits = (int)(nq < 64 * kThreads ? (nq + kThreads - 1) / kThreads : 64);
     hipLaunchKernelGGL(verify_resample_kernel, dim3(splits, R), dim3(kThreads), 0, s, draft_logits, target_logits,
-                       stats, pos, K, V, invT, slo, shi, keys);
+                       stats, pos, K, V, invT, slo, shi, vec, keys);
     hipLaunchKernelGGL(verify_finalize_kernel, dim3((R + 255) / 256), dim3(256), 0, s, keys, next_token, R, V,
                        dev_status);
   }
