@@ -730,6 +730,19 @@ extern "C" int dspark_markov_block_logits(const float* base_logits, const void* 
   const int cus = cu_count();
   if (cus <= 0) return fail(DSPARK_ERR_HIP, "markov_block_logits: device query failed");
   const bool bf = wdtype == DSPARK_BF16;
+  // bf16 weights: one launch over all rows with W2 held in registers (markov_round.hip)
+  if (bf && markov_rows_eligible(N, V, r, base_logits, w1, w2, logits)) {
+    const hipError_t e = markov_rows_launch(base_logits, (const uint16_t*)w1, (const uint16_t*)w2, prev, logits, N, V,
+                                            r, softcap, keys, dev_status, s);
+    if (e != hipSuccess && e != hipErrorNotSupported)
+      return fail(DSPARK_ERR_HIP, "markov_block_logits: %s", hipGetErrorString(e));
+    if (e == hipSuccess) {
+      if (argmax_tokens)
+        hipLaunchKernelGGL(finalize_tokens_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, s, keys,
+                           argmax_tokens, N, 1, V, dev_status);
+      return check_launch("markov_block_logits");
+    }
+  }
   const bool mfma_ok = bf && V % 8 == 0 && r % 8 == 0 && r <= 512 && (uintptr_t)w1 % 16 == 0 &&
                        (uintptr_t)w2 % 16 == 0 && (uintptr_t)base_logits % 16 == 0 &&
                        (uintptr_t)logits % 16 == 0;

@@ -132,6 +132,14 @@ __device__ __forceinline__ int lds_read_i32(uint32_t a0) {
   asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(x) : "v"(a0) : "memory");
   return x;
 }
+__device__ __forceinline__ uint64_t lds_read_u64(uint32_t a0) {
+  uint64_t x;
+  asm volatile("ds_read_b64 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(x) : "v"(a0) : "memory");
+  return x;
+}
+__device__ __forceinline__ void lds_write_u64(uint32_t a0, uint64_t x) {
+  asm volatile("ds_write_b64 %0, %1\n\ts_waitcnt lgkmcnt(0)" :: "v"(a0), "v"(x) : "memory");
+}
 __device__ __forceinline__ void lds_write_i32(uint32_t a0, int x) {
   asm volatile("ds_write_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" :: "v"(a0), "v"(x) : "memory");
 }
@@ -466,6 +474,255 @@ Capacity round_capacity(const void* kern) {
   return c;
 }
 
+
+// ---------------------------------------------------------------------------
+// Teacher-forced logits of N independent rows (page 2, "从 DFlash 到 dLLM
+// Self-Spec（三）", §3.4: every position of a training block takes the true
+// previous token): one Markov step per row, prev from the caller, logits
+// stored (optionally soft-capped, c tanh(l / c)) and each row's greedy argmax
+// folded into the key slots.  Same layout of the work as the round kernel:
+// W2 in registers (read once per launch), every workgroup streams all row
+// blocks of its vocabulary columns, base logits and E rows through three-slot
+// rings of direct-to-LDS copies.  There is no dependency between row blocks,
+// so no wait on other workgroups: an ordinary launch.  The E rows' tokens are
+// read with scalar loads (two per wave and block), whose waits do not hold
+// the copies in flight.
+struct RowsArgs {
+  const float* base;
+  const uint16_t* w1;
+  const uint16_t* w2;
+  const int32_t* prev;
+  float* logits;
+  uint64_t* keys;
+  int32_t* status;
+  int N, V, r;
+  float invc;  // 1 / softcap
+};
+
+template <bool kSoftcap>
+__global__ __launch_bounds__(kRT) __attribute__((amdgpu_waves_per_eu(2, 2))) void markov_rows_mfma(RowsArgs a) {
+  __shared__ __align__(16) unsigned char bring[kNS * kBSlot];  // base logits, three 16-row blocks
+  __shared__ __align__(16) unsigned char ering[kNS * kESlot];  // E rows, three 16-row blocks
+  __shared__ __align__(16) uint64_t rowkey[2 * 16];           // row keys of the last two blocks
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 15, g = lane >> 4;
+  const int N = a.N, V = a.V, r = a.r;
+  const int nrb = (N + 15) / 16;
+  const int ks = r / 32;
+  const int G = (int)gridDim.x;
+
+  const int NU = (V + 15) / 16;
+  const int U0 = (int)((int64_t)blockIdx.x * NU / G), U1 = (int)((int64_t)(blockIdx.x + 1) * NU / G);
+  const int nuw = U1 - U0;
+  const int ua = __builtin_amdgcn_readfirstlane(U0 + wave * nuw / kRW);
+  const int nu = __builtin_amdgcn_readfirstlane(U0 + (wave + 1) * nuw / kRW - ua);
+  const int pitch = 4 * nuw + 1;
+  const int npieces = nuw > 0 ? 16 * pitch : 0;
+  const int ninst = (npieces + 63) / 64;
+  const int my_inst = (ninst - wave + kRW - 1) / kRW;
+  uint32_t issued = 0;
+
+  // ---- W2 operands in registers, as in the round kernel
+  u32x4 A[kKU][kKS];
+  {
+    const int spc = 2 * nuw + 1;
+    const int spitch = spc * 16;
+    const int nwi = (32 * spc + 63) / 64;
+    const int my_w = nuw > 0 ? (nwi - wave + kRW - 1) / kRW : 0;
+    auto stage = [&](int kk) -> unsigned char* { return bring + (kk & 1) * (kNS * kBSlot / 2); };
+    auto issue_w2 = [&](int kk) {
+      unsigned char* dst = stage(kk);
+      for (int jj = 0; jj < my_w; ++jj) {
+        const int i = wave + jj * kRW;
+        const int p = i * 64 + lane;
+        if (p < 32 * spc) {
+          const int row = p / spc;
+          int q = p - row * spc;
+          q = q < 2 * nuw ? q : 2 * nuw - 1;
+          const int col = min(U0 * 16 + q * 8, V - 8);
+          __builtin_amdgcn_global_load_lds((const void*)(a.w2 + (int64_t)(32 * kk + row) * V + col),
+                                           (lds_void*)(dst + i * 1024), 16, 0, 0);
+        }
+      }
+      issued += my_w;
+    };
+    uint32_t done_at[2] = {0, 0};
+    issue_w2(0);
+    done_at[0] = issued;
+    if (ks > 1) {
+      issue_w2(1);
+      done_at[1] = issued;
+    }
+    const int ul = ua - U0;
+#pragma unroll
+    for (int kk = 0; kk < kKS; ++kk) {
+      if (kk < ks) {
+        wait_vmcnt_upto((int)(issued - done_at[kk & 1]));
+        block_barrier();
+        const unsigned char* stg = stage(kk);
+#pragma unroll
+        for (int u = 0; u < kKU; ++u) {
+          u32x4 v = u32x4{0u, 0u, 0u, 0u};
+          if (u < nu) {
+            const unsigned char* ap = stg + (8 * g + n / 4) * spitch + 8 * (n % 4) + 32 * (ul + u);
+            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)ap);
+            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(ap + 4 * spitch));
+            const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+            v = u32x4{l2.x, l2.y, h2.x, h2.y};
+          }
+          A[u][kk] = v;
+        }
+        __syncthreads();
+        if (kk + 2 < ks) {
+          issue_w2(kk + 2);
+          done_at[kk & 1] = issued;
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < kKU; ++u) A[u][kk] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  }
+
+  uint32_t last_b[kNS] = {0, 0, 0}, last_e[kNS] = {0, 0, 0};
+  const float inv_pitch = 1.0f / (float)pitch;
+  auto issue_base = [&](int rb, int slot) {
+    unsigned char* dst = bring + slot * kBSlot;
+    for (int j = 0; j < my_inst; ++j) {
+      const int i = wave + j * kRW;
+      int p = i * 64 + lane;
+      asm volatile("" : "+v"(p));
+      if (p < npieces) {
+        const int q = (int)(((float)p + 0.5f) * inv_pitch);
+        int c = p - q * pitch;
+        c = c < 4 * nuw ? c : 4 * nuw - 1;
+        const int row = min(rb * 16 + q, N - 1);
+        const int col = min(U0 * 16 + 4 * c, V - 4);
+        __builtin_amdgcn_global_load_lds((const void*)(a.base + (int64_t)row * V + col),
+                                         (lds_void*)(dst + i * 1024), 16, 0, 0);
+      }
+    }
+    issued += my_inst;
+    last_b[slot] = issued;
+  };
+  // E rows of block rb: copy `wave` covers block rows 2 wave and 2 wave + 1, whose tokens come in by
+  // scalar loads; lane l stores chunk l & 31 of its row, which holds W1 chunk (l & 31) ^ (row & 15)
+  typedef const __attribute__((address_space(4))) int32_t const_i32;
+  const const_i32* prev_c = (const const_i32*)a.prev;
+  const int ksc = r / 8;
+  auto issue_e = [&](int rb, int slot) {
+    const int r0 = min(rb * 16 + 2 * wave, N - 1), r1 = min(rb * 16 + 2 * wave + 1, N - 1);
+    int t0 = prev_c[r0], t1 = prev_c[r1];
+    if ((uint32_t)t0 >= (uint32_t)V || (uint32_t)t1 >= (uint32_t)V) {
+      if (blockIdx.x == 0 && lane == 0) status_or(a.status, DSPARK_STATUS_BAD_TOKEN);
+      t0 = (uint32_t)t0 < (uint32_t)V ? t0 : 0;
+      t1 = (uint32_t)t1 < (uint32_t)V ? t1 : 0;
+    }
+    const int q = 2 * wave + (lane >> 5);
+    const int tok = (lane >> 5) ? t1 : t0;
+    int c = (lane & 31) ^ q;
+    c = c < ksc ? c : c % ksc;
+    __builtin_amdgcn_global_load_lds((const void*)(a.w1 + (int64_t)tok * r + c * 8),
+                                     (lds_void*)(ering + slot * kESlot + wave * 1024), 16, 0, 0);
+    issued += 1;
+    last_e[slot] = issued;
+  };
+
+  if (threadIdx.x < 32) rowkey[threadIdx.x] = 0ull;
+  __syncthreads();
+  issue_base(0, 0);
+  issue_e(0, 0);
+  if (nrb > 1) {
+    issue_base(1, 1);
+    issue_e(1, 1);
+  }
+
+  const uint32_t key_lds = lds_off(rowkey);
+  const uint32_t bring_lds = lds_off(bring), ering_lds = lds_off(ering);
+  const int64_t rstr = replica_stride(N);
+  // the keys of block rb (final after the barrier that follows its products) -> device slots
+  auto flush = [&](int rb) {
+    if (wave == 0 && lane < 16) {
+      const uint32_t kr = key_lds + 8 * ((rb & 1) * 16 + lane);
+      const uint64_t key = lds_read_u64(kr);
+      lds_write_u64(kr, 0ull);
+      const int row = rb * 16 + lane;
+      if (row < N && key)
+        __hip_atomic_fetch_max(a.keys + (int64_t)(blockIdx.x % kKeyReplicas) * rstr + row, key, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    }
+  };
+  for (int rb = 0; rb < nrb; ++rb) {
+    const int sl = rb % kNS;
+    {
+      const uint32_t need = last_b[sl] > last_e[sl] ? last_b[sl] : last_e[sl];
+      wait_vmcnt_upto((int)(issued - need));
+    }
+    lds_wait_all();  // this wave's key folds of block rb - 1 have completed
+    block_barrier();
+    if (rb > 0) flush(rb - 1);
+    if (rb + 2 < nrb) {
+      issue_base(rb + 2, (rb + 2) % kNS);
+      issue_e(rb + 2, (rb + 2) % kNS);
+    }
+    if (nu > 0) {
+      const int row = rb * 16 + n;
+      const uint32_t erow = ering_lds + sl * kESlot + n * 512, swz = (uint32_t)n;
+      f32x4 acc[kKU];
+#pragma unroll
+      for (int u = 0; u < kKU; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < kKS; kk += 4) {
+        if (kk < ks) {
+          u32x4 e0, e1, e2, e3;
+          lds_read4(erow + (((4 * kk + g) ^ swz) << 4), erow + (((4 * kk + 4 + g) ^ swz) << 4),
+                    erow + (((4 * kk + 8 + g) ^ swz) << 4), erow + (((4 * kk + 12 + g) ^ swz) << 4), e0, e1, e2,
+                    e3);
+#pragma unroll
+          for (int u = 0; u < kKU; ++u) acc[u] = mfma16x16x32(A[u][kk], e0, acc[u]);
+#pragma unroll
+          for (int u = 0; u < kKU; ++u) acc[u] = mfma16x16x32(A[u][kk + 1], e1, acc[u]);
+#pragma unroll
+          for (int u = 0; u < kKU; ++u) acc[u] = mfma16x16x32(A[u][kk + 2], e2, acc[u]);
+#pragma unroll
+          for (int u = 0; u < kKU; ++u) acc[u] = mfma16x16x32(A[u][kk + 3], e3, acc[u]);
+        }
+      }
+      const uint32_t slb = bring_lds + sl * kBSlot + (n * pitch + 4 * (ua - U0) + g) * 16;
+      u32x4 bw[kKU];
+      lds_read5(slb, slb + (nu > 1 ? 64 : 0), slb + (nu > 2 ? 128 : 0), slb + (nu > 3 ? 192 : 0),
+                slb + (nu > 4 ? 256 : 0), bw[0], bw[1], bw[2], bw[3], bw[4]);
+      float bz = -INFINITY;
+      uint32_t bv = 0xffffffffu;
+#pragma unroll
+      for (int u = 0; u < kKU; ++u) {
+        if (u < nu) {
+          const int c0 = (ua + u) * 16 + 4 * g;
+          f32x4 l = acc[u] + __builtin_bit_cast(f32x4, bw[u]);
+          if constexpr (kSoftcap) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) l[e] = tanhf(l[e] * a.invc) / a.invc;
+          }
+          const bool ok = row < N && c0 < V;
+          if (ok) *(f32x4*)(a.logits + (int64_t)row * V + c0) = l;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const bool better = ok && l[e] > bz;
+            bz = better ? l[e] : bz;
+            bv = better ? (uint32_t)(c0 + e) : bv;
+          }
+        }
+      }
+      if (bv != 0xffffffffu) lds_max_u64_nowait(key_lds + 8 * ((rb & 1) * 16 + n), argmax_key(bz, bv));
+    }
+  }
+  lds_wait_all();
+  block_barrier();
+  if (nrb > 0) flush(nrb - 1);
+}
+
 }  // namespace
 
 namespace dspark {
@@ -492,6 +749,30 @@ hipError_t markov_round_launch(const float* base, const uint16_t* w1, const uint
                  spin_limit};
   void* params[] = {(void*)&args};
   return hipLaunchCooperativeKernel(kern, dim3((unsigned)G), dim3(kRT), params, 0, s);
+}
+
+
+bool markov_rows_eligible(int N, int V, int r, const void* base, const void* w1, const void* w2, const void* logits) {
+  if (N < 1 || r < 32 || r > 32 * kKS || r % 32 || V < 16 || V % 8) return false;
+  if (((uintptr_t)base | (uintptr_t)w1 | (uintptr_t)w2 | (uintptr_t)logits) % 16) return false;
+  return true;
+}
+
+hipError_t markov_rows_launch(const float* base, const uint16_t* w1, const uint16_t* w2, const int32_t* prev,
+                              float* logits, int N, int V, int r, float softcap, uint64_t* keys, int32_t* status,
+                              hipStream_t s) {
+  const Capacity cap =
+      round_capacity(softcap > 0.f ? (const void*)markov_rows_mfma<true> : (const void*)markov_rows_mfma<false>);
+  const int cus = cap.cus;
+  if (cus <= 0 || cap.per_cu < 1) return hipErrorNotSupported;
+  const int NU = (V + 15) / 16;
+  if (NU < cus || (NU + cus - 1) / cus > kMaxUnitsWG) return hipErrorNotSupported;
+  RowsArgs args{base, w1, w2, prev, logits, keys, status, N, V, r, softcap > 0.f ? 1.f / softcap : 1.f};
+  if (softcap > 0.f)
+    hipLaunchKernelGGL(markov_rows_mfma<true>, dim3((unsigned)cus), dim3(kRT), 0, s, args);
+  else
+    hipLaunchKernelGGL(markov_rows_mfma<false>, dim3((unsigned)cus), dim3(kRT), 0, s, args);
+  return hipGetLastError();
 }
 
 }  // namespace dspark

@@ -55,6 +55,14 @@ hipError_t markov_round_launch(const float* base, const uint16_t* w1, const uint
                                int32_t* tokens, float* step_logits, int R, int gamma, int V, int r, float invT,
                                int greedy, uint32_t slo, uint32_t shi, uint64_t* keys, uint32_t spin_limit,
                                int32_t* status, hipStream_t s);
+// Teacher-forced logits of N rows (one step each, prev from the caller) with W2 held in registers:
+// logits [N, V] (soft-capped when softcap > 0) and each row's argmax folded into the zeroed key
+// slots of keys_per_step(N).  Same shape limits as the round kernel (any N >= 1).
+// hipErrorNotSupported (nothing enqueued) when the shape or the device does not allow it.
+bool markov_rows_eligible(int N, int V, int r, const void* base, const void* w1, const void* w2, const void* logits);
+hipError_t markov_rows_launch(const float* base, const uint16_t* w1, const uint16_t* w2, const int32_t* prev,
+                              float* logits, int N, int V, int r, float softcap, uint64_t* keys, int32_t* status,
+                              hipStream_t s);
 // Poll limit of the bounded waits inside cooperative grids (dspark_set_wait_limit).
 uint32_t wait_limit();
 // tokens[row, step] = the argmax index folded in step's keys, for R x gamma.

@@ -58,6 +58,8 @@ def _check_tokens(tok, ref_logits):
     (200, 20000, 256, "bf16", 0.0),    # two 128-row groups, ragged vocabulary tail
     (200, 20000, 256, "bf16", 30.0),   # soft cap
     (45, 2048, 512, "bf16", 0.0),      # rank 512
+    (300, 8192, 128, "bf16", 0.0),     # W2 held in registers: 19 row blocks, the last ragged
+    (17, 16384, 96, "bf16", 12.0),     # the same with rank 96 (three rank steps) and a soft cap
     (19, 1001, 40, "bf16", 5.0),       # V not a multiple of 8: vector-ALU path, soft cap
     (23, 3000, 48, "f32", 0.0),        # float32 weights: vector-ALU path
 ])
@@ -97,6 +99,23 @@ def test_block_logits_bad_token_is_clamped_and_flagged(dsp):
     fixed[[3, 7]] = 0
     ref = OT.block_logits(base, W.values(w1, "bf16"), W.values(w2, "bf16"), fixed)
     assert np.abs(logits.cpu().numpy() - ref).max() < 2e-4
+
+
+def test_block_logits_bad_token_register_path(dsp):
+    """The W2-in-registers kernel (V / 16 >= compute units) clamps and flags bad tokens too."""
+    base, w1, w2, prev = _markov_inputs(11, 40, 8192, 64, "bf16")
+    prev[0] = -1
+    prev[33] = 8192
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    logits, tok = dsp.markov_block_logits(dev(base), as_dtype(w1, "bf16"), as_dtype(w2, "bf16"), dev(prev),
+                                          status=st, want_tokens=True)
+    from semi_autoregressive_block_amd import _lib
+    assert int(st.item()) & _lib.STATUS_BAD_TOKEN
+    fixed = prev.copy()
+    fixed[[0, 33]] = 0
+    ref = OT.block_logits(base, W.values(w1, "bf16"), W.values(w2, "bf16"), fixed)
+    assert np.abs(logits.cpu().numpy() - ref).max() < 2e-4
+    _check_tokens(tok.cpu().numpy(), ref)
 
 
 def _loss_inputs(seed, B, A, g, V, dtype):
