@@ -177,16 +177,18 @@ def test_head_workspaces_and_bad_arguments(lib):
     """Workspace sizes of the gated / recurrent heads and argument checks that
     return before any device work."""
     mod, L = lib
-    # keys | P [R*gamma, 3r] | E [R*gamma, r] | state [2, R, r], each 256-aligned
+    # keys | P [splits][R*gamma, 3r] | E [R*gamma, r] | state [2, R, r], each 256-aligned.  The
+    # projection's contraction is split so that at most 256 workgroups of 128x128 output tiles
+    # run, at most 8 splits: 2048 x 768 is 96 tiles -> 2 splits, 2048 x 256 is 32 -> 8, 64 x 64 is 1 -> 8.
     R, g, r = 128, 16, 256
     keys = g * L.dspark_markov_sample_workspace_bytes(R, 1, 151936, r, 1)
     assert L.dspark_markov_head_sample_workspace_bytes(mod.HEAD_RNN, R, g, 151936, r) == \
-        keys + R * g * 3 * r * 4 + R * g * r * 4 + 2 * R * r * 4
+        keys + 2 * R * g * 3 * r * 4 + R * g * r * 4 + 2 * R * r * 4
     assert L.dspark_markov_head_sample_workspace_bytes(mod.HEAD_GATED, R, g, 151936, r) == \
-        keys + R * g * r * 4 + R * g * r * 4
+        keys + 8 * R * g * r * 4 + R * g * r * 4
     assert L.dspark_markov_head_sample_workspace_bytes(7, R, g, 151936, r) == 0
     assert L.dspark_markov_head_block_logits_workspace_bytes(mod.HEAD_GATED, 4, 16, 1000, 64) == \
-        L.dspark_markov_block_logits_workspace_bytes(64, 1000, 64, 1) + 64 * 64 * 4 * 2
+        L.dspark_markov_block_logits_workspace_bytes(64, 1000, 64, 1) + 8 * 64 * 64 * 4 + 64 * 64 * 4
     null = None
     args = dict(kind=mod.HEAD_RNN, R=2, gamma=4, V=100, r=16, d=32, wdtype=1)
 
