@@ -363,9 +363,14 @@ int dspark_verify(const float* draft_logits, const float* target_logits, const i
  *   row_l1     [B, A, gamma] float32 (out, nullable)
  *   grad       [B, A, gamma, V] float32 (out, nullable: the backward pass is skipped)
  *   tau_greedy [B, A] float32 (out, nullable)
- * Limits: gamma <= 1024, decay > 0.  Workspace from dspark_l1_loss_workspace_bytes.
+ * Limits: gamma <= 1024, decay > 0.  Workspace from
+ * dspark_l1_loss_workspace_bytes(B, A, gamma, V, dtype) (0 for an invalid
+ * shape or dtype); its size depends on V and dtype because rows of 16-byte
+ * vectors are split over clusters of workgroups that keep per-slice records.
+ * A cooperative wait that exceeds dspark_set_wait_limit poisons the rows it
+ * served (NaN loss, distances and gradients) instead of hanging.
  * ---------------------------------------------------------------------- */
-size_t dspark_l1_loss_workspace_bytes(int B, int A, int gamma);
+size_t dspark_l1_loss_workspace_bytes(int B, int A, int gamma, int V, int dtype);
 int dspark_l1_loss(const void* draft_logits, const void* target_logits, const uint8_t* eval_mask,
                    float decay, float* loss, float* row_l1, float* grad, float* tau_greedy,
                    int B, int A, int gamma, int V, int dtype,

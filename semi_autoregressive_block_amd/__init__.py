@@ -425,8 +425,8 @@ def verify(draft_logits, target_logits, draft_tokens, *, temperature=1.0, seed=0
     return n_accepted, next_token
 
 
-def l1_loss_workspace_bytes(B, A, gamma) -> int:
-    return int(_LIB.dspark_l1_loss_workspace_bytes(B, A, gamma))
+def l1_loss_workspace_bytes(B, A, gamma, V, dtype=_lib.BF16) -> int:
+    return int(_LIB.dspark_l1_loss_workspace_bytes(B, A, gamma, V, dtype))
 
 
 def l1_loss(draft, target, *, eval_mask=None, decay=4.0, want_grad=False, want_rows=False,
@@ -458,7 +458,7 @@ def l1_loss(draft, target, *, eval_mask=None, decay=4.0, want_grad=False, want_r
         tau_greedy = torch.empty((B, A), dtype=torch.float32, device=dev)
     if tau_greedy is not None:
         _check(tau_greedy, "tau_greedy", torch.float32, dev, 2)
-    ws, wsb = _workspace(l1_loss_workspace_bytes(B, A, gamma), dev, workspace)
+    ws, wsb = _workspace(l1_loss_workspace_bytes(B, A, gamma, V, _dt(draft)), dev, workspace)
     rc = _LIB.dspark_l1_loss(_ptr(draft), _ptr(target), _ptr(eval_mask), float(decay), _ptr(loss), _ptr(row_l1),
                              _ptr(grad), _ptr(tau_greedy), B, A, gamma, V, _dt(draft), _ptr(ws), wsb, _stream(dev))
     if rc != 0:

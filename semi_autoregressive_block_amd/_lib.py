@@ -48,7 +48,7 @@ SIGNATURES = {
     "dspark_eval_mask": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _p, _p]),
     "dspark_markov_block_logits_workspace_bytes": (_sz, [_i, _i, _i, _i]),
     "dspark_markov_block_logits": (_i, [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _f, _p, _sz, _p, _p]),
-    "dspark_l1_loss_workspace_bytes": (_sz, [_i, _i, _i]),
+    "dspark_l1_loss_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
     "dspark_l1_loss": (_i, [_p, _p, _p, _f, _p, _p, _p, _p, _i, _i, _i, _i, _i, _p, _sz, _p]),
     "dspark_markov_head_sample_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
     "dspark_markov_head_sample": (_i, [_i, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _f, _u64,

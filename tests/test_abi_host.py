@@ -152,7 +152,17 @@ def test_block_logits_and_l1_loss_reject_bad_arguments(lib):
     assert L.dspark_l1_loss(p, p, NULL, 0.0, p, NULL, NULL, NULL, 1, 1, 1, 8, 1, p, 1 << 20, NULL) == mod.ERR_INVALID_ARG
     assert L.dspark_l1_loss(p, p, NULL, 4.0, NULL, NULL, NULL, NULL, 1, 1, 1, 8, 1, p, 1 << 20, NULL) == mod.ERR_INVALID_ARG
     assert L.dspark_l1_loss(p, p, NULL, 4.0, p, NULL, NULL, NULL, 1, 1, 1, 8, 1, p, 0, NULL) == mod.ERR_WORKSPACE
-    assert L.dspark_l1_loss_workspace_bytes(4, 512, 8) == 3 * 4 * 512 * 8 * 4
+    # rows that are not 16-byte vectors take the row-wise kernel: c | l1 | greedy only
+    rows = 4 * 512 * 8
+    assert L.dspark_l1_loss_workspace_bytes(4, 512, 8, 1001, 1) == 3 * rows * 4
+    # clusters of 50 slices of 3072 elements (151936 / 3072 = 49.5): records [rows][50] of 16 bytes,
+    # then statistics slots (2 x 50 x 16 bytes) and S slots (4 x 50 x 4 bytes) for at most
+    # 4096 // 50 = 81 resident clusters, each part 256-byte aligned, and one 256-byte error word
+    up = lambda x: (x + 255) // 256 * 256
+    assert L.dspark_l1_loss_workspace_bytes(4, 512, 8, 151936, 1) == \
+        3 * rows * 4 + rows * 50 * 16 + up(81 * 2 * 50 * 16) + up(81 * 4 * 50 * 4) + 256
+    assert L.dspark_l1_loss_workspace_bytes(4, 512, 8, 151936, 3) == 0   # unknown dtype
+    assert L.dspark_l1_loss_workspace_bytes(4, 512, 8, 0, 1) == 0
 
 
 def test_confidence_schedule_rejects_bad_arguments(lib):

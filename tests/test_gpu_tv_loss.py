@@ -7,7 +7,9 @@ tighter below); argmax tokens exact wherever the oracle's top-2 margin
 exceeds 1e-3; loss and per-row L1 distances within 1e-4 (float32 softmaxes);
 gradients within 1e-4 of the row's largest gradient magnitude, except at
 elements whose p and q agree to 1e-5 relative (there the sign of p - q, and
-so the subgradient, may differ between float32 and float64); tau_greedy
+so the subgradient, may differ between float32 and float64), plus the slack
+those ties leave on S = sum s p (c p times 2 sum_ties p, and 1e-5 for
+S's float32 summation); tau_greedy
 exact (ties between equal logits go to the lowest index on both sides)."""
 
 import math
@@ -136,19 +138,29 @@ def _loss_inputs(seed, B, A, g, V, dtype):
     return d, t, m
 
 
-def _check_grad(g, d, t, ref):
+def _check_grad(g, d, t, m, ref, decay=4.0):
+    """Gradient within 1e-4 of the row's largest magnitude, except at near
+    ties of p and q (1e-5 relative), whose sign float32 cannot resolve.  The
+    same ties enter S = sum_u s_u p_u with either sign, so S is known only to
+    within 2 sum_ties p, and each element's c p (s - S) to within c p times
+    that; the bar includes this slack, and 1e-5 more for S as a float32 sum
+    (it matters where s - S vanishes, e.g. every s = +1 on the support, so
+    that the exact gradient and the row's scale are zero)."""
     p, q = OR.softmax(d), OR.softmax(t)
     tie = np.abs(p - q) <= 1e-5 * np.maximum(p, q)
+    c = OT.row_coefficients(m, decay)[..., None]
+    s_slack = 2.0 * np.where(tie, p, 0.0).sum(axis=-1, keepdims=True)
     scale = np.abs(ref).max(axis=-1, keepdims=True)
-    bad = (np.abs(g - ref) > 1e-4 * scale + 1e-12) & ~tie
+    bad = (np.abs(g - ref) > 1e-4 * scale + c * p * (s_slack + 1e-5) + 1e-12) & ~tie
     assert not bad.any(), (int(bad.sum()), np.abs(g - ref)[bad].max())
 
 
 @pytest.mark.parametrize("B,A,g,V,dtype", [
-    (2, 3, 4, 1000, "bf16"),     # V not a multiple of 8: element-wise path
-    (2, 3, 4, 4096, "bf16"),     # 16-byte vectors
+    (2, 3, 4, 1001, "bf16"),     # V not a multiple of 8: row-wise kernel, element loads
+    (2, 3, 4, 1000, "bf16"),     # cluster kernel with one (ragged) slice per row
+    (2, 3, 4, 4096, "bf16"),     # two slices per row
     (1, 5, 8, 3000, "f32"),
-    (1, 2, 3, 7, "f32"),         # tiny vocabulary
+    (1, 2, 3, 7, "f32"),         # tiny vocabulary, row-wise kernel
 ])
 def test_l1_loss_small(dsp, B, A, g, V, dtype):
     d, t, m = _loss_inputs(B * 100 + V, B, A, g, V, dtype)
@@ -158,7 +170,7 @@ def test_l1_loss_small(dsp, B, A, g, V, dtype):
     assert abs(loss.item() - OT.l1_loss(dv, tv, m)) < 1e-5
     assert np.abs(rows.cpu().numpy() - OT.l1_distance(dv, tv)).max() < 1e-5
     np.testing.assert_array_equal(tau.cpu().numpy(), OT.tau_greedy(dv, tv, m))
-    _check_grad(grad.cpu().numpy(), dv, tv, OT.l1_loss_grad(dv, tv, m))
+    _check_grad(grad.cpu().numpy(), dv, tv, m, OT.l1_loss_grad(dv, tv, m))
 
 
 def test_l1_loss_full_vocabulary(dsp):
@@ -170,7 +182,72 @@ def test_l1_loss_full_vocabulary(dsp):
     assert abs(loss.item() - OT.l1_loss(dv, tv, m)) < 1e-5
     assert np.abs(rows.cpu().numpy() - OT.l1_distance(dv, tv)).max() < 1e-5
     np.testing.assert_array_equal(tau.cpu().numpy(), OT.tau_greedy(dv, tv, m))
-    _check_grad(grad.cpu().numpy(), dv, tv, OT.l1_loss_grad(dv, tv, m))
+    _check_grad(grad.cpu().numpy(), dv, tv, m, OT.l1_loss_grad(dv, tv, m))
+
+
+@pytest.mark.parametrize("B,A,g,V,dtype,want_grad", [
+    (4, 16, 8, 20000, "bf16", True),    # 7 slices, the last ragged; several rows per cluster
+    (4, 16, 8, 20000, "bf16", False),   # no gradient: the pipeline without the S exchange
+    (2, 16, 8, 10000, "f32", True),     # float32: 4 slices, the last ragged
+    (1, 16, 8, 151936, "bf16", True),   # full vocabulary, 50 slices, ~8 rows per cluster
+])
+def test_l1_loss_cluster_pipeline(dsp, B, A, g, V, dtype, want_grad):
+    """Every row of a launch whose clusters each run several rows through the
+    three-stage pipeline (statistics, L1/S shares, gradient) against the oracle."""
+    d, t, m = _loss_inputs(B * 1000 + V + int(want_grad), B, A, g, V, dtype)
+    dv, tv = W.values(d, dtype), W.values(t, dtype)
+    loss, grad, rows, tau = dsp.l1_loss(as_dtype(d, dtype), as_dtype(t, dtype), eval_mask=dev(m),
+                                        want_grad=want_grad, want_rows=True, want_tau_greedy=True)
+    assert abs(loss.item() - OT.l1_loss(dv, tv, m)) < 1e-5
+    assert np.abs(rows.cpu().numpy() - OT.l1_distance(dv, tv)).max() < 1e-5
+    np.testing.assert_array_equal(tau.cpu().numpy(), OT.tau_greedy(dv, tv, m))
+    if want_grad:
+        _check_grad(grad.cpu().numpy(), dv, tv, m, OT.l1_loss_grad(dv, tv, m))
+    else:
+        assert grad is None
+
+
+def test_l1_loss_masked_vocabulary(dsp):
+    """-inf logits: a padded vocabulary tail in both tensors (p = q = 0, sign 0),
+    tokens masked in one tensor only, and a slice that is -inf throughout."""
+    B, A, g, V = 2, 8, 8, 16384
+    d, t, m = _loss_inputs(77, B, A, g, V, "f32")
+    d[..., 15000:] = -np.inf
+    t[..., 15000:] = -np.inf
+    d[..., 3072:6144] = -np.inf          # the whole second slice of the draft
+    t[..., 100:200] = -np.inf            # the target only
+    d[0, 1, 2, 0] = -np.inf              # index 0
+    db, tb = W.to_bf16_bits(d), W.to_bf16_bits(t)
+    dv, tv = W.values(db, "bf16"), W.values(tb, "bf16")
+    loss, grad, rows, tau = dsp.l1_loss(as_dtype(db, "bf16"), as_dtype(tb, "bf16"), eval_mask=dev(m),
+                                        want_grad=True, want_rows=True, want_tau_greedy=True)
+    assert abs(loss.item() - OT.l1_loss(dv, tv, m)) < 1e-5
+    assert np.abs(rows.cpu().numpy() - OT.l1_distance(dv, tv)).max() < 1e-5
+    np.testing.assert_array_equal(tau.cpu().numpy(), OT.tau_greedy(dv, tv, m))
+    gh = grad.cpu().numpy()
+    assert np.isfinite(gh).all()
+    assert not gh[..., 15000:].any()
+    _check_grad(gh, dv, tv, m, OT.l1_loss_grad(dv, tv, m))
+
+
+def test_l1_loss_wait_timeout_poisons_and_recovers(dsp):
+    """A poll limit of one, set from the host, drives the bounded waits of the
+    cluster kernel into their timeout path while every workgroup still exits
+    normally: the rows a timed-out workgroup served read NaN.  The next call at
+    the default limit matches the oracle again."""
+    d, t, m = _loss_inputs(12, 2, 16, 8, 151936, "bf16")
+    db, tb = as_dtype(d, "bf16"), as_dtype(t, "bf16")
+    dsp.set_wait_limit(1)
+    try:
+        loss, _, rows, _ = dsp.l1_loss(db, tb, eval_mask=dev(m), want_grad=True, want_rows=True)
+        torch.cuda.synchronize()
+    finally:
+        dsp.set_wait_limit(0)
+    assert np.isnan(rows.cpu().numpy()).any()
+    loss, _, rows, _ = dsp.l1_loss(db, tb, eval_mask=dev(m), want_grad=True, want_rows=True)
+    dv, tv = W.values(d, "bf16"), W.values(t, "bf16")
+    assert np.abs(rows.cpu().numpy() - OT.l1_distance(dv, tv)).max() < 1e-5
+    assert abs(loss.item() - OT.l1_loss(dv, tv, m)) < 1e-5
 
 
 def test_l1_loss_no_mask_and_all_masked(dsp):
