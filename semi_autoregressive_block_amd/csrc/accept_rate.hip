@@ -47,7 +47,6 @@ constexpr int kVec = 4;                           // 16-byte vectors per data th
                                                   // slice of both tensors; three workgroups per CU)
 constexpr int kChunkVec = kDataThreads * kVec;    // vectors of one tensor per workgroup and row
 constexpr int kMaxG = 2 * kWave;                  // two cluster members per exchange lane
-static_assert(kThreads == kClusterThreads, "the capacity query assumes four-wave workgroups");
 
 
 // bf16 (or float32) vector of the raw slice -> float32 values; lanes whose
@@ -509,7 +508,7 @@ extern "C" int dspark_accept_rate(const void* draft_logits, const void* target_l
   const void* kern = bf ? (const void*)tv_cluster_kernel<true> : (const void*)tv_cluster_kernel<false>;
   int64_t ncl = 0;
   if (geo.G > 0 && aligned) {
-    const int cap = cluster_capacity(kern, "accept_rate");
+    const int cap = cluster_capacity(kern, kThreads, "accept_rate");
     if (cap <= 0) return fail(DSPARK_ERR_HIP, "accept_rate: occupancy query failed");
     ncl = cap / geo.G;
     const int64_t bound = max_clusters(rows, geo.G);

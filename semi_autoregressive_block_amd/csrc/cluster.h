@@ -110,28 +110,28 @@ __device__ __forceinline__ uint32_t peek32(const uint32_t* slot) {
 }
 
 // ---- host side
-constexpr int kClusterThreads = 256;   // four waves: one on each SIMD of a compute unit
 constexpr int kLdsBytesPerCU = 160 * 1024;
 
-// Co-resident workgroups of a cluster `kernel` (kClusterThreads threads) on
-// the current device, cached per (device, kernel): the occupancy query is far
-// slower than a launch.  The runtime's figure is capped by what the kernel's
-// registers and LDS allow (each workgroup puts one wave on each of the four
-// SIMDs; 512 VGPRs per SIMD lane, allocated in blocks of 8), so a cluster
-// never waits on a member that the hardware could not place.  -1 on a failed
-// query.
-inline int cluster_capacity(const void* kernel, const char* who) {
+// Co-resident workgroups of a cluster `kernel` launched with `threads`
+// threads per workgroup on the current device, cached per (device, kernel):
+// the occupancy query is far slower than a launch.  The runtime's figure is
+// capped by what the kernel's registers and LDS allow (four SIMDs of at most
+// eight waves and 512 VGPRs per lane, allocated in blocks of 8; a
+// workgroup's waves take any free slots), so a cluster never waits on a
+// member that the hardware could not place.  -1 on a failed query.
+inline int cluster_capacity(const void* kernel, int threads, const char* who) {
   static KeyedCache<int> cache;
   int dev = 0, have = 0;
   if (hipGetDevice(&dev) != hipSuccess) return -1;
   if (cache.find(dev, kernel, have)) return have;
   int cus = 0, per = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, kClusterThreads, 0) != hipSuccess) return -1;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, threads, 0) != hipSuccess) return -1;
   hipFuncAttributes attr{};
   if (hipFuncGetAttributes(&attr, kernel) != hipSuccess) return -1;
+  const int waves = (threads + kWave - 1) / kWave;
   const int vgprs = ((attr.numRegs > 0 ? attr.numRegs : 1) + 7) / 8 * 8;
-  const int by_regs = std::min(8, 512 / vgprs);
+  const int by_regs = 4 * std::min(8, 512 / vgprs) / waves;
   const int by_lds = attr.sharedSizeBytes > 0 ? kLdsBytesPerCU / (int)attr.sharedSizeBytes : 8;
   per = std::min(per, std::min(by_regs, by_lds));
   if (getenv("DSPARK_VERBOSE"))

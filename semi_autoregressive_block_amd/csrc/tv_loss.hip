@@ -200,7 +200,6 @@ constexpr int kCN = 16;                           // elements of each tensor per
 constexpr int kChunkEl = kCDataThreads * kCN;     // slice length, both dtypes
 constexpr int kCMaxG = 2 * kWave;                 // two cluster members per exchange lane
 constexpr uint32_t kSCopies = 4;                  // rotating slots of the S exchange
-static_assert(kCThreads == cluster::kClusterThreads, "the capacity query assumes four-wave workgroups");
 static_assert(kChunkEl < 65536, "slice indices are packed as 16-bit fields");
 
 template <bool kBf16>
@@ -700,7 +699,7 @@ extern "C" int dspark_l1_loss(const void* draft_logits, const void* target_logit
   if (vec && geo.G > 0 && (uintptr_t)grad % 16 == 0) {
     ckern = bf ? (grad ? (const void*)l1_cluster_kernel<true, true> : (const void*)l1_cluster_kernel<true, false>)
                : (grad ? (const void*)l1_cluster_kernel<false, true> : (const void*)l1_cluster_kernel<false, false>);
-    const int cap = cluster::cluster_capacity(ckern, "l1_loss");
+    const int cap = cluster::cluster_capacity(ckern, kCThreads, "l1_loss");
     if (cap <= 0) return fail(DSPARK_ERR_HIP, "l1_loss: occupancy query failed");
     ncl = std::min<int64_t>(cap / geo.G, max_clusters(rows, geo.G));
   }
