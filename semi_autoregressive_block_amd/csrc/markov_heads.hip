@@ -46,20 +46,25 @@ constexpr int kMaxRank = 512;
 //
 // A workgroup of four waves owns a 128 x 128 output tile and one contiguous split of the
 // contraction (blockIdx.z; a second kernel sums the splits' partial tiles in fixed order, so
-// results do not depend on scheduling).  The contraction goes in 32-wide slabs through a
-// six-stage LDS ring filled by direct-to-LDS copies (five slabs, 80 KB, in flight: one workgroup
-// per compute unit, whose load rate is set by the bytes it keeps in flight): a stage holds the
-// tile's 128 A rows and 128 B rows, 64 bytes each, with the four 16-byte pieces of row x stored
-// at piece p ^ ((x >> 2) & 3), so that the 16 rows one read instruction touches per cycle fall
-// in distinct banks.  Wave (wm, wn) computes the 64 x 64 quarter at rows 64 wm, columns 64 wn as
+// results do not depend on scheduling).  The contraction goes in 64-wide slabs through a
+// four-stage LDS ring filled by direct-to-LDS copies (three slabs, 96 KB, in flight; one
+// workgroup per compute unit): a stage holds the tile's 128 A rows and 128 B rows, 128 bytes
+// each, so every copy instruction fetches whole 128-byte lines, with the eight 16-byte pieces of
+// row x stored at piece p ^ (x & 7), so that the 8 rows one read instruction touches per cycle
+// fall in distinct banks.  Wave (wm, wn) computes the 64 x 64 quarter at rows 64 wm, columns 64 wn as
 // 2 x 2 products v_mfma_f32_32x32x16_bf16 with B as the first operand, so lane l ends up holding
 // row l mod 32 of a product and columns 8q + 4(l / 32) .. +3: 16-byte stores.  The LDS reads are
 // inline assembly that waits for its own results, because the compiler would otherwise wait for
 // every copy in flight before each of them.
 constexpr int kGemmTile = 128;
-constexpr int kGemmSlab = 32;
-constexpr int kGemmStages = 6;
-constexpr int kGemmStageBytes = 2 * kGemmTile * kGemmSlab * 2;  // A and B pieces of one slab
+constexpr int kGemmSlab = 64;
+constexpr int kGemmStages = 4;
+constexpr int kGemmPieces = kGemmSlab / 8;                  // 16-byte pieces of a row per slab
+constexpr int kGemmRowBytes = kGemmSlab * 2;
+constexpr int kGemmStageBytes = 2 * kGemmTile * kGemmRowBytes;  // A and B pieces of one slab
+constexpr int kGemmCopies = kGemmStageBytes / 1024;             // 1 KB copies per stage
+constexpr int kGemmCopiesPerWave = kGemmCopies / 4;
+static_assert(kGemmPieces == 8, "the bank swizzle below assumes 128-byte rows");
 
 __device__ __forceinline__ void lds_read4_b128(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3, u32x4& x0,
                                                u32x4& x1, u32x4& x2, u32x4& x3) {
@@ -80,7 +85,8 @@ __device__ __forceinline__ void wait_vmcnt_copies(int n) {  // n = copies allowe
     default: wait_vmcnt<16>(); break;
   }
 }
-static_assert(4 * (kGemmStages - 2) <= 16, "copies in flight beyond the waits above");
+static_assert(kGemmCopiesPerWave * (kGemmStages - 2) <= 16 && kGemmCopiesPerWave % 4 == 0,
+              "copies in flight beyond the waits above");
 
 __global__ __launch_bounds__(256) void head_proj_gemm(const uint16_t* __restrict__ A, int64_t lda,
                                                       const uint16_t* __restrict__ B, int64_t ldb,
@@ -94,30 +100,31 @@ __global__ __launch_bounds__(256) void head_proj_gemm(const uint16_t* __restrict
   const int kb = blockIdx.z * kchunk, ke = min(K, kb + kchunk);
   const int nst = (ke - kb + kGemmSlab - 1) / kGemmSlab;  // >= 1: the host launches no empty split
 
-  // copies: per stage 16 of 1 KB (A then B), 4 per wave; copy c, lane l -> LDS chunk 64 c + l of the
-  // stage = row (64 c + l) / 4 of A (c < 8) or B, stored piece (l & 3), which holds the row's piece
-  // (l & 3) ^ ((row >> 2) & 3)
-  const uint16_t* src[4];
-  int kpiece[4];
+  // copies: per stage 32 of 1 KB (A then B), 8 per wave; copy c, lane l -> LDS chunk 64 c + l of the
+  // stage = row (64 c + l) / 8 of A (c < 16) or B, stored piece (l & 7), which holds the row's piece
+  // (l & 7) ^ (row & 7)
+  constexpr int kHalf = kGemmCopies / 2;
+  const uint16_t* src[kGemmCopiesPerWave];
+  int kpiece[kGemmCopiesPerWave];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int c = wave * 4 + j;  // 0 .. 15
-    const int x = ((c & 7) * 64 + lane) >> 2;
-    const int piece = (lane & 3) ^ ((x >> 2) & 3);
-    src[j] = c < 8 ? A + (int64_t)min(i0 + x, M - 1) * lda : B + (int64_t)min(c0 + x, N - 1) * ldb;
+  for (int j = 0; j < kGemmCopiesPerWave; ++j) {
+    const int c = wave * kGemmCopiesPerWave + j;  // 0 .. 31
+    const int x = ((c % kHalf) * 64 + lane) / kGemmPieces;
+    const int piece = (lane % kGemmPieces) ^ (x & 7);
+    src[j] = c < kHalf ? A + (int64_t)min(i0 + x, M - 1) * lda : B + (int64_t)min(c0 + x, N - 1) * ldb;
     kpiece[j] = piece * 8;
   }
   auto issue = [&](int st) {
     unsigned char* dst = ring + (st % kGemmStages) * kGemmStageBytes;
     const int k = kb + st * kGemmSlab;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < kGemmCopiesPerWave; ++j) {
       // a piece past the contraction end reads the row's first piece (valid memory); its products
       // are dropped below by zeroing the operands
       const int kk = k + kpiece[j] < ke ? k + kpiece[j] : 0;
-      __builtin_amdgcn_global_load_lds((const void*)(src[j] + kk),
-                                       (__attribute__((address_space(3))) void*)(dst + (wave * 4 + j) * 1024), 16,
-                                       0, 0);
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(src[j] + kk),
+          (__attribute__((address_space(3))) void*)(dst + (wave * kGemmCopiesPerWave + j) * 1024), 16, 0, 0);
     }
   };
 
@@ -137,8 +144,8 @@ __global__ __launch_bounds__(256) void head_proj_gemm(const uint16_t* __restrict
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int x = (q < 2 ? 64 * wm + 32 * q : 64 * wn + 32 * (q - 2)) + (lane & 31);
-    roff[q] = (uint32_t)((q < 2 ? 0 : kGemmTile * 64) + x * 64);
-    rsw[q] = (x >> 2) & 3;
+    roff[q] = (uint32_t)((q < 2 ? 0 : kGemmTile * kGemmRowBytes) + x * kGemmRowBytes);
+    rsw[q] = x & 7;
   }
   const int h = lane >> 5;
 
@@ -146,13 +153,13 @@ __global__ __launch_bounds__(256) void head_proj_gemm(const uint16_t* __restrict
   for (int st = 0; st < pre; ++st) issue(st);
   for (int st = 0; st < nst; ++st) {
     const int ahead = min(nst - 1 - st, kGemmStages - 2);  // stages issued after this one
-    wait_vmcnt_copies(4 * ahead);
+    wait_vmcnt_copies(kGemmCopiesPerWave * ahead);
     __builtin_amdgcn_s_barrier();  // every wave's copies of stage st are in; stage st - 1 is consumed
     if (st + kGemmStages - 1 < nst) issue(st + kGemmStages - 1);
     const uint32_t sbase = ring_lds + (st % kGemmStages) * kGemmStageBytes;
     const int k = kb + st * kGemmSlab;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int t = 0; t < kGemmSlab / 16; ++t) {
       const int pc = 2 * t + h;  // this lane's piece in the slab
       u32x4 fa0, fa1, fb0, fb1;
       lds_read4_b128(sbase + roff[0] + ((pc ^ rsw[0]) << 4), sbase + roff[1] + ((pc ^ rsw[1]) << 4),
