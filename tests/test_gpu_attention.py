@@ -77,6 +77,19 @@ def test_bf16_cases(dsp, case):
     _compare(_run(dsp, c), _ref(c), TOL["bf16"])
 
 
+@pytest.mark.parametrize("D,Hq,Hkv", [(128, 8, 2), (64, 4, 4)])
+def test_streaming_tiles_long_contexts(dsp, D, Hq, Hkv):
+    """Streaming tiles (one 16-position block per request) over contexts of
+    130 to 8193 keys: odd numbers of 32-key slabs and of slab pairs, a long
+    request with keep = 0, and anchors inside and at the end of the context."""
+    ctx = [4096, 4097, 4200, 6001, 8193, 130, 7000, 5000]
+    anchor = np.array([[4096], [4097], [4200], [3000], [8193], [130], [6999], [5000]], dtype=np.int32)
+    keep = np.ones((len(ctx), 1), dtype=np.uint8)
+    keep[7, 0] = 0
+    c = W.attention_case(31 + D, ctx, 1, 16, Hq, Hkv, D, "bf16", anchor=anchor, keep=keep)
+    _compare(_run(dsp, c), _ref(c), TOL["bf16"])
+
+
 def test_fp32_vector_path_multichunk(dsp):
     c = W.attention_case(21, [1200, 50], 3, 8, 4, 2, 64, "f32")
     _compare(_run(dsp, c), _ref(c), TOL["f32"])
