@@ -44,6 +44,7 @@ struct Soft {
 // -FLT_MAX, not -inf, so a masked logit (-inf) adds 2^-inf = 0 even before
 // the first finite one (-inf - -inf would be NaN), at no extra instruction.
 constexpr float kSoftInit = -3.402823466e38f;
+constexpr float kLog2eF = 1.4426950408889634f, kLn2F = 0.69314718055994531f;
 __device__ __forceinline__ void soft_add2(Soft& a, float y) {
   if (y > a.m) {
     a.s = a.s * exp2f(a.m - y) + 1.f;
@@ -199,6 +200,8 @@ __global__ __launch_bounds__(kThreads) void verify_resample_kernel(
   const int row = blockIdx.y, k = pos_in[row];
   const float* s = stats + ((int64_t)row * (K + 1) + k) * kStat;
   const float mt = s[0], ls_t = logf(s[1]), md = s[2], ls_d = k < K ? logf(s[3]) : 0.f;
+  // p = exp(x invT - mt - ls_t) as 2^(x invT log2e - (mt + ls_t) log2e): one fma and one v_exp_f32
+  const float cs = invT * kLog2eF, ot = (mt + ls_t) * kLog2eF, od = (md + ls_d) * kLog2eF;
   const float* t = target + ((int64_t)row * (K + 1) + k) * V;
   const float* d = draft + ((int64_t)row * K + (k < K ? k : 0)) * V;
   const int64_t nq = (V + 3) / 4;
@@ -225,9 +228,10 @@ __global__ __launch_bounds__(kThreads) void verify_resample_kernel(
       if (v >= V) break;
       float z;
       if (k < K) {
-        const float p = expf(tv[e] * invT - mt - ls_t), qd = expf(dv[e] * invT - md - ls_d);
+        const float p = __builtin_amdgcn_exp2f(fmaf(tv[e], cs, -ot));
+        const float qd = __builtin_amdgcn_exp2f(fmaf(dv[e], cs, -od));
         if (!(p > qd)) continue;
-        z = logf(p - qd) + gumbel_from_bits(w[e]);
+        z = kLn2F * __builtin_amdgcn_logf(p - qd) + gumbel_from_bits(w[e]);
       } else {
         z = tv[e] * invT + gumbel_from_bits(w[e]);
       }
