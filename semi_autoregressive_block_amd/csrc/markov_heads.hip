@@ -44,36 +44,47 @@ constexpr int kMaxRank = 512;
 // hidden-state part of the heads' maps.  A rows are lda elements apart, B rows ldb; K, lda, ldb
 // multiples of 8 and both bases 16-byte aligned (checked by the host).
 //
-// A workgroup of four waves owns a 128 x 128 output tile and one contiguous split of the
+// A workgroup of eight waves owns a 128 x 128 output tile and one contiguous split of the
 // contraction (blockIdx.z; a second kernel sums the splits' partial tiles in fixed order, so
 // results do not depend on scheduling).  The contraction goes in 64-wide slabs through a
 // four-stage LDS ring filled by direct-to-LDS copies (three slabs, 96 KB, in flight; one
 // workgroup per compute unit): a stage holds the tile's 128 A rows and 128 B rows, 128 bytes
-// each, so every copy instruction fetches whole 128-byte lines, with the eight 16-byte pieces of
-// row x stored at piece p ^ (x & 7), so that the 8 rows one read instruction touches per cycle
-// fall in distinct banks.  Wave (wm, wn) computes the 64 x 64 quarter at rows 64 wm, columns 64 wn as
-// 2 x 2 products v_mfma_f32_32x32x16_bf16 with B as the first operand, so lane l ends up holding
-// row l mod 32 of a product and columns 8q + 4(l / 32) .. +3: 16-byte stores.  The LDS reads are
-// inline assembly that waits for its own results, because the compiler would otherwise wait for
-// every copy in flight before each of them.
+// each, so every copy instruction fetches whole 128-byte lines.  The LDS serves a 16-byte read
+// sixteen lanes (256 bytes) at a time, and a read instruction's lanes 0-15 take 16 consecutive
+// rows, so piece p of row x is stored at p ^ ((x >> 1) & 7): rows x and x + 1 fall in the two
+// halves of the banks and the eight pairs in distinct 16-byte bank groups.  Wave (wm, wn) computes
+// the 64 x 32 piece at rows 64 wm, columns 32 wn as two products v_mfma_f32_32x32x16_bf16 with B
+// as the first operand, so lane l ends up holding row l mod 32 of a product and columns
+// 8q + 4(l / 32) .. +3: 16-byte stores.  Two waves per SIMD, because one wave alone cannot keep the
+// LDS busy.  A stage's twelve operand reads per wave go out together, one stage ahead of the
+// products (two register sets, used in turn), and they are inline assembly with the wait in a
+// separate statement, because the compiler would otherwise wait for every copy in flight before
+// each of them.
 constexpr int kGemmTile = 128;
 constexpr int kGemmSlab = 64;
 constexpr int kGemmStages = 4;
+constexpr int kGemmWaves = 8;
 constexpr int kGemmPieces = kGemmSlab / 8;                  // 16-byte pieces of a row per slab
 constexpr int kGemmRowBytes = kGemmSlab * 2;
 constexpr int kGemmStageBytes = 2 * kGemmTile * kGemmRowBytes;  // A and B pieces of one slab
 constexpr int kGemmCopies = kGemmStageBytes / 1024;             // 1 KB copies per stage
-constexpr int kGemmCopiesPerWave = kGemmCopies / 4;
+constexpr int kGemmCopiesPerWave = kGemmCopies / kGemmWaves;
 static_assert(kGemmPieces == 8, "the bank swizzle below assumes 128-byte rows");
 
-__device__ __forceinline__ void lds_read4_b128(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3, u32x4& x0,
-                                               u32x4& x1, u32x4& x2, u32x4& x3) {
-  asm volatile(
-      "ds_read_b128 %0, %4\n\tds_read_b128 %1, %5\n\tds_read_b128 %2, %6\n\tds_read_b128 %3, %7\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(x0), "=&v"(x1), "=&v"(x2), "=&v"(x3)
-      : "v"(a0), "v"(a1), "v"(a2), "v"(a3)
-      : "memory");
+// Three 16-byte LDS reads, no wait: the results are not defined until lds_wait12 below.
+__device__ __forceinline__ void lds_issue3_b128(uint32_t a0, uint32_t a1, uint32_t a2, u32x4& x0, u32x4& x1,
+                                                u32x4& x2) {
+  asm volatile("ds_read_b128 %0, %3\n\tds_read_b128 %1, %4\n\tds_read_b128 %2, %5"
+               : "=&v"(x0), "=&v"(x1), "=&v"(x2)
+               : "v"(a0), "v"(a1), "v"(a2)
+               : "memory");
+}
+// Waits for every LDS read in flight; the registers the reads fill are defined again here, so no
+// use of them moves above the wait.
+__device__ __forceinline__ void lds_wait12(u32x4 (&r)[12]) {
+  asm volatile("s_waitcnt lgkmcnt(0)"
+               : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]), "+v"(r[4]), "+v"(r[5]), "+v"(r[6]), "+v"(r[7]),
+                 "+v"(r[8]), "+v"(r[9]), "+v"(r[10]), "+v"(r[11])::"memory");
 }
 
 __device__ __forceinline__ void wait_vmcnt_copies(int n) {  // n = copies allowed in flight (a multiple of 4)
@@ -88,21 +99,21 @@ __device__ __forceinline__ void wait_vmcnt_copies(int n) {  // n = copies allowe
 static_assert(kGemmCopiesPerWave * (kGemmStages - 2) <= 16 && kGemmCopiesPerWave % 4 == 0,
               "copies in flight beyond the waits above");
 
-__global__ __launch_bounds__(256) void head_proj_gemm(const uint16_t* __restrict__ A, int64_t lda,
-                                                      const uint16_t* __restrict__ B, int64_t ldb,
-                                                      float* __restrict__ P, int64_t split_stride, int M, int N,
-                                                      int K, int kchunk) {
+__global__ __launch_bounds__(64 * kGemmWaves) void head_proj_gemm(const uint16_t* __restrict__ A, int64_t lda,
+                                                                  const uint16_t* __restrict__ B, int64_t ldb,
+                                                                  float* __restrict__ P, int64_t split_stride,
+                                                                  int M, int N, int K, int kchunk) {
   __shared__ __align__(16) unsigned char ring[kGemmStages * kGemmStageBytes];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave & 1, wn = wave >> 1;  // rows 64 wm, columns 32 wn of the tile
   const int i0 = blockIdx.x * kGemmTile, c0 = blockIdx.y * kGemmTile;
   const int kb = blockIdx.z * kchunk, ke = min(K, kb + kchunk);
   const int nst = (ke - kb + kGemmSlab - 1) / kGemmSlab;  // >= 1: the host launches no empty split
 
-  // copies: per stage 32 of 1 KB (A then B), 8 per wave; copy c, lane l -> LDS chunk 64 c + l of the
-  // stage = row (64 c + l) / 8 of A (c < 16) or B, stored piece (l & 7), which holds the row's piece
-  // (l & 7) ^ (row & 7)
+  // copies: per stage 32 of 1 KB (A then B), 4 per wave; copy c, lane l -> LDS chunk 64 c + l of the
+  // stage = row x = (64 c + l) / 8 of A (c < 16) or B, stored piece (l & 7), which holds the row's
+  // piece (l & 7) ^ ((x >> 1) & 7)
   constexpr int kHalf = kGemmCopies / 2;
   const uint16_t* src[kGemmCopiesPerWave];
   int kpiece[kGemmCopiesPerWave];
@@ -110,7 +121,7 @@ __global__ __launch_bounds__(256) void head_proj_gemm(const uint16_t* __restrict
   for (int j = 0; j < kGemmCopiesPerWave; ++j) {
     const int c = wave * kGemmCopiesPerWave + j;  // 0 .. 31
     const int x = ((c % kHalf) * 64 + lane) / kGemmPieces;
-    const int piece = (lane % kGemmPieces) ^ (x & 7);
+    const int piece = (lane % kGemmPieces) ^ ((x >> 1) & 7);
     src[j] = c < kHalf ? A + (int64_t)min(i0 + x, M - 1) * lda : B + (int64_t)min(c0 + x, N - 1) * ldb;
     kpiece[j] = piece * 8;
   }
@@ -128,52 +139,87 @@ __global__ __launch_bounds__(256) void head_proj_gemm(const uint16_t* __restrict
     }
   };
 
-  f32x16 acc[2][2];
+  f32x16 acc[2];
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+    for (int r = 0; r < 16; ++r) acc[a][r] = 0.f;
 
-  // this lane's operand rows: A rows 64 wm + 32 a + (l & 31), B rows 64 wn + 32 b + (l & 31); the
-  // piece of k16 step t is 2 t + (l >> 5)
+  // this lane's operand rows: A rows 64 wm + 32 a + (l & 31), B row 32 wn + (l & 31); the piece of
+  // k16 step t is 2 t + (l >> 5)
   const uint32_t ring_lds = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)ring;
-  uint32_t roff[4];  // byte offsets of the four operand rows inside a stage
-  int rsw[4];
+  uint32_t roff[3];  // byte offsets of the three operand rows inside a stage
+  int rsw[3];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int x = (q < 2 ? 64 * wm + 32 * q : 64 * wn + 32 * (q - 2)) + (lane & 31);
+  for (int q = 0; q < 3; ++q) {
+    const int x = (q < 2 ? 64 * wm + 32 * q : 32 * wn) + (lane & 31);
     roff[q] = (uint32_t)((q < 2 ? 0 : kGemmTile * kGemmRowBytes) + x * kGemmRowBytes);
-    rsw[q] = x & 7;
+    rsw[q] = (x >> 1) & 7;
   }
   const int h = lane >> 5;
 
   const int pre = nst < kGemmStages - 1 ? nst : kGemmStages - 1;
   for (int st = 0; st < pre; ++st) issue(st);
-  for (int st = 0; st < nst; ++st) {
-    const int ahead = min(nst - 1 - st, kGemmStages - 2);  // stages issued after this one
-    wait_vmcnt_copies(kGemmCopiesPerWave * ahead);
-    __builtin_amdgcn_s_barrier();  // every wave's copies of stage st are in; stage st - 1 is consumed
+  // stage st's copies are in (every wave's, after the barrier) and stage st - 1 is consumed: its
+  // slot takes the copies of stage st + 3
+  auto stage_in = [&](int st) {
+    wait_vmcnt_copies(kGemmCopiesPerWave * min(nst - 1 - st, kGemmStages - 2));
+    __builtin_amdgcn_s_barrier();
     if (st + kGemmStages - 1 < nst) issue(st + kGemmStages - 1);
+  };
+  auto read_stage = [&](int st, u32x4 (&r)[12]) {
     const uint32_t sbase = ring_lds + (st % kGemmStages) * kGemmStageBytes;
-    const int k = kb + st * kGemmSlab;
 #pragma unroll
     for (int t = 0; t < kGemmSlab / 16; ++t) {
-      const int pc = 2 * t + h;  // this lane's piece in the slab
-      u32x4 fa0, fa1, fb0, fb1;
-      lds_read4_b128(sbase + roff[0] + ((pc ^ rsw[0]) << 4), sbase + roff[1] + ((pc ^ rsw[1]) << 4),
-                     sbase + roff[2] + ((pc ^ rsw[2]) << 4), sbase + roff[3] + ((pc ^ rsw[3]) << 4), fa0, fa1, fb0,
-                     fb1);
-      if (k + 8 * pc >= ke) fa0 = fa1 = fb0 = fb1 = u32x4{0u, 0u, 0u, 0u};
-      acc[0][0] = mfma32x32x16(fb0, fa0, acc[0][0]);
-      acc[0][1] = mfma32x32x16(fb1, fa0, acc[0][1]);
-      acc[1][0] = mfma32x32x16(fb0, fa1, acc[1][0]);
-      acc[1][1] = mfma32x32x16(fb1, fa1, acc[1][1]);
+      const int pc = 2 * t + h;
+      lds_issue3_b128(sbase + roff[0] + ((pc ^ rsw[0]) << 4), sbase + roff[1] + ((pc ^ rsw[1]) << 4),
+                      sbase + roff[2] + ((pc ^ rsw[2]) << 4), r[3 * t], r[3 * t + 1], r[3 * t + 2]);
     }
+  };
+  auto products = [&](const u32x4 (&c)[12]) {
+#pragma unroll
+    for (int t = 0; t < kGemmSlab / 16; ++t) {
+      acc[0] = mfma32x32x16(c[3 * t + 2], c[3 * t], acc[0]);
+      acc[1] = mfma32x32x16(c[3 * t + 2], c[3 * t + 1], acc[1]);
+    }
+  };
+  // stage st's products from registers c while stage st + 1's reads land in n
+  auto body = [&](int st, const u32x4 (&c)[12], u32x4 (&n)[12]) {
+    stage_in(st + 1);
+    read_stage(st + 1, n);
+    __builtin_amdgcn_sched_barrier(0);
+    products(c);
+    __builtin_amdgcn_sched_barrier(0);
+    lds_wait12(n);
+  };
+  // the last stage: its pieces past the contraction end become zero
+  auto last = [&](u32x4 (&c)[12]) {
+    const int k = kb + (nst - 1) * kGemmSlab;
+#pragma unroll
+    for (int t = 0; t < kGemmSlab / 16; ++t)
+      if (k + 8 * (2 * t + h) >= ke)
+#pragma unroll
+        for (int q = 0; q < 3; ++q) c[3 * t + q] = u32x4{0u, 0u, 0u, 0u};
+    products(c);
+  };
+  // two register sets in turn (the loop takes stages in pairs, so neither is copied)
+  u32x4 ra[12], rb[12];
+  stage_in(0);
+  read_stage(0, ra);
+  lds_wait12(ra);
+  int st = 0;
+  for (; st + 2 < nst; st += 2) {
+    body(st, ra, rb);
+    body(st + 1, rb, ra);
+  }
+  if (st + 1 < nst) {
+    body(st, ra, rb);
+    last(rb);
+  } else {
+    last(ra);
   }
 
-  // lane l: row i0 + 64 wm + 32 a + (l & 31), columns c0 + 64 wn + 32 b + 8 q + 4 h .. +3 (N is a
+  // lane l: row i0 + 64 wm + 32 a + (l & 31), columns c0 + 32 wn + 8 q + 4 h .. +3 (N is a
   // multiple of 8, so a group that starts inside the row ends inside it)
   float* Pz = P + (int64_t)blockIdx.z * split_stride;
 #pragma unroll
@@ -181,14 +227,11 @@ __global__ __launch_bounds__(256) void head_proj_gemm(const uint16_t* __restrict
     const int i = i0 + 64 * wm + 32 * a + (lane & 31);
     if (i >= M) continue;
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int c = c0 + 64 * wn + 32 * b + 8 * q + 4 * h;
-        if (c < N)
-          *(f32x4*)(Pz + (int64_t)i * N + c) =
-              f32x4{acc[a][b][4 * q], acc[a][b][4 * q + 1], acc[a][b][4 * q + 2], acc[a][b][4 * q + 3]};
-      }
+    for (int q = 0; q < 4; ++q) {
+      const int c = c0 + 32 * wn + 8 * q + 4 * h;
+      if (c < N)
+        *(f32x4*)(Pz + (int64_t)i * N + c) = f32x4{acc[a][4 * q], acc[a][4 * q + 1], acc[a][4 * q + 2], acc[a][4 * q + 3]};
+    }
   }
 }
 
@@ -452,7 +495,8 @@ hipError_t run_head(const HeadArgs& a, const int32_t* prev_tok, int64_t prev_str
   const int nsplit = (a.d + kchunk - 1) / kchunk;  // <= sk_max, none empty
   const int64_t split_stride = (int64_t)M * N;
   hipLaunchKernelGGL(head_proj_gemm,
-                     dim3((M + kGemmTile - 1) / kGemmTile, (N + kGemmTile - 1) / kGemmTile, nsplit), dim3(256), 0,
+                     dim3((M + kGemmTile - 1) / kGemmTile, (N + kGemmTile - 1) / kGemmTile, nsplit),
+                     dim3(64 * kGemmWaves), 0,
                      s, (const uint16_t*)a.hidden, (int64_t)a.d, Bh, ldw, P, split_stride, M, N, a.d, kchunk);
   if (nsplit > 1)
     hipLaunchKernelGGL(proj_sum_splits, dim3((unsigned)((split_stride / 4 + 255) / 256)), dim3(256), 0, s, P, nsplit,
