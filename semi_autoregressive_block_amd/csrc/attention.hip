@@ -407,6 +407,16 @@ struct Ring {
   static constexpr int kPieces = D * 2 / 16;             // 16-byte pieces per key row
   static constexpr int kTensorBytes = 32 * D * 2;        // K (or V) of one slab
   static constexpr int kSlotBytes = 2 * kTensorBytes;    // parity-0 slab then parity-1 slab
+  // The XOR term of key row `key`.  A 16-byte read is served sixteen lanes (256 bytes, every
+  // bank once) at a time, and lanes 0-15 read keys 0-15: 256-byte rows (D = 128) XOR the piece
+  // with key mod 16; 128-byte rows (D = 64) sit two to a bank line, so keys 2m and 2m + 1 take
+  // the two halves and the piece is XORed with m mod 8.
+  __device__ static constexpr int ksw(int key) { return kPieces >= 16 ? key % kPieces : (key >> 1) % kPieces; }
+  // The rotation of key row `key`'s 64-byte V groups.  A transposing read's 32 lanes take 64 bytes
+  // of each of four keys 4m .. 4m + 3: 256-byte rows rotate by key mod 4; 128-byte rows (two to a
+  // bank line) rotate by (key >> 1) mod 2, so keys 4m + 1 and 4m + 3 sit in the other half.
+  static constexpr int kGroups = kPieces / 4;            // 64-byte groups per key row
+  __device__ static constexpr int vsw(int key) { return kGroups >= 4 ? key % kGroups : (key >> 1) % kGroups; }
 };
 
 // Where a workgroup's slabs come from (wave-uniform): slab s < n_ctx_slabs
@@ -422,8 +432,8 @@ struct SlabSource {
 };
 
 // This lane's operand pieces of one staged slab.  K piece kk (key r32, head
-// dims 16*kk + 8h .. +7) sits at chunk r32*P + ((2kk + h) ^ (r32 mod P)) =
-// r32*P + (2kk ^ y), y = h ^ (r32 mod P).  V^T comes from ds_read_b64_tr_b16:
+// dims 16*kk + 8h .. +7) sits at chunk r32*P + ((2kk + h) ^ ksw(r32)) =
+// r32*P + (2kk ^ y), y = h ^ ksw(r32).  V^T comes from ds_read_b64_tr_b16:
 // in each 16-lane group, lane l receives element l mod 4 of the 8 bytes
 // addressed by lane 4e + l/4, as its element e.  So when lane l (= r32 mod
 // 16) addresses key kb + l/4, head dims d0 + 4(l mod 4) .. +3, it receives
@@ -439,11 +449,11 @@ struct SlabView {
   __device__ SlabView(const unsigned char* kslab, const unsigned char* vslab, int h, int r32)
       : kp(kslab), vp(vslab) {
     kbase = r32 * P * 16;
-    kx = (h ^ (r32 % P)) * 16;
+    kx = (h ^ Rg::ksw(r32)) * 16;
     const int l = r32 % 16, g2 = r32 / 16;
     const int key = 4 * h + l / 4;  // plus 16t + 8e
     vbase = key * (D * 2) + 32 * g2 + 8 * (l % 4);
-    vx = 64 * ((l / 4) % (P / 4));  // the piece XOR (4 * (key mod P/4)) in bytes
+    vx = 64 * Rg::vsw(l / 4);  // the group rotation of key 4h + l/4 (+16t + 8e: same low two bits)
   }
   __device__ u32x4 k(int kk) const { return *(const u32x4*)(kp + kbase + ((32 * kk) ^ kx)); }
   __device__ u32x4 v(int t, int j) const {
@@ -483,7 +493,7 @@ struct DmaPair {
         const int q = (inst * 64) / (32 * P);     // slab parity of this copy
         const int cc = (inst * 64) % (32 * P) + lane;  // chunk within the slab
         const int key = cc / P;
-        const int piece = (cc % P) ^ (hv ? 4 * (key % (P / 4)) : key % P);
+        const int piece = (cc % P) ^ (hv ? 4 * Rg::vsw(key) : Rg::ksw(key));
         const int s = min(2 * pair + q, st.nslab - 1);
         const bool own = s >= st.n_ctx_slabs;
         const int k0 = own ? (s - st.n_ctx_slabs) * 32 : s * 32;
