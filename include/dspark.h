@@ -335,8 +335,9 @@ int dspark_markov_head_block_logits(int kind, const float* base_logits, const vo
  *
  *   draft_logits  [R, K, V] float32 (the draft's step logits)
  *   target_logits [R, K + 1, V] float32
- *   draft_tokens  [R, K] int32 (outside [0, V): token 0 is used and
- *                 DSPARK_STATUS_BAD_TOKEN set in *dev_status, nullable)
+ *   draft_tokens  [R, K] int32 (any token outside [0, V) sets
+ *                 DSPARK_STATUS_BAD_TOKEN in *dev_status, nullable, wherever it
+ *                 lies; one that is tested is tested as token 0)
  *   n_accepted    [R] int32 (out): kept drafts, 0 .. K
  *   next_token    [R] int32 (out): the target's token after them
  * Workspace from dspark_verify_workspace_bytes (256-byte aligned).

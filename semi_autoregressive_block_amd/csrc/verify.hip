@@ -158,32 +158,55 @@ __global__ __launch_bounds__(kThreads) void verify_stats_kernel(const float* __r
   }
 }
 
-// One thread per row: the left-to-right acceptance test.
-__global__ void verify_decide_kernel(const float* __restrict__ draft, const float* __restrict__ target,
-                                     const int32_t* __restrict__ tokens, const float* __restrict__ stats, int R,
-                                     int K, int V, float invT, int greedy, uint32_t slo, uint32_t shi,
-                                     int32_t* __restrict__ n_acc, int32_t* __restrict__ pos_out,
-                                     int32_t* __restrict__ next_token, int32_t* __restrict__ status) {
-  const int row = blockIdx.x * blockDim.x + threadIdx.x;
-  if (row >= R) return;
-  int k = 0;
-  for (; k < K; ++k) {
-    int x = tokens[(int64_t)row * K + k];
-    if (x < 0 || x >= V) {
-      status_or(status, DSPARK_STATUS_BAD_TOKEN);
-      x = 0;
+// The left-to-right acceptance test of every request: its first rejected position.
+__global__ __launch_bounds__(64) void verify_decide_kernel(const float* __restrict__ draft,
+                                                            const float* __restrict__ target,
+                                                            const int32_t* __restrict__ tokens,
+                                                            const float* __restrict__ stats, int R, int K, int V,
+                                                            float invT, int greedy, uint32_t slo, uint32_t shi,
+                                                            int32_t* __restrict__ n_acc, int32_t* __restrict__ pos_out,
+                                                            int32_t* __restrict__ next_token,
+                                                            int32_t* __restrict__ status) {
+  // 16 lanes per request (four requests per wave), lane p testing position c + p of each
+  // 16-position chunk c: every position's loads are in flight at once, and a ballot finds the
+  // request's first rejection.  A position's test is the same arithmetic as a sequential scan.
+  // Every draft token is range-checked, also those past the stop.
+  const int lane = threadIdx.x, sub = lane >> 4, p = lane & 15;
+  const int row = blockIdx.x * 4 + sub;
+  const bool live = row < R;
+  int stop = -1;  // the request's first rejected position once found (the same in its 16 lanes)
+  bool bad_any = false;
+  for (int c = 0; c < K; c += 16) {
+    const int pos = c + p;
+    const bool inrange = live && pos < K;
+    int x = 0;
+    if (inrange) {
+      x = tokens[(int64_t)row * K + pos];
+      if (x < 0 || x >= V) {
+        bad_any = true;
+        x = 0;
+      }
     }
-    const float* s = stats + ((int64_t)row * (K + 1) + k) * kStat;
-    if (greedy) {
-      if ((uint32_t)x != __float_as_uint(s[4])) break;
-      continue;
+    bool reject = false;
+    if (inrange && stop < 0) {
+      const float* s = stats + ((int64_t)row * (K + 1) + pos) * kStat;
+      if (greedy) {
+        reject = (uint32_t)x != __float_as_uint(s[4]);
+      } else {
+        const float lp = target[((int64_t)row * (K + 1) + pos) * V + x] * invT - s[0] - logf(s[1]);
+        const float lq = draft[((int64_t)row * K + pos) * V + x] * invT - s[2] - logf(s[3]);
+        const u32x4 w = philox4x32_10(u32x4{(uint32_t)pos, 0u, (uint32_t)row, 2u}, slo, shi);
+        const float u = ((float)(w[0] >> 9) + 0.5f) * 0x1.0p-23f;
+        reject = !(u < expf(lp - lq));
+      }
     }
-    const float lp = target[((int64_t)row * (K + 1) + k) * V + x] * invT - s[0] - logf(s[1]);
-    const float lq = draft[((int64_t)row * K + k) * V + x] * invT - s[2] - logf(s[3]);
-    const u32x4 w = philox4x32_10(u32x4{(uint32_t)k, 0u, (uint32_t)row, 2u}, slo, shi);
-    const float u = ((float)(w[0] >> 9) + 0.5f) * 0x1.0p-23f;
-    if (!(u < expf(lp - lq))) break;
+    const uint32_t rej = (uint32_t)(__ballot(reject) >> (16 * sub)) & 0xffffu;
+    if (rej && stop < 0) stop = c + __builtin_ctz(rej);
   }
+  const bool bad_row = ((uint32_t)(__ballot(bad_any) >> (16 * sub)) & 0xffffu) != 0u;
+  if (!live || p != 0) return;
+  if (bad_row) status_or(status, DSPARK_STATUS_BAD_TOKEN);
+  const int k = stop < 0 ? K : stop;
   n_acc[row] = k;
   pos_out[row] = k;
   if (greedy)
@@ -294,7 +317,7 @@ extern "C" int dspark_verify(const float* draft_logits, const float* target_logi
   const int vec = V % 4 == 0 && (uintptr_t)target_logits % 16 == 0 && (uintptr_t)draft_logits % 16 == 0;
   hipLaunchKernelGGL(verify_stats_kernel, dim3(K + 1, R), dim3(kThreads), 0, s, draft_logits, target_logits, K, V,
                      invT, greedy, vec, stats);
-  hipLaunchKernelGGL(verify_decide_kernel, dim3((R + 63) / 64), dim3(64), 0, s, draft_logits, target_logits,
+  hipLaunchKernelGGL(verify_decide_kernel, dim3((R + 3) / 4), dim3(64), 0, s, draft_logits, target_logits,
                      draft_tokens, stats, R, K, V, invT, greedy, slo, shi, n_accepted, pos, next_token, dev_status);
   if (!greedy) {
     hipLaunchKernelGGL(verify_zero_keys, dim3((R + 255) / 256), dim3(256), 0, s, keys, R);

@@ -202,6 +202,55 @@ def test_greedy_ties(dsp):
     assert np.all(tok_or == lo)
 
 
+def test_long_drafts_sampled(dsp):
+    """K = 40 drafts (the decision takes positions in chunks of 16): stops
+    before 16, between 16 and 31, and rows that keep all 40."""
+    R, K, V = 32, 40, 600
+    d, t, x = _inputs(77, R, K, V, spread=0.05)
+    n = _check(dsp, d, t, x, 1.0, seed=5)
+    assert (n < 16).any() and ((n >= 16) & (n < 32)).any() and (n == K).any()
+
+
+def test_long_drafts_greedy(dsp):
+    """K = 40 at T = 0: a stop at each chunk edge and inside each chunk."""
+    R, K, V = 12, 40, 500
+    rng = np.random.default_rng(78)
+    t = rng.standard_normal((R, K + 1, V)).astype(np.float32)
+    d = rng.standard_normal((R, K, V)).astype(np.float32)
+    x = np.argmax(t[:, :K], axis=-1).astype(np.int32)
+    stops = [0, 1, 15, 16, 17, 31, 32, 33, 39]
+    for i, k in enumerate(stops):
+        x[i, k] = (x[i, k] + 1) % V
+    n, tok = dsp.verify(dev(d), dev(t), dev(x), temperature=0.0)
+    n_or, tok_or = VF.verify(d, t, x, temperature=0.0)
+    np.testing.assert_array_equal(n.cpu().numpy(), n_or)
+    np.testing.assert_array_equal(tok.cpu().numpy(), tok_or)
+    np.testing.assert_array_equal(n_or, stops + [K] * (R - len(stops)))
+
+
+def test_bad_token_past_the_stop_is_flagged(dsp):
+    """An out-of-range draft token is reported wherever it lies; one past the
+    stopping position changes nothing else."""
+    R, K, V = 3, 20, 300
+    rng = np.random.default_rng(79)
+    t = rng.standard_normal((R, K + 1, V)).astype(np.float32)
+    d = rng.standard_normal((R, K, V)).astype(np.float32)
+    x = np.argmax(t[:, :K], axis=-1).astype(np.int32)
+    x[1, 2] = (x[1, 2] + 1) % V  # row 1 stops at position 2
+    n_or, tok_or = VF.verify(d, t, x, temperature=0.0)
+    xb = x.copy()
+    xb[1, 18] = V  # never tested
+    from semi_autoregressive_block_amd import _lib
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    n, tok = dsp.verify(dev(d), dev(t), dev(xb), temperature=0.0, status=st)
+    assert int(st.item()) & _lib.STATUS_BAD_TOKEN
+    np.testing.assert_array_equal(n.cpu().numpy(), n_or)
+    np.testing.assert_array_equal(tok.cpu().numpy(), tok_or)
+    st.zero_()
+    dsp.verify(dev(d), dev(t), dev(x), temperature=0.0, status=st)
+    assert int(st.item()) == 0
+
+
 def test_bad_draft_token_is_flagged(dsp):
     d, t, x = _inputs(5, 2, 3, 64)
     x[1, 0] = 64
