@@ -161,18 +161,20 @@ __global__ __launch_bounds__(64 * NW) void markov_step_mfma(
       const u32x4 v = *(const u32x4*)(w2 + (int64_t)min(k, r - 1) * V + min(col, (int64_t)V - 8));
       st.w[i] = (k < r && col < V) ? v : u32x4{0u, 0u, 0u, 0u};
     }
+    // the base logits are read once: non-temporal loads, so that they do not push the W2 tiles
+    // (read again by the next step) out of the caches
     if constexpr (FL) {
       // whole 128-byte lines: load j covers rows 4j + lane/16 of the wave's 16,
       // 16-byte chunk lane % 16 of the tile's 256 bytes per row
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int rj = min(blockIdx.y * 16 * NW + wave * 16 + 4 * j + (lane >> 4), R - 1);
-        st.b[j] = *(const f32x4*)(base + ((int64_t)rj * gamma + step) * V + min(tc + 4 * (lane & 15), (int64_t)V - 4));
+        st.b[j] = __builtin_nontemporal_load((const f32x4*)(base + ((int64_t)rj * gamma + step) * V + min(tc + 4 * (lane & 15), (int64_t)V - 4)));
       }
     } else {
       const float* brow = base + ((int64_t)rowc * gamma + step) * V;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) st.b[j] = *(const f32x4*)(brow + min(tc + 16 * j + 4 * g, (int64_t)V - 4));
+      for (int j = 0; j < 4; ++j) st.b[j] = __builtin_nontemporal_load((const f32x4*)(brow + min(tc + 16 * j + 4 * g, (int64_t)V - 4)));
     }
   };
   auto store_w2 = [&](unsigned char* bufp, const Set& st) {
