@@ -166,7 +166,7 @@ __global__ __launch_bounds__(64) void verify_decide_kernel(const float* __restri
                                                             float invT, int greedy, uint32_t slo, uint32_t shi,
                                                             int32_t* __restrict__ n_acc, int32_t* __restrict__ pos_out,
                                                             int32_t* __restrict__ next_token,
-                                                            int32_t* __restrict__ status) {
+                                                            int32_t* __restrict__ status, uint64_t* __restrict__ keys) {
   // 16 lanes per request (four requests per wave), lane p testing position c + p of each
   // 16-position chunk c: every position's loads are in flight at once, and a ballot finds the
   // request's first rejection.  A position's test is the same arithmetic as a sequential scan.
@@ -211,6 +211,8 @@ __global__ __launch_bounds__(64) void verify_decide_kernel(const float* __restri
   pos_out[row] = k;
   if (greedy)
     next_token[row] = (int32_t)__float_as_uint(stats[((int64_t)row * (K + 1) + k) * kStat + 4]);
+  else
+    keys[row] = 0ull;  // the draw's key, folded by the resample pass's atomic maxima
 }
 
 // Gumbel-max draw at each row's stopping position: from max(0, p - q) when
@@ -278,11 +280,6 @@ __global__ void verify_finalize_kernel(const uint64_t* __restrict__ keys, int32_
   next_token[row] = (int32_t)t;
 }
 
-__global__ void verify_zero_keys(uint64_t* keys, int R) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < R) keys[i] = 0ull;
-}
-
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 }  // namespace
@@ -318,9 +315,9 @@ extern "C" int dspark_verify(const float* draft_logits, const float* target_logi
   hipLaunchKernelGGL(verify_stats_kernel, dim3(K + 1, R), dim3(kThreads), 0, s, draft_logits, target_logits, K, V,
                      invT, greedy, vec, stats);
   hipLaunchKernelGGL(verify_decide_kernel, dim3((R + 3) / 4), dim3(64), 0, s, draft_logits, target_logits,
-                     draft_tokens, stats, R, K, V, invT, greedy, slo, shi, n_accepted, pos, next_token, dev_status);
+                     draft_tokens, stats, R, K, V, invT, greedy, slo, shi, n_accepted, pos, next_token, dev_status,
+                     keys);
   if (!greedy) {
-    hipLaunchKernelGGL(verify_zero_keys, dim3((R + 255) / 256), dim3(256), 0, s, keys, R);
     const int64_t nq = (V + 3) / 4;
     const int splits = (int)(nq < 64 * kThreads ? (nq + kThreads - 1) / kThreads : 64);
     hipLaunchKernelGGL(verify_resample_kernel, dim3(splits, R), dim3(kThreads), 0, s, draft_logits, target_logits,
