@@ -386,7 +386,9 @@ def main():
         if args.only == "train_attention":
             print(json.dumps({"train_attention_ms": t2_ms, "TFLOPs": t2_flops / t2_ms / 1e9}))
             return
-        result["train_attention"] = dict(ms=t2_ms, flops=t2_flops)
+        # draft positions: kept blocks x gamma query positions (each over all query heads)
+        t2_pos = c2["gamma"] * int((k2 != 0).sum())
+        result["train_attention"] = dict(ms=t2_ms, flops=t2_flops, positions=t2_pos)
         del t2, out2, ws2
         torch.cuda.empty_cache()
 
@@ -612,7 +614,8 @@ def main():
         line["attention_training"] = {"workload": "1 x 4096 context, 512 anchors (472 kept), gamma=8, "
                                                   "Hq=32/Hkv=8, D=128, bf16",
                                       "ms": a["ms"], "TFLOPs": tf, "mfma_frac": tf / MFMA_BF16_PEAK_TFLOPS,
-                                      "algorithmic_flops": a["flops"]}
+                                      "algorithmic_flops": a["flops"],
+                                      "positions_per_s": a["positions"] / (a["ms"] / 1e3)}
     if "config1" in result:
         a = result["config1"]
         line["config1"] = {"workload": "tiny float32 round: 2 x 8 blocks of 8 over context 128, Hq=4/Hkv=2, D=64; "
