@@ -63,8 +63,8 @@ CASES = [
     (4, [64, 3000, 1], 2, 16, 32, 8, 128),
     (5, [2500, 900], 20, 8, 8, 8, 64),
     (6, [4100], 3, 64, 2, 1, 128),      # gamma 64: own keys span two slabs
-    (7, [3000, 260], 40, 8, 16, 4, 128),  # 256-row tiles, five per (request, KV head), the last ragged
-    (8, [1800], 37, 8, 8, 2, 128),      # 256-row tiles over blocks of 32 rows, a ragged last tile
+    (7, [3000, 260], 40, 8, 16, 4, 128),  # ten 128-row tiles per (request, KV head), four blocks each
+    (8, [1800], 37, 8, 8, 2, 128),      # 128-row tiles over blocks of 32 rows, a ragged last tile (32 rows)
 ]
 
 
