@@ -225,10 +225,16 @@ def _sampled(dsp, inp, picks, gamma):
 
 
 def test_config2_full_size_sampled(dsp):
+    """The training-shaped launch the bench times: every query head of five
+    anchors (the first, a middle one, the last kept, the first padded one and
+    the one with the longest context; all heads of an anchor span its blocks'
+    eight KV-head workgroups) plus 24 random (anchor, head) pairs."""
     inp = W.config2_device(torch, DEV)
+    anchor, keep = inp["anchor"].cpu().numpy()[0], inp["keep"].cpu().numpy()[0]
+    longest = int(np.argmax(np.where(keep != 0, anchor, -1)))
     rng = np.random.default_rng(7)
     picks = [(0, int(a), int(h)) for a, h in zip(rng.integers(0, 512, 24), rng.integers(0, 32, 24))]
-    picks += [(0, 471, 31), (0, 472, 0), (0, 511, 5), (0, 0, 0)]
+    picks += [(0, a, h) for a in sorted({0, 255, 471, 472, longest}) for h in range(32)]
     _sampled(dsp, inp, picks, 8)
 
 
