@@ -186,16 +186,14 @@ def _full_size_check(dsp, inp, T, seed, rows):
 
 def test_config3_full_size(dsp):
     """R=64, gamma=16, V=151936, r=256, bf16 weights, T=1 Gumbel: the launch
-    the bench times; 12 sampled rows checked step by step (teacher-forced)."""
+    the bench times; every row checked step by step (teacher-forced)."""
     inp = W.config3_device(torch, torch.device("cuda:0"))
-    rows = list(np.random.default_rng(1).choice(64, size=12, replace=False))
-    tok = _full_size_check(dsp, inp, inp["temperature"], inp["seed"], rows)
+    tok = _full_size_check(dsp, inp, inp["temperature"], inp["seed"], list(range(64)))
     assert tok.min() >= 0 and tok.max() < 151936
 
 
 def test_config5_markov_full_size(dsp):
-    """R=128 rows, gamma=16, greedy: 12 sampled rows."""
+    """R=128 rows, gamma=16, greedy: the round the bench times, every row."""
     inp = W.config5_device(torch, torch.device("cuda:0"))
-    rows = list(np.random.default_rng(2).choice(128, size=12, replace=False))
-    _full_size_check(dsp, inp, 0.0, 0, rows)
+    _full_size_check(dsp, inp, 0.0, 0, list(range(128)))
 
