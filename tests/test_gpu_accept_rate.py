@@ -85,25 +85,29 @@ def test_deterministic(dsp):
     assert torch.equal(x1, x2)
 
 
-def test_config4_full_size_sampled(dsp):
+def test_config4_full_size_every_row(dsp):
     """Full workload: 4 x 512 x 8 rows of V = 151936 bf16 (2 x 4.98 GB), the
-    launch the bench times; 40 sampled blocks checked against the oracle,
-    accept and tau; the rest checked for range."""
+    launch the bench times; every one of the 16384 rows checked against the
+    oracle (accept and tau), 32 blocks at a time."""
     inp = W.config4_device(torch, torch.device("cuda:0"))
     m = inp["mask"]
     em = dsp.eval_mask(dev(m.anchor), dev(m.keep), dev(m.seq_lens), dev(m.loss_mask), gamma=8)
     acc, tau = dsp.accept_rate(inp["draft"], inp["target"], eval_mask=em, want_tau=True)
     acc_h, tau_h, em_h = acc.cpu().numpy(), tau.cpu().numpy(), em.cpu().numpy()
     assert np.all((acc_h >= 0) & (acc_h <= 1))
-    rng = np.random.default_rng(44)
-    for _ in range(40):
-        b, a = int(rng.integers(0, 4)), int(rng.integers(0, 512))
-        dv = W.bf16_to_f32(host_bits(inp["draft"][b, a]))
-        tv = W.bf16_to_f32(host_bits(inp["target"][b, a]))
-        ref = OR.accept_rate(dv, tv)
-        assert np.abs(acc_h[b, a] - ref).max() < TOL["bf16"]
-        assert np.abs(acc_h[b, a] - ref).max() < 2e-5
-        assert abs(tau_h[b, a] - OR.tau(ref, em_h[b, a])) < 1e-4
+    flat = list(range(4 * 512))
+    worst = 0.0
+    for c in range(0, len(flat), 32):
+        idx = torch.as_tensor(flat[c:c + 32], device=inp["draft"].device)
+        bs, as_ = idx // 512, idx % 512
+        dv = W.bf16_to_f32(host_bits(inp["draft"][bs, as_]))
+        tv = W.bf16_to_f32(host_bits(inp["target"][bs, as_]))
+        ref = OR.accept_rate(dv, tv)  # [blocks, 8]
+        got = acc_h[bs.cpu().numpy(), as_.cpu().numpy()]
+        worst = max(worst, float(np.abs(got - ref).max()))
+        for j, (b, a) in enumerate(zip(bs.tolist(), as_.tolist())):
+            assert abs(tau_h[b, a] - OR.tau(ref[j], em_h[b, a])) < 1e-4, (b, a)
+    assert worst < TOL["bf16"] and worst < 2e-5, worst
     del inp
     torch.cuda.empty_cache()
 
