@@ -19,7 +19,7 @@ import pytest
 import torch
 
 import workloads as W
-from gpu_util import DEV, as_dtype, dev
+from gpu_util import DEV, as_dtype, dev, host_bits
 from oracle import accept_rate as OR
 from oracle import tv_loss as OT
 
@@ -276,3 +276,65 @@ def test_l1_loss_identical_is_zero_and_deterministic(dsp):
     a = dsp.l1_loss(x, y, eval_mask=dev(m), want_grad=True)
     b = dsp.l1_loss(x, y, eval_mask=dev(m), want_grad=True)
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_block_logits_training_batch_sampled_rows(dsp):
+    """The launch the bench times: 16384 rows (workload 4's training batch) x
+    V = 151936, rank 256, bf16 W1/W2 (W2 held in registers over the whole
+    launch); 256 rows checked against the oracle (the first and last rows, rows
+    on either side of 16-row block and 128-row group edges, and a random
+    sample), logits and greedy tokens."""
+    bl = W.config4_block_logits_device(torch, DEV)
+    N, V, r = bl["N"], bl["V"], bl["r"]
+    logits, tok = dsp.markov_block_logits(bl["base"], bl["w1"], bl["w2"], bl["prev"], want_tokens=True)
+    edges = {0, 1, 15, 16, 127, 128, 8191, 8192, N - 17, N - 16, N - 1}
+    rows = sorted(edges | set(np.random.default_rng(21).choice(N, size=256 - len(edges), replace=False).tolist()))
+    sel = torch.as_tensor(rows, device=DEV)
+    w1 = bl["w1"].double().cpu().numpy()
+    w2 = bl["w2"].double().cpu().numpy()
+    ref = OT.block_logits(bl["base"][sel].double().cpu().numpy(), w1, w2, bl["prev"][sel].cpu().numpy())
+    got = logits[sel].cpu().numpy()
+    assert np.abs(got - ref).max() < 2e-4
+    _check_tokens(tok[sel].cpu().numpy(), ref)
+
+
+def test_l1_loss_training_batch(dsp):
+    """The launch the bench times: workload 4's 4 x 512 x 8 rows of V = 151936
+    bf16 with its eval mask.  Every row's L1 distance and greedy agreement
+    (hence the loss and tau_greedy) against the oracle, 32 blocks at a time;
+    the gradient on 16 blocks (128 rows), including the first and last."""
+    inp = W.config4_device(torch, DEV)
+    m = inp["mask"]
+    em = dsp.eval_mask(dev(m.anchor), dev(m.keep), dev(m.seq_lens), dev(m.loss_mask), gamma=8)
+    loss, grad, rows, tau = dsp.l1_loss(inp["draft"], inp["target"], eval_mask=em, want_grad=True,
+                                        want_rows=True, want_tau_greedy=True)
+    em_h, rows_h, tau_h = em.cpu().numpy(), rows.cpu().numpy(), tau.cpu().numpy()
+    grad_blocks = {0, 4 * 512 - 1} | set(np.random.default_rng(31).choice(4 * 512, size=14, replace=False).tolist())
+    w = OT.position_weights(8, 4.0)
+    den_all = float((em_h * w).sum())
+    l1 = np.zeros((4, 512, 8))
+    agree = np.zeros((4, 512, 8))
+    for c in range(0, 4 * 512, 32):
+        idx = torch.arange(c, c + 32, device=DEV)
+        bs, as_ = (idx // 512).cpu().numpy(), (idx % 512).cpu().numpy()
+        dv = W.bf16_to_f32(host_bits(inp["draft"][idx // 512, idx % 512]))
+        tv = W.bf16_to_f32(host_bits(inp["target"][idx // 512, idx % 512]))
+        l1[bs, as_] = OT.l1_distance(dv, tv)
+        agree[bs, as_] = OT.greedy_accept(dv, tv)
+        for j in range(32):
+            if c + j in grad_blocks:
+                # the loss normalises its row weights over the whole batch, the
+                # oracle over the block it is given: compare in the block's units
+                b, a = int(bs[j]), int(as_[j])
+                g = grad[b, a].cpu().numpy()[None, None].astype(np.float64)
+                d1, t1, m1 = dv[j][None, None], tv[j][None, None], em_h[b, a][None, None]
+                den_block = float((m1 * w).sum())
+                if den_block == 0.0:
+                    assert not g.any()
+                    continue
+                _check_grad(g * (den_all / den_block), d1, t1, m1, OT.l1_loss_grad(d1, t1, m1))
+    assert np.abs(rows_h - l1).max() < 1e-5
+    ref_loss = float((OT.row_coefficients(em_h, 4.0) * l1).sum())
+    assert abs(loss.item() - ref_loss) < 1e-5 * max(1.0, abs(ref_loss))
+    ref_tau = 1.0 + np.cumprod(agree * em_h, axis=-1).sum(axis=-1)
+    np.testing.assert_array_equal(tau_h, ref_tau)
