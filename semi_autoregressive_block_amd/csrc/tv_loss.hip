@@ -538,25 +538,54 @@ __global__ __launch_bounds__(kCThreads) void l1_cluster_kernel(
   }
 }
 
-// Per row: L1 = sum of the G slice shares (fixed order) and the greedy flag
-// from the first maxima (slices in index order, so the first slice that holds
-// the row maximum holds its lowest index).  One thread per row.
-__global__ void l1_cluster_finalize_kernel(const u32x4* __restrict__ rec, int G, float* __restrict__ row_l1,
-                                           float* __restrict__ greedy, int64_t rows) {
-  const int64_t row = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (row >= rows) return;
-  const u32x4* r = rec + row * G;
-  float l = 0.f, bd = -INFINITY, bt = -INFINITY;
-  uint32_t id = 0, it = 0;
-  for (int g = 0; g < G; ++g) {
-    const u32x4 x = r[g];
-    l += __uint_as_float(x[0]);
-    const float md = __uint_as_float(x[1]), mt = __uint_as_float(x[2]);
-    if (g == 0 || md > bd) { bd = md; id = (uint32_t)g * kChunkEl + (x[3] >> 16); }
-    if (g == 0 || mt > bt) { bt = mt; it = (uint32_t)g * kChunkEl + (x[3] & 0xffffu); }
+// Per row: L1 = sum of the G slice shares (a fixed reduction tree) and the
+// greedy flag from the first maxima (slices in index order, so the first
+// slice that holds the row maximum holds its lowest index).  One wave per
+// row: lane g reads slice records g and g + 64 (consecutive 16-byte records,
+// coalesced), then the wave folds sums and (maximum, lowest slice) keys.
+__device__ __forceinline__ uint64_t first_max_key(float v, int g) {
+  return ((uint64_t)float_order_key(v) << 32) | (uint64_t)(0xffffffffu - (uint32_t)g);
+}
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t k) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const uint32_t lo = __shfl_xor((uint32_t)k, off, kWave), hi = __shfl_xor((uint32_t)(k >> 32), off, kWave);
+    const uint64_t o = ((uint64_t)hi << 32) | lo;
+    k = o > k ? o : k;
   }
-  row_l1[row] = l;
-  greedy[row] = id == it ? 1.f : 0.f;
+  return k;
+}
+constexpr int kFinRows = 4;  // rows (waves) per workgroup
+__global__ __launch_bounds__(64 * kFinRows) void l1_cluster_finalize_kernel(const u32x4* __restrict__ rec, int G,
+                                                                          float* __restrict__ row_l1,
+                                                                          float* __restrict__ greedy, int64_t rows) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * kFinRows + (threadIdx.x >> 6);
+  if (row >= rows) return;  // whole waves
+  const u32x4* r = rec + row * G;
+  float l = 0.f;
+  uint64_t kd = 0, kt = 0;  // 0: no slice (below every real key)
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int g = lane + 64 * h;
+    if (g < G) {
+      const u32x4 x = r[g];
+      l += __uint_as_float(x[0]);
+      const uint64_t d = first_max_key(__uint_as_float(x[1]), g), t = first_max_key(__uint_as_float(x[2]), g);
+      kd = d > kd ? d : kd;
+      kt = t > kt ? t : kt;
+    }
+  }
+  l = cluster::wave_sum(l);
+  kd = wave_max_u64(kd);
+  kt = wave_max_u64(kt);
+  // the winning slices' first-maximum positions
+  const int gd = (int)(0xffffffffu - (uint32_t)kd), gt = (int)(0xffffffffu - (uint32_t)kt);
+  const uint32_t pd = rec[row * G + gd][3] >> 16, pt = rec[row * G + gt][3] & 0xffffu;
+  if (lane == 0) {
+    row_l1[row] = l;
+    greedy[row] = (uint32_t)gd * kChunkEl + pd == (uint32_t)gt * kChunkEl + pt ? 1.f : 0.f;
+  }
 }
 
 __global__ void l1_zero_u32_kernel(uint32_t* p, int64_t n) {
@@ -569,13 +598,23 @@ __global__ void l1_zero_u32_kernel(uint32_t* p, int64_t n) {
 __global__ __launch_bounds__(kThreads) void l1_coef_kernel(const uint8_t* __restrict__ m, float* __restrict__ coef,
                                                            int64_t rows, int gamma, float decay) {
   __shared__ float red[1][kWaves];
+  // the position k = n mod gamma advances by kThreads mod gamma per step (no 64-bit division)
+  const int step = kThreads % gamma;
   float part[1] = {0.f};
-  for (int64_t n = threadIdx.x; n < rows; n += kThreads)
-    if (!m || m[n]) part[0] += expf(-(float)(n % gamma) / decay);
+  int k = (int)threadIdx.x % gamma;
+  for (int64_t n = threadIdx.x; n < rows; n += kThreads) {
+    if (!m || m[n]) part[0] += expf(-(float)k / decay);
+    k += step;
+    if (k >= gamma) k -= gamma;
+  }
   block_sum(part, red);
   const float inv = part[0] > 0.f ? 1.f / part[0] : 0.f;
-  for (int64_t n = threadIdx.x; n < rows; n += kThreads)
-    coef[n] = (!m || m[n]) ? expf(-(float)(n % gamma) / decay) * inv : 0.f;
+  k = (int)threadIdx.x % gamma;
+  for (int64_t n = threadIdx.x; n < rows; n += kThreads) {
+    coef[n] = (!m || m[n]) ? expf(-(float)k / decay) * inv : 0.f;
+    k += step;
+    if (k >= gamma) k -= gamma;
+  }
 }
 
 // loss = sum_n c_n l1_n (one workgroup, fixed order); tau_greedy per block.
@@ -725,8 +764,8 @@ extern "C" int dspark_l1_loss(const void* draft_logits, const void* target_logit
       fprintf(stderr, "[dspark] l1_loss: %d CUs, G=%d, clusters=%lld\n", cus, G, (long long)ncl);
     hipError_t e = hipLaunchCooperativeKernel(ckern, dim3((unsigned)(ncl * G)), dim3(kCThreads), args, 0, s);
     if (e != hipSuccess) return fail(DSPARK_ERR_HIP, "l1_loss: cooperative launch: %s", hipGetErrorString(e));
-    hipLaunchKernelGGL(l1_cluster_finalize_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s,
-                       (const u32x4*)rec, G, l1, greedy, rows);
+    hipLaunchKernelGGL(l1_cluster_finalize_kernel, dim3((unsigned)((rows + kFinRows - 1) / kFinRows)),
+                       dim3(64 * kFinRows), 0, s, (const u32x4*)rec, G, l1, greedy, rows);
   } else {
     const unsigned grid = (unsigned)(rows < cus ? rows : cus);
     if (bf) {
