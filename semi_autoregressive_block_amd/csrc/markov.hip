@@ -305,15 +305,16 @@ __global__ __launch_bounds__(64 * NW) void markov_step_mfma(
 
 // ------------------------------------------------------------- vector path
 // float32 (or unaligned bf16) weights: one thread per quad of columns,
-// 16 rows per pass with E in LDS, fp32 FMAs.
+// RC rows per pass (16, or 4 when 16-row chunks would leave most compute
+// units idle) with E in LDS, fp32 FMAs.
 constexpr int kRowChunk = 16;
 constexpr int kVThreads = 64;  // one wave per workgroup
 
-// One wave per (16-row chunk, run of column quads): E = the chunk's rank-r
-// rows, transposed into LDS ([k][16 rows]) so that each rank step reads the
-// 16 values with four broadcast reads; every lane owns one quad of columns
-// at a time and accumulates its 16 x 4 products in registers.
-template <bool kBf16W, bool SC = false, bool EB = false>
+// One wave per (RC-row chunk, run of column quads): E = the chunk's rank-r
+// rows, transposed into LDS ([k][RC rows]) so that each rank step reads the
+// RC values with RC / 4 broadcast reads; every lane owns one quad of columns
+// at a time and accumulates its RC x 4 products in registers.
+template <bool kBf16W, bool SC = false, bool EB = false, int RC = kRowChunk>
 __global__ __launch_bounds__(kVThreads) void markov_step_valu(
     const float* __restrict__ base, const void* __restrict__ w1v, const float* __restrict__ ebuf,
     const void* __restrict__ w2v,
@@ -322,42 +323,42 @@ __global__ __launch_bounds__(kVThreads) void markov_step_valu(
     int r, int step, float invT, int greedy, uint32_t seed_lo, uint32_t seed_hi,
     int32_t* __restrict__ status) {
   extern __shared__ __align__(16) unsigned char smem[];
-  float* Et = (float*)smem;  // [r][kRowChunk]
-  __shared__ int prev_tok[kRowChunk];
+  float* Et = (float*)smem;  // [r][RC]
+  __shared__ int prev_tok[RC];
   auto w1 = [&](int64_t i) -> float {
     return kBf16W ? __uint_as_float((uint32_t)((const uint16_t*)w1v)[i] << 16) : ((const float*)w1v)[i];
   };
   auto w2 = [&](int64_t i) -> float {
     return kBf16W ? __uint_as_float((uint32_t)((const uint16_t*)w2v)[i] << 16) : ((const float*)w2v)[i];
   };
-  const int row0 = blockIdx.y * kRowChunk;
-  if (!EB && threadIdx.x < kRowChunk) {  // the chunk's previous tokens, decoded once
+  const int row0 = blockIdx.y * RC;
+  if (!EB && threadIdx.x < RC) {  // the chunk's previous tokens, decoded once
     const int row = row0 + threadIdx.x;
     prev_tok[threadIdx.x] =
         row < R ? decode_prev(keys_prev, first_prev, row, R, V, blockIdx.x == 0 ? status : nullptr) : 0;
   }
   __syncthreads();
-  for (int c = threadIdx.x; c < kRowChunk * r; c += kVThreads) {
+  for (int c = threadIdx.x; c < RC * r; c += kVThreads) {
     const int rr = c / r, k = c % r, row = row0 + rr;
     float v = 0.f;
     if (row < R) {
       if constexpr (EB) v = ebuf[((int64_t)row * gamma + step) * r + k];
       else v = w1((int64_t)prev_tok[rr] * r + k);
     }
-    Et[k * kRowChunk + rr] = v;
+    Et[k * RC + rr] = v;
   }
   __syncthreads();
 
   const int64_t nq = (V + 3) / 4;
-  float best_z[kRowChunk];
-  uint32_t best_v[kRowChunk];
+  float best_z[RC];
+  uint32_t best_v[RC];
 #pragma unroll
-  for (int i = 0; i < kRowChunk; ++i) { best_z[i] = -INFINITY; best_v[i] = 0xffffffffu; }
+  for (int i = 0; i < RC; ++i) { best_z[i] = -INFINITY; best_v[i] = 0xffffffffu; }
   for (int64_t q = (int64_t)blockIdx.x * kVThreads + threadIdx.x; q < nq; q += (int64_t)gridDim.x * kVThreads) {
     const int64_t v0 = q * 4;
-    float acc[kRowChunk][4];
+    float acc[RC][4];
 #pragma unroll
-    for (int i = 0; i < kRowChunk; ++i)
+    for (int i = 0; i < RC; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
     constexpr int kKB = 8;  // rank steps whose W2 loads go out together
@@ -371,9 +372,9 @@ __global__ __launch_bounds__(kVThreads) void markov_step_valu(
 #pragma unroll
       for (int kb = 0; kb < kKB; ++kb) {
         if (k0 + kb >= r) break;
-        const f32x4* e4 = (const f32x4*)(Et + (k0 + kb) * kRowChunk);
+        const f32x4* e4 = (const f32x4*)(Et + (k0 + kb) * RC);
 #pragma unroll
-        for (int i4 = 0; i4 < kRowChunk / 4; ++i4) {
+        for (int i4 = 0; i4 < RC / 4; ++i4) {
           const f32x4 e = e4[i4];
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
@@ -385,14 +386,14 @@ __global__ __launch_bounds__(kVThreads) void markov_step_valu(
         }
       }
     }
-    float bl[kRowChunk][4];  // the chunk's base logits, all loads in flight together
+    float bl[RC][4];  // the chunk's base logits, all loads in flight together
 #pragma unroll
-    for (int i = 0; i < kRowChunk; ++i)
+    for (int i = 0; i < RC; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         bl[i][j] = (row0 + i < R && v0 + j < V) ? base[((int64_t)(row0 + i) * gamma + step) * V + v0 + j] : 0.f;
 #pragma unroll
-    for (int i = 0; i < kRowChunk; ++i) {
+    for (int i = 0; i < RC; ++i) {
       const int row = row0 + i;
       if (row >= R) break;
       u32x4 xs = u32x4{0u, 0u, 0u, 0u};
@@ -411,7 +412,7 @@ __global__ __launch_bounds__(kVThreads) void markov_step_valu(
     }
   }
 #pragma unroll
-  for (int i = 0; i < kRowChunk; ++i) {
+  for (int i = 0; i < RC; ++i) {
     uint64_t key = best_v[i] == 0xffffffffu ? 0ull : argmax_key(best_z[i], best_v[i]);
 #pragma unroll
     for (int m = 1; m < 64; m <<= 1) {
@@ -501,18 +502,27 @@ hipError_t launch_step(bool mfma_ok, bool bf, int cus, hipStream_t s, const floa
     return r <= 256 ? launch_mfma<4, 8, 2, false, SC, EB>(gx, gy, s, base, a, ebuf, b, first_prev, kp, ko, step_logits, R, gamma, V, r, step, invT, greedy, slo, shi, st)
                     : launch_mfma<4, 16, 2, false, SC, EB>(gx, gy, s, base, a, ebuf, b, first_prev, kp, ko, step_logits, R, gamma, V, r, step, invT, greedy, slo, shi, st);
   }
-  const int gy = (R + kRowChunk - 1) / kRowChunk;
   int gx = 4 * cus;
   const int64_t quads = (V + 3) / 4;
   if ((int64_t)gx * kVThreads > quads) gx = (int)((quads + kVThreads - 1) / kVThreads);
   if (gx < 1) gx = 1;
-  const size_t shm = (size_t)kRowChunk * r * 4;
+  // small shapes (a few dozen single-wave workgroups at 16 rows each) take 4-row chunks:
+  // four times the workgroups, a quarter of each lane's chain
+  const bool narrow = (int64_t)gx * ((R + kRowChunk - 1) / kRowChunk) < cus;
+  const int rc = narrow ? 4 : kRowChunk;
+  const int gy = (R + rc - 1) / rc;
+  const size_t shm = (size_t)rc * r * 4;
+  auto go = [&](auto kern) {
+    (void)allow_lds_once(kern, shm);
+    hipLaunchKernelGGL(kern, dim3(gx, gy), dim3(kVThreads), shm, s, base, w1, ebuf, w2, first_prev, kp, ko,
+                       step_logits, R, gamma, V, r, step, invT, greedy, slo, shi, st);
+  };
   if (bf) {
-    (void)allow_lds_once(markov_step_valu<true, SC, EB>, shm);
-    hipLaunchKernelGGL((markov_step_valu<true, SC, EB>), dim3(gx, gy), dim3(kVThreads), shm, s, base, w1, ebuf, w2, first_prev, kp, ko, step_logits, R, gamma, V, r, step, invT, greedy, slo, shi, st);
+    if (narrow) go(markov_step_valu<true, SC, EB, 4>);
+    else go(markov_step_valu<true, SC, EB>);
   } else {
-    (void)allow_lds_once(markov_step_valu<false, SC, EB>, shm);
-    hipLaunchKernelGGL((markov_step_valu<false, SC, EB>), dim3(gx, gy), dim3(kVThreads), shm, s, base, w1, ebuf, w2, first_prev, kp, ko, step_logits, R, gamma, V, r, step, invT, greedy, slo, shi, st);
+    if (narrow) go(markov_step_valu<false, SC, EB, 4>);
+    else go(markov_step_valu<false, SC, EB>);
   }
   return hipGetLastError();
 }
