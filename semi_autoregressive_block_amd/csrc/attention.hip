@@ -712,9 +712,20 @@ __global__ __launch_bounds__(64) void block_attn_valu(Params p, int D) {
   for (int k0 = 0; k0 < p.gamma; k0 += kValuRows) {
     const int nr = min(kValuRows, p.gamma - k0);
     __syncthreads();
-    for (int kr = 0; kr < kValuRows; ++kr) {
-      const int64_t qrow = (own0 + k0 + min(kr, nr - 1)) * p.Hq + h;
-      for (int d = lane; d < D; d += 64) qs[kr][d] = ld(p.q, qrow * D + d);
+    {
+      // all the group's Q loads in flight before the first store
+      float qv[kValuRows][2];
+#pragma unroll
+      for (int kr = 0; kr < kValuRows; ++kr) {
+        const int64_t qrow = (own0 + k0 + min(kr, nr - 1)) * p.Hq + h;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) qv[kr][e] = lane + 64 * e < D ? ld(p.q, qrow * D + lane + 64 * e) : 0.f;
+      }
+#pragma unroll
+      for (int kr = 0; kr < kValuRows; ++kr)
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+          if (lane + 64 * e < D) qs[kr][lane + 64 * e] = qv[kr][e];
     }
     float m[kValuRows], l[kValuRows], o0[kValuRows], o1[kValuRows];
 #pragma unroll
@@ -722,13 +733,34 @@ __global__ __launch_bounds__(64) void block_attn_valu(Params p, int D) {
     for (int j0 = 0; j0 < nkeys; j0 += 64) {
       const int nj = min(64, nkeys - j0);
       __syncthreads();  // the previous chunk's reads are done
-      for (int jj = 0; jj < nj; ++jj) {
-        const int64_t off = key_off(j0 + jj);
-        const void* kp = j0 + jj < lim ? (const void*)p.kc : (const void*)p.kb;
-        const void* vp = j0 + jj < lim ? (const void*)p.vc : (const void*)p.vb;
-        for (int d = lane; d < D; d += 64) {
-          ks[jj][d] = ld(kp, off + d);
-          vs[jj][d] = ld(vp, off + d);
+      // eight keys' K and V loads in flight before their stores (one round
+      // trip per eight keys, not per key)
+      for (int jb = 0; jb < nj; jb += 8) {
+        float kv[8][2], vv[8][2];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int jj = min(jb + u, nj - 1);
+          const int64_t off = key_off(j0 + jj);
+          const void* kp = j0 + jj < lim ? (const void*)p.kc : (const void*)p.kb;
+          const void* vp = j0 + jj < lim ? (const void*)p.vc : (const void*)p.vb;
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const int d = lane + 64 * e;
+            kv[u][e] = d < D ? ld(kp, off + d) : 0.f;
+            vv[u][e] = d < D ? ld(vp, off + d) : 0.f;
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          if (jb + u >= nj) break;
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const int d = lane + 64 * e;
+            if (d < D) {
+              ks[jb + u][d] = kv[u][e];
+              vs[jb + u][d] = vv[u][e];
+            }
+          }
         }
       }
       __syncthreads();
